@@ -1,0 +1,338 @@
+"""Pins for the oracle's exact attention, samplers and HyperAttention (CPU only).
+
+Pins: a pure-Python brute force of the definition, row-stochasticity, the
+merge identity, special cases that reduce the estimator to exact attention,
+and the closed-form mean and variance of the two sampling estimators.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import exact, hyperattention as ha, sampling, sortlsh
+
+
+def brute_attention(Q, K, V, causal):
+    n, d = len(Q), len(Q[0])
+    out = []
+    for i in range(n):
+        keys = range(i + 1) if causal else range(len(K))
+        s = [sum(Q[i][t] * K[j][t] for t in range(d)) / math.sqrt(d) for j in keys]
+        a = [math.exp(x) for x in s]
+        den = sum(a)
+        out.append([sum(a[jj] * V[j][c] for jj, j in enumerate(keys)) / den
+                    for c in range(len(V[0]))])
+    return np.array(out)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_exact_matches_brute_force(causal):
+    rs = np.random.default_rng(0)
+    for n, d in ((1, 4), (9, 4), (24, 8)):
+        Q, K, V = (rs.standard_normal((n, d)) for _ in range(3))
+        O, lse = exact.exact_attention(Q, K, V, causal=causal)
+        B = brute_attention(Q.tolist(), K.tolist(), V.tolist(), causal)
+        assert np.abs(O - B).max() < 1e-12
+        # lse is the log row sum of exp(scores)
+        for i in range(n):
+            hi = i + 1 if causal else n
+            s = [float(Q[i] @ K[j]) / math.sqrt(d) for j in range(hi)]
+            assert abs(lse[i] - math.log(sum(math.exp(x) for x in s))) < 1e-12
+
+
+def test_softmax_rows_sum_to_one_and_causal_row0():
+    rs = np.random.default_rng(1)
+    Q, K, V = (rs.standard_normal((50, 16)) * 2 for _ in range(3))
+    for causal in (False, True):
+        O, lse = exact.exact_attention(Q, K, V, causal=causal)
+        S = Q @ K.T / 4.0
+        if causal:
+            S = np.where(np.tril(np.ones((50, 50))) > 0, S, -np.inf)
+        P = np.exp(S - lse[:, None])
+        assert np.abs(P.sum(1) - 1).max() < 1e-12
+        assert np.abs(P @ V - O).max() < 1e-12
+    O, _ = exact.exact_attention(Q, K, V, causal=True)
+    assert np.array_equal(O[0], V[0])
+
+
+def test_constant_values_and_key_permutation():
+    rs = np.random.default_rng(2)
+    Q, K = rs.standard_normal((20, 8)), rs.standard_normal((20, 8))
+    V = np.tile(rs.standard_normal(8), (20, 1))
+    O, _ = exact.exact_attention(Q, K, V)
+    assert np.abs(O - V).max() < 1e-12
+    V = rs.standard_normal((20, 8))
+    p = rs.permutation(20)
+    assert np.abs(exact.exact_attention(Q, K, V)[0]
+                  - exact.exact_attention(Q, K[p], V[p])[0]).max() < 1e-12
+
+
+def test_lse_merge_is_union_of_key_sets():
+    rs = np.random.default_rng(3)
+    Q, K, V = (rs.standard_normal((30, 8)) for _ in range(3))
+    whole = exact.exact_attention(Q, K, V)
+    parts = [exact.exact_attention(Q, K[s], V[s]) for s in
+             (slice(0, 7), slice(7, 19), slice(19, 30))]
+    O, L = exact.lse_merge(parts)
+    assert np.abs(O - whole[0]).max() < 1e-12
+    assert np.abs(L - whole[1]).max() < 1e-12
+
+
+def test_exact_rows_matches_full():
+    rs = np.random.default_rng(4)
+    Q, K, V = (rs.standard_normal((40, 8)) for _ in range(3))
+    rows = [0, 5, 39]
+    for causal in (False, True):
+        O, L = exact.exact_attention(Q, K, V, causal=causal)
+        Or, Lr = exact.exact_attention_rows(Q, K, V, rows, causal=causal)
+        assert np.abs(Or - O[rows]).max() < 1e-12
+        assert np.abs(Lr - L[rows]).max() < 1e-12
+
+
+# ---------------------------------------------------------------- samplers
+
+def test_uniform_samples_closed_form_power_of_two():
+    from oracle import rng
+    idx, alpha = sampling.uniform_samples(9, 2, 3, 1000, 256, 64)
+    assert alpha == 4.0
+    for t in range(64):
+        u = rng.draw(9, rng.PURPOSE_UNIFORM, 2, 3, t) >> 32
+        assert idx[t] == 1000 + (u >> 24)           # top 8 bits: exactly uniform
+    idx, alpha = sampling.uniform_samples(9, 2, 3, 50, 10, 16)
+    assert alpha == 1.0 and np.array_equal(idx, np.arange(50, 60))
+
+
+def test_uniform_samples_in_range_and_flat():
+    idx, _ = sampling.uniform_samples(4, 0, 1, 100, 12, 6000)
+    assert idx.min() >= 100 and idx.max() < 112
+    idx, _ = sampling.uniform_samples(4, 0, 1, 100, 12, 11)
+    big, _ = sampling.uniform_samples(4, 0, 1, 0, 12 * 1000, 6000)
+    counts = np.bincount(big // 1000, minlength=12)
+    chi2 = ((counts - 500.0) ** 2 / 500.0).sum()       # 11 dof
+    assert chi2 < 40
+
+
+def test_row_sq_norms_exact_for_small_integers():
+    V = np.arange(24, dtype=np.float64).reshape(3, 8) - 11
+    a = sampling.row_sq_norms(V)
+    assert list(a) == [sum(int(x) ** 2 for x in row) for row in V]
+
+
+def test_vnorm_weights_properties():
+    rs = np.random.default_rng(5)
+    V = rs.standard_normal((64, 16))
+    V[3] = 0
+    a, W, P = sampling.vnorm_weights(V)
+    assert W[3] == 0 and np.all(W[np.arange(64) != 3] > 0)
+    assert W[np.argmax(a)] == 2 ** 32
+    order = np.argsort(a)
+    assert np.all(np.diff(W[order].astype(np.int64)) >= 0)
+    assert P[0] == 0 and int(P[-1]) == sum(int(w) for w in W)
+    for j in range(64):          # W_j / 2^32 is a_j / max a, rounded up
+        assert 0 <= int(W[j]) - a[j] / a.max() * 2 ** 32 < 1 + 2.0 ** -20
+    _, W0, P0 = sampling.vnorm_weights(np.zeros((5, 4)))
+    assert not W0.any() and not P0.any()
+
+
+def test_vnorm_inverse_cdf_equals_linear_scan():
+    rs = np.random.default_rng(6)
+    V = rs.standard_normal((40, 8))
+    V[rs.integers(0, 40, 6)] = 0
+    _, W, P = sampling.vnorm_weights(V)
+    lo, n_k, m = 8, 24, 20
+    idx, w = sampling.vnorm_samples(77, 1, 5, lo, n_k, P, W, m)
+    from oracle import rng
+    T = int(P[lo + n_k]) - int(P[lo])
+    for t in range(m):
+        U = (rng.draw(77, rng.PURPOSE_VNORM, 1, 5, t) * T) >> 64
+        acc, pick = 0, None
+        for j in range(lo, lo + n_k):             # linear scan of the CDF
+            acc += int(W[j])
+            if acc > U:
+                pick = j
+                break
+        assert idx[t] == pick
+        assert W[pick] > 0
+        assert w[t] == np.float32(T / (m * int(W[pick])))
+
+
+def test_vnorm_frequencies_match_weights():
+    rs = np.random.default_rng(7)
+    V = rs.standard_normal((16, 8)) * rs.uniform(0.2, 2.0, (16, 1))
+    _, W, P = sampling.vnorm_weights(V)
+    idx, w = sampling.vnorm_samples(3, 0, 1, 0, 16, P, W, 12)
+    big = []
+    for node in range(1, 400):
+        i, _ = sampling.vnorm_samples(3, 0, node, 0, 16, P, W, 15)
+        big.extend(i)
+    counts = np.bincount(big, minlength=16)
+    p = W.astype(np.float64) / float(P[-1])
+    exp_c = p * len(big)
+    chi2 = ((counts - exp_c) ** 2 / exp_c).sum()          # 15 dof
+    assert chi2 < 50
+    # unbiasedness weight identity: p_j * m * (T / (m W_j)) = 1
+    T = float(P[-1])
+    assert np.allclose(p * 12 * (T / (12 * W.astype(np.float64))), 1.0)
+
+
+def test_vnorm_empty_and_exhaustive():
+    V = np.zeros((32, 8))
+    V[20:] = 1.0
+    _, W, P = sampling.vnorm_weights(V)
+    idx, w = sampling.vnorm_samples(1, 0, 1, 0, 16, P, W, 4)
+    assert len(idx) == 0 and len(w) == 0
+    idx, w = sampling.vnorm_samples(1, 0, 1, 16, 16, P, W, 4)
+    assert np.all(idx >= 20)                   # zero rows are never drawn
+    idx, w = sampling.vnorm_samples(1, 0, 1, 16, 16, P, W, 16)
+    assert np.array_equal(idx, np.arange(16, 32)) and np.all(w == 1)
+
+
+# ---------------------------------------------------------- HyperAttention
+
+def _inputs(n, d, H=1, seed=0, spread=1.0):
+    rs = np.random.default_rng(seed)
+    return tuple(rs.standard_normal((H, n, d)) * spread for _ in range(3))
+
+
+def test_schedule_covers_causal_mask_exactly_once():
+    n, base = 64, 8
+    subs, blocks = ha.schedule(n, True, base)
+    cover = np.zeros((n, n), dtype=int)
+    for _, _, q_lo, k_lo, size in subs:
+        cover[q_lo:q_lo + size, k_lo:k_lo + size] += 1
+    for lo, size in blocks:
+        cover[lo:lo + size, lo:lo + size] += np.tril(np.ones((size, size), dtype=int))
+    assert np.array_equal(cover, np.tril(np.ones((n, n), dtype=int)))
+    nodes = [s[1] for s in subs]
+    assert len(set(nodes)) == len(nodes) and sorted(nodes) == list(range(1, 8))
+    assert [s[0] for s in subs].count(3) == 4
+    assert ha.schedule(64, True, 64) == ([], [(0, 64)])
+    assert len(ha.schedule(24, True, 4)[1]) == 8    # 24 -> 12 -> 6 -> 3 <= 4
+    with pytest.raises(ValueError):
+        ha.schedule(20, True, 4)                 # 20 -> 10 -> 5 (odd, > 4)
+
+
+def test_single_bucket_reduces_to_exact():
+    Q, K, V = _inputs(64, 8, H=2)
+    Oe = [exact.exact_attention(Q[h], K[h], V[h]) for h in range(2)]
+    for m, seed in ((1, 0), (7, 3), (200, 9)):
+        O, L = ha.hyperattention(Q, K, V, causal=False, b=64, m=m, r=4, seed=seed)
+        for h in range(2):
+            assert np.abs(O[h] - Oe[h][0]).max() < 1e-12
+            assert np.abs(L[h] - Oe[h][1]).max() < 1e-12
+
+
+def test_exhaustive_samples_reduce_to_exact():
+    Q, K, V = _inputs(64, 8, seed=1)
+    Oe, Le = exact.exact_attention(Q[0], K[0], V[0])
+    for b in (1, 8, 16):
+        O, L = ha.hyperattention(Q, K, V, causal=False, b=b, m=64, r=8, seed=4)
+        assert np.abs(O[0] - Oe).max() < 1e-12
+        assert np.abs(L[0] - Le).max() < 1e-12
+
+
+def test_causal_reductions_to_exact_causal():
+    Q, K, V = _inputs(128, 8, seed=2)
+    Oe, Le = exact.exact_attention(Q[0], K[0], V[0], causal=True)
+    cases = [dict(b=8, m=4, recursion_base=128),    # no recursion
+             dict(b=64, m=4, recursion_base=16),    # every sub-problem one bucket
+             dict(b=8, m=64, recursion_base=16),    # exhaustive samples everywhere
+             dict(b=64, m=1, recursion_base=1)]     # recursion to single rows
+    for kw in cases:
+        O, L = ha.hyperattention(Q, K, V, causal=True, r=8, seed=5, **kw)
+        assert np.abs(O[0] - Oe).max() < 1e-12, kw
+        assert np.abs(L[0] - Le).max() < 1e-12, kw
+
+
+def test_rows_subset_matches_full():
+    Q, K, V = _inputs(256, 16, H=2, seed=3)
+    for causal in (False, True):
+        kw = dict(causal=causal, b=16, m=8, r=8, recursion_base=32, seed=12)
+        O, L = ha.hyperattention(Q, K, V, **kw)
+        rows = [0, 3, 77, 128, 255]
+        Or, Lr = ha.hyperattention(Q, K, V, rows=rows, **kw)
+        assert np.abs(Or[:, rows] - O[:, rows]).max() < 1e-12
+        assert np.abs(Lr[:, rows] - L[:, rows]).max() < 1e-12
+        mask = np.ones(256, dtype=bool)
+        mask[rows] = False
+        assert np.isnan(Or[:, mask]).all()
+
+
+def _fixed_problem(seed=0):
+    n, d, b = 32, 8, 8
+    Q, K, V = (x[0] for x in _inputs(n, d, seed=seed, spread=1.3))
+    G = sortlsh.hyperplanes(0, 1, 4, d)[0]
+    srt = sortlsh.sortlsh(sortlsh.hash_codes(Q, G), sortlsh.hash_codes(K, G), b)
+    scale = 1 / math.sqrt(d)
+    A = np.exp(Q @ K.T * scale)
+    inb = srt["bucket_q"][:, None] == srt["bucket_k"][None, :]
+    return n, Q, K, V, srt, scale, A, inb
+
+
+def test_approx_d_unbiased_with_closed_form_variance():
+    """E[d~_i] = D_ii and Var = (n sum_out A^2 - (sum_out A)^2) / m."""
+    n, Q, K, V, srt, scale, A, inb = _fixed_problem(0)
+    m, trials = 4, 3000
+    est = np.empty((trials, n))
+    for s in range(trials):
+        u, alpha = sampling.uniform_samples(s, 0, 1, 0, n, m)
+        _, lse = ha.estimate_block(Q, K, V, srt, u, alpha, np.zeros(0, int),
+                                   np.zeros(0), scale, with_product=False)
+        est[s] = np.exp(lse)
+    out = np.where(inb, 0.0, A)
+    var = (n * (out ** 2).sum(1) - out.sum(1) ** 2) / m
+    mean_err = (est.mean(0) - A.sum(1)) / np.sqrt(var / trials)
+    assert np.abs(mean_err).max() < 4.5
+    ratio = est.var(0) / var
+    assert np.all((ratio > 0.8) & (ratio < 1.25))
+
+
+def test_vnorm_product_unbiased_with_closed_form_variance():
+    """E[N_i] = sum_j A_ij V_j; E||dN||^2 = (sum_out A^2 |V|^2/p - |sum_out A V|^2)/m."""
+    n, Q, K, V, srt, scale, A, inb = _fixed_problem(1)
+    _, W, P = sampling.vnorm_weights(V)
+    p = W.astype(np.float64) / float(P[-1])
+    m, trials = 4, 3000
+    u_all = np.arange(n)                    # exhaustive uniform part: d~ exact
+    D = A.sum(1)
+    Ns = np.empty((trials, n, V.shape[1]))
+    for s in range(trials):
+        v, w = sampling.vnorm_samples(s, 0, 1, 0, n, P, W, m)
+        O, _ = ha.estimate_block(Q, K, V, srt, u_all, 1.0, v, w, scale)
+        Ns[s] = O * D[:, None]
+    out = np.where(inb, 0.0, A)
+    true = A @ V
+    err2 = ((Ns - true[None]) ** 2).sum(2).mean(0)
+    pred = ((out ** 2 * (V ** 2).sum(1)[None, :] / p[None, :]).sum(1)
+            - ((out @ V) ** 2).sum(1)) / m
+    ratio = err2 / pred
+    assert np.all((ratio > 0.8) & (ratio < 1.25))
+    bias = (Ns.mean(0) - true) / np.sqrt(pred / trials)[:, None]
+    assert np.abs(bias).max() < 5.0
+
+
+def test_rowsum_estimate_reduces_to_exact_lse():
+    Q, K, V = _inputs(64, 8, H=1, seed=6)
+    _, Le = exact.exact_attention(Q[0], K[0], V[0])
+    L = ha.rowsum_estimate(Q, K, b=64, m=3, r=8, seed=1)
+    assert np.abs(L[0] - Le).max() < 1e-12
+    L = ha.rowsum_estimate(Q, K, b=8, m=64, r=8, seed=1)
+    assert np.abs(L[0] - Le).max() < 1e-12
+
+
+def test_rowsum_estimate_is_lse_of_forward():
+    Q, K, V = _inputs(128, 8, H=1, seed=7)
+    _, L = ha.hyperattention(Q, K, V, causal=False, b=16, m=64, r=8, seed=3)
+    L2 = ha.rowsum_estimate(Q, K, b=16, m=64, r=8, seed=3)
+    # same d~; the forward's shift c also covers the V-norm sample scores
+    assert np.abs(L - L2).max() < 1e-12
+
+
+def test_approximation_error_order_on_iid_inputs():
+    """Reported, not pinned: relative error ~ sqrt(n/m) on diffuse attention."""
+    Q, K, V = _inputs(1024, 64, seed=8)
+    O, _ = ha.hyperattention(Q, K, V, causal=False, b=128, m=128, r=8, seed=2)
+    Oe, _ = exact.exact_attention(Q[0], K[0], V[0])
+    rel = np.linalg.norm(O[0] - Oe) / np.linalg.norm(Oe)
+    assert 0.5 * math.sqrt(1024 / 128) < rel < 2.0 * math.sqrt(1024 / 128)
