@@ -1,0 +1,175 @@
+"""PyTorch-facing binding of libhyperattn.so.
+
+Argument marshalling only: tensors are checked, outputs and workspaces are
+allocated with torch on the tensors' device, and the library is called on
+torch's current HIP stream. Every step of the computation runs in the
+library's HIP kernels; there is no other code path.
+
+Tensors are [heads, n, d] (or [batch, heads, n, d], folded into heads),
+contiguous, on a ROCm device, dtype torch.bfloat16 or torch.float32.
+"""
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import HA_BF16, HA_F32, check, lib
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return HA_BF16
+    if t.dtype == torch.float32:
+        return HA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _fold(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dim() == 4:
+        return t.reshape(t.shape[0] * t.shape[1], t.shape[2], t.shape[3])
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be [heads, n, d] or [batch, heads, n, d]")
+    return t
+
+
+def _qkv(q, k, v=None):
+    shape = q.shape
+    q, k = _fold(q, "q"), _fold(k, "k")
+    if v is not None:
+        v = _fold(v, "v")
+    for t in (k,) + ((v,) if v is not None else ()):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must have the same shape, dtype and device")
+    return shape, q, k, v
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def workspace_bytes(n, d, heads, *, causal, b, m, r=8, recursion_base=4096, dtype=HA_BF16):
+    nb = lib().hyperattn_workspace_bytes(n, d, heads, int(causal), b, m, recursion_base, r, dtype)
+    if nb == 0 and _lib.last_error():
+        raise _lib.HyperAttnError(-2, _lib.last_error())
+    return nb
+
+
+def alloc_workspace(nbytes, device):
+    # torch's caching allocator returns blocks aligned to at least 512 bytes
+    ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    assert ws.data_ptr() % 256 == 0
+    return ws
+
+
+def forward(q, k, v, *, causal, b=256, m=256, r=8, recursion_base=4096, seed=0,
+            return_lse=False, workspace=None, out=None, lse_out=None):
+    """HyperAttention forward; returns O (and lse if asked)."""
+    shape, q, k, v = _qkv(q, k, v)
+    H, n, d = q.shape
+    dt = _dtype_code(q)
+    o = out if out is not None else torch.empty_like(q)
+    lse = lse_out
+    if return_lse and lse is None:
+        lse = torch.empty((H, n), dtype=torch.float32, device=q.device)
+    nb = workspace_bytes(n, d, H, causal=causal, b=b, m=m, r=r,
+                         recursion_base=recursion_base, dtype=dt)
+    ws = workspace if workspace is not None else alloc_workspace(nb, q.device)
+    check(lib().hyperattn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), n, d, H,
+                                  int(causal), b, m, recursion_base, r, seed, dt, _ptr(ws),
+                                  ws.numel(), _stream(q.device)))
+    o = o.reshape(shape)
+    if return_lse:
+        return o, lse.reshape(shape[:-1])
+    return o
+
+
+def exact(q, k, v, *, causal=False, return_lse=False, out=None):
+    """Exact softmax attention (the library's own kernel)."""
+    shape, q, k, v = _qkv(q, k, v)
+    H, n, d = q.shape
+    o = out if out is not None else torch.empty_like(q)
+    lse = torch.empty((H, n), dtype=torch.float32, device=q.device) if return_lse else None
+    check(lib().exact_attention_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), n, d, H,
+                                        int(causal), _dtype_code(q), _stream(q.device)))
+    o = o.reshape(shape)
+    if return_lse:
+        return o, lse.reshape(shape[:-1])
+    return o
+
+
+def rowsum_estimate(q, k, *, b=256, m=256, r=8, seed=0):
+    """log d~ per row (Algorithm 2, non-causal)."""
+    shape, q, k, _ = _qkv(q, k)
+    H, n, d = q.shape
+    dt = _dtype_code(q)
+    out = torch.empty((H, n), dtype=torch.float32, device=q.device)
+    nb = workspace_bytes(n, d, H, causal=False, b=b, m=m, r=r, recursion_base=1, dtype=dt)
+    ws = alloc_workspace(nb, q.device)
+    check(lib().rowsum_estimate(_ptr(q), _ptr(k), n, d, H, b, m, r, seed, dt, _ptr(out),
+                                _ptr(ws), ws.numel(), _stream(q.device)))
+    return out.reshape(shape[:-1])
+
+
+def sortlsh_hash(x, *, r=8, seed=0, with_perm=False):
+    """Hash codes [heads, n] uint8 (and the stable sort permutation if asked)."""
+    shape = x.shape
+    x = _fold(x, "x")
+    H, n, d = x.shape
+    codes = torch.empty((H, n), dtype=torch.uint8, device=x.device)
+    perm = torch.empty((H, n), dtype=torch.int32, device=x.device) if with_perm else None
+    nb = lib().sortlsh_hash_workspace_bytes(n, H, int(with_perm))
+    ws = alloc_workspace(nb, x.device) if with_perm else None
+    check(lib().sortlsh_hash(_ptr(x), n, d, H, r, seed, _dtype_code(x), _ptr(codes), _ptr(perm),
+                             _ptr(ws), nb, _stream(x.device)))
+    codes = codes.reshape(shape[:-1])
+    return (codes, perm.reshape(shape[:-1])) if with_perm else codes
+
+
+def hyperplanes(seed, heads, r, d):
+    """The hash's Gaussian hyperplanes [heads, r, d] (host computation)."""
+    G = np.empty((heads, r, d), dtype=np.float32)
+    check(lib().sortlsh_hyperplanes(seed, heads, r, d,
+                                    G.ctypes.data_as(ctypes.POINTER(ctypes.c_float))))
+    return G
+
+
+def workspace_layout(n, d, heads, *, causal, b, m, r=8, recursion_base=4096, dtype=HA_BF16):
+    """{region: (offset, bytes)} of hyperattn_forward's workspace."""
+    off = (ctypes.c_int64 * len(_lib.WS_REGIONS))()
+    nb = (ctypes.c_int64 * len(_lib.WS_REGIONS))()
+    check(lib().hyperattn_workspace_layout(n, d, heads, int(causal), b, m, recursion_base, r,
+                                           dtype, off, nb))
+    return {name: (off[i], nb[i]) for i, name in enumerate(_lib.WS_REGIONS)}
+
+
+class KernelTimer:
+    """Per-kernel durations from hipEvents the library records around launches."""
+
+    def __enter__(self):
+        L = lib()
+        check(L.hyperattn_profile_collect())
+        check(L.hyperattn_profile_reset())
+        check(L.hyperattn_profile_enable(1))
+        return self
+
+    def __exit__(self, *exc):
+        L = lib()
+        check(L.hyperattn_profile_enable(0))
+        check(L.hyperattn_profile_collect())
+        self.stats = {}
+        for i in range(L.hyperattn_profile_count()):
+            name = L.hyperattn_profile_name(i).decode()
+            launches = L.hyperattn_profile_launches(i)
+            if launches:
+                self.stats[name] = (launches, L.hyperattn_profile_total_ms(i))
+        return False

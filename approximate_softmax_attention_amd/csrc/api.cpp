@@ -1,0 +1,302 @@
+// The C ABI declared in include/hyperattn.h: argument validation, the launch
+// sequence of each entry point, the thread-local error message and the
+// event-based kernel timing.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+namespace ha {
+
+namespace {
+thread_local std::string g_error;
+}
+
+void set_error(const char* fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+}
+
+int fail(int code, const char* fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+// ------------------------------------------------------------ profiling
+namespace {
+
+struct ProfRecord {
+  int name;
+  hipEvent_t start, stop;
+  int device;
+};
+
+struct ProfName {
+  std::string name;
+  int64_t launches = 0;
+  double total_ms = 0.0;
+};
+
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_pending;
+std::vector<ProfRecord> g_free;
+std::vector<ProfName> g_names;
+
+int name_index(const char* name) {
+  for (size_t i = 0; i < g_names.size(); ++i)
+    if (g_names[i].name == name) return int(i);
+  g_names.push_back(ProfName{name});
+  return int(g_names.size() - 1);
+}
+
+}  // namespace
+
+ProfRange::ProfRange(const char* name, hipStream_t s) : slot(-1), stream(s) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  if (!g_prof_on) return;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return;
+  ProfRecord r{};
+  bool have = false;
+  for (size_t i = 0; i < g_free.size(); ++i)
+    if (g_free[i].device == dev) {
+      r = g_free[i];
+      g_free.erase(g_free.begin() + i);
+      have = true;
+      break;
+    }
+  if (!have) {
+    if (hipEventCreate(&r.start) != hipSuccess) return;
+    if (hipEventCreate(&r.stop) != hipSuccess) {
+      (void)hipEventDestroy(r.start);
+      return;
+    }
+    r.device = dev;
+  }
+  r.name = name_index(name);
+  if (hipEventRecord(r.start, s) != hipSuccess) {
+    g_free.push_back(r);
+    return;
+  }
+  g_pending.push_back(r);
+  slot = int(g_pending.size() - 1);
+}
+
+ProfRange::~ProfRange() {
+  if (slot < 0) return;
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  if (size_t(slot) < g_pending.size()) (void)hipEventRecord(g_pending[slot].stop, stream);
+}
+
+}  // namespace ha
+
+using namespace ha;
+
+extern "C" {
+
+const char* hyperattn_last_error(void) { return g_error.c_str(); }
+
+size_t hyperattn_workspace_bytes(int64_t n, int d, int heads, int causal, int b, int m,
+                                 int recursion_base, int r, int dtype) {
+  g_error.clear();
+  Plan p;
+  if (make_plan(p, n, d, heads, causal, b, m, recursion_base, r, dtype, true) != HA_OK) return 0;
+  return p.total;
+}
+
+int hyperattn_workspace_layout(int64_t n, int d, int heads, int causal, int b, int m,
+                               int recursion_base, int r, int dtype, int64_t* offsets,
+                               int64_t* bytes) {
+  g_error.clear();
+  if (!offsets || !bytes) return fail(HA_ERR_NULL, "offsets and bytes must not be NULL");
+  Plan p;
+  const int rc = make_plan(p, n, d, heads, causal, b, m, recursion_base, r, dtype, true);
+  if (rc != HA_OK) return rc;
+  for (int i = 0; i < HA_WS_COUNT; ++i) {
+    offsets[i] = p.off[i];
+    bytes[i] = p.bytes[i];
+  }
+  return HA_OK;
+}
+
+int sortlsh_hyperplanes(uint64_t seed, int heads, int r, int d, float* G_host) {
+  g_error.clear();
+  if (!G_host) return fail(HA_ERR_NULL, "G_host is NULL");
+  if (r < 1 || r > 8) return fail(HA_ERR_UNSUPPORTED, "r=%d not in [1, 8]", r);
+  if (d != 64 && d != 128) return fail(HA_ERR_UNSUPPORTED, "d=%d not 64 or 128", d);
+  if (heads < 0 || heads >= (1 << 16)) return fail(HA_ERR_SHAPE, "heads=%d out of range", heads);
+  host_hyperplanes(seed, heads, r, d, G_host);
+  return HA_OK;
+}
+
+int exact_attention_forward(const void* Q, const void* K, const void* V, void* O, float* lse,
+                            int64_t n, int d, int heads, int causal, int dtype, void* stream) {
+  g_error.clear();
+  if (dtype != HA_F32 && dtype != HA_BF16)
+    return fail(HA_ERR_UNSUPPORTED, "dtype %d is not HA_F32 or HA_BF16", dtype);
+  if (d != 64 && d != 128) return fail(HA_ERR_UNSUPPORTED, "d=%d not 64 or 128", d);
+  if (n < 0 || n >= (int64_t(1) << 31)) return fail(HA_ERR_SHAPE, "n=%lld out of range", (long long)n);
+  if (heads < 0 || heads >= (1 << 16)) return fail(HA_ERR_SHAPE, "heads=%d out of range", heads);
+  if (n == 0 || heads == 0) return HA_OK;
+  if (!Q || !K || !V || !O) return fail(HA_ERR_NULL, "Q, K, V and O must not be NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launch_exact(Q, K, V, O, lse, n, d, heads, causal ? 1 : 0, dtype, n, nullptr, nullptr, s);
+}
+
+int hyperattn_forward(const void* Q, const void* K, const void* V, void* O, float* lse,
+                      int64_t n, int d, int heads, int causal, int b, int m, int recursion_base,
+                      int r, uint64_t seed, int dtype, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  g_error.clear();
+  Plan p;
+  int rc = make_plan(p, n, d, heads, causal, b, m, recursion_base, r, dtype, true);
+  if (rc != HA_OK) return rc;
+  if (n == 0 || heads == 0) return HA_OK;
+  if (!Q || !K || !V || !O) return fail(HA_ERR_NULL, "Q, K, V and O must not be NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.causal && p.L == 0)   // the whole sequence is one base block
+    return launch_exact(Q, K, V, O, lse, n, d, heads, 1, dtype, n, nullptr, nullptr, s);
+  rc = check_workspace(p, workspace, workspace_bytes);
+  if (rc != HA_OK) return rc;
+  const float* G = nullptr;
+  if ((rc = device_hyperplanes(seed, heads, r, d, &G)) != HA_OK) return rc;
+  if ((rc = launch_hash(p, Q, K, V, G, workspace, s)) != HA_OK) return rc;
+  if ((rc = launch_vnorm_scan(p, workspace, s)) != HA_OK) return rc;
+  if ((rc = launch_sort(p, workspace, 2, s)) != HA_OK) return rc;
+  if ((rc = launch_samples(p, seed, workspace, s)) != HA_OK) return rc;
+  if ((rc = launch_bucket_attention(p, Q, K, V, O, lse, workspace, s)) != HA_OK) return rc;
+  if (p.causal)
+    rc = launch_exact(Q, K, V, O, lse, n, d, heads, 1, dtype, p.base_block, &p, workspace, s);
+  return rc;
+}
+
+int rowsum_estimate(const void* Q, const void* K, int64_t n, int d, int heads, int b, int m, int r,
+                    uint64_t seed, int dtype, float* log_d, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  g_error.clear();
+  Plan p;
+  int rc = make_plan(p, n, d, heads, 0, b, m, 1, r, dtype, false);
+  if (rc != HA_OK) return rc;
+  if (n == 0 || heads == 0) return HA_OK;
+  if (!Q || !K || !log_d) return fail(HA_ERR_NULL, "Q, K and log_d must not be NULL");
+  // the caller sizes the workspace with hyperattn_workspace_bytes(..., causal=0, ...),
+  // which covers this plan's smaller carve-up region by region
+  Plan full;
+  rc = make_plan(full, n, d, heads, 0, b, m, 1, r, dtype, true);
+  if (rc != HA_OK) return rc;
+  rc = check_workspace(full, workspace, workspace_bytes);
+  if (rc != HA_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float* G = nullptr;
+  if ((rc = device_hyperplanes(seed, heads, r, d, &G)) != HA_OK) return rc;
+  if ((rc = launch_hash(p, Q, K, nullptr, G, workspace, s)) != HA_OK) return rc;
+  if ((rc = launch_sort(p, workspace, 2, s)) != HA_OK) return rc;
+  if ((rc = launch_samples(p, seed, workspace, s)) != HA_OK) return rc;
+  return launch_bucket_attention(p, Q, K, nullptr, nullptr, log_d, workspace, s);
+}
+
+size_t sortlsh_hash_workspace_bytes(int64_t n, int heads, int with_perm) {
+  g_error.clear();
+  if (n < 0 || heads < 0) return 0;
+  return with_perm ? sort_single_scratch_bytes(n, heads) : 0;
+}
+
+int sortlsh_hash(const void* X, int64_t n, int d, int heads, int r, uint64_t seed, int dtype,
+                 uint8_t* codes, int32_t* perm, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  g_error.clear();
+  if (dtype != HA_F32 && dtype != HA_BF16)
+    return fail(HA_ERR_UNSUPPORTED, "dtype %d is not HA_F32 or HA_BF16", dtype);
+  if (d != 64 && d != 128) return fail(HA_ERR_UNSUPPORTED, "d=%d not 64 or 128", d);
+  if (r < 1 || r > 8) return fail(HA_ERR_UNSUPPORTED, "r=%d not in [1, 8]", r);
+  if (n < 0 || n >= (int64_t(1) << 31)) return fail(HA_ERR_SHAPE, "n=%lld out of range", (long long)n);
+  if (heads < 0 || heads >= (1 << 16)) return fail(HA_ERR_SHAPE, "heads=%d out of range", heads);
+  if (n == 0 || heads == 0) return HA_OK;
+  if (!X || !codes) return fail(HA_ERR_NULL, "X and codes must not be NULL");
+  const size_t need = perm ? sort_single_scratch_bytes(n, heads) : 0;
+  if (perm) {
+    if (!workspace) return fail(HA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+      return fail(HA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(HA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float* G = nullptr;
+  int rc;
+  if ((rc = device_hyperplanes(seed, heads, r, d, &G)) != HA_OK) return rc;
+  if ((rc = launch_hash_one(X, n, d, heads, r, dtype, G, codes, s)) != HA_OK) return rc;
+  if (perm) rc = launch_sort_single(codes, n, heads, perm, workspace, s);
+  return rc;
+}
+
+// ------------------------------------------------------------ profiling
+int hyperattn_profile_enable(int on) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  g_prof_on = on != 0;
+  return HA_OK;
+}
+
+int hyperattn_profile_collect(void) {
+  g_error.clear();
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  int cur = 0;
+  HA_HIP_TRY(hipGetDevice(&cur));
+  for (ProfRecord& r : g_pending) {
+    HA_HIP_TRY(hipSetDevice(r.device));
+    HA_HIP_TRY(hipEventSynchronize(r.stop));
+    float ms = 0.f;
+    HA_HIP_TRY(hipEventElapsedTime(&ms, r.start, r.stop));
+    g_names[r.name].launches += 1;
+    g_names[r.name].total_ms += ms;
+    g_free.push_back(r);
+  }
+  g_pending.clear();
+  HA_HIP_TRY(hipSetDevice(cur));
+  return HA_OK;
+}
+
+int hyperattn_profile_reset(void) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  for (ProfName& nm : g_names) {
+    nm.launches = 0;
+    nm.total_ms = 0.0;
+  }
+  return HA_OK;
+}
+
+int hyperattn_profile_count(void) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  return int(g_names.size());
+}
+
+const char* hyperattn_profile_name(int i) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  return (i >= 0 && size_t(i) < g_names.size()) ? g_names[i].name.c_str() : "";
+}
+
+int64_t hyperattn_profile_launches(int i) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  return (i >= 0 && size_t(i) < g_names.size()) ? g_names[i].launches : 0;
+}
+
+double hyperattn_profile_total_ms(int i) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  return (i >= 0 && size_t(i) < g_names.size()) ? g_names[i].total_ms : 0.0;
+}
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+// Internal declarations shared by the library's translation units: the plan
+// (sizes, recursion levels, workspace carve-up), element-type helpers, error
+// reporting and the kernel launchers. Nothing here is part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/hyperattn.h"
+
+namespace ha {
+
+constexpr int kMaxLevels = 21;      // 20 halvings + 1
+constexpr int kSortChunk = 2048;     // elements per sort work-group
+constexpr int kSortBins = 256;       // codes are < 2^r <= 256
+
+// ---------------------------------------------------------------- errors
+void set_error(const char* fmt, ...);
+int fail(int code, const char* fmt, ...);
+#define HA_HIP_TRY(expr)                                                     \
+  do {                                                                       \
+    hipError_t e_ = (expr);                                                  \
+    if (e_ != hipSuccess)                                                    \
+      return ::ha::fail(HA_ERR_HIP, "%s failed: %s (%s:%d)", #expr,          \
+                        hipGetErrorString(e_), __FILE__, __LINE__);          \
+  } while (0)
+#define HA_LAUNCH_CHECK(name)                                                \
+  do {                                                                       \
+    hipError_t e_ = hipGetLastError();                                       \
+    if (e_ != hipSuccess)                                                    \
+      return ::ha::fail(HA_ERR_HIP, "launch of %s failed: %s", name,         \
+                        hipGetErrorString(e_));                              \
+  } while (0)
+
+// ------------------------------------------------------------- profiling
+// Brackets one launch with events on its stream when profiling is enabled.
+struct ProfRange {
+  ProfRange(const char* name, hipStream_t s);
+  ~ProfRange();
+  int slot;
+  hipStream_t stream;
+};
+
+// ------------------------------------------------------- level geometry
+// One level of the flattened causal recursion (or the single non-causal
+// sub-problem). Level l (0-based) has nseg sub-problems of size h: the
+// queries of sub-problem s are rows [2sh + h, 2sh + 2h), its keys rows
+// [2sh, 2sh + h) (non-causal: both [0, n)). The node id is 2^l + s.
+struct Level {
+  int64_t h;          // sub-problem size n_k
+  int64_t nseg;       // sub-problems at this level
+  int b_eff;          // bucket size min(b, h)
+  int64_t nbucket;    // h / b_eff
+  int64_t sort_cps;   // sort chunks per segment
+  int64_t sort_wg0;   // first sort chunk work-group of this level
+  int64_t seg_wg0;    // first per-segment work-group of this level
+  int64_t att_wg0;    // first attention work-group of this level
+  int64_t att_qch;    // query chunks per bucket
+};
+
+struct LevelTable {
+  int count;
+  int causal;
+  int64_t n;
+  Level lv[kMaxLevels];
+};
+
+struct Plan {
+  int64_t n = 0;
+  int d = 0, heads = 0, causal = 0, b = 0, m = 0, base = 0, r = 0, dtype = 0;
+  int esize = 0;              // bytes per input element
+  bool product = true;        // false for rowsum_estimate (no V)
+  int L = 0;                  // sub-problem levels (0: causal with n <= base)
+  int64_t S = 0;              // slots per level per head: n or n / 2
+  int64_t nodes = 0;          // 2^L - 1 (causal) or 1
+  int64_t base_block = 0;     // causal diagonal block size n >> L
+  int64_t vblocks = 0;        // V-norm blocks per head
+  int64_t sort_wgs = 0;       // sort chunk work-groups (all levels/heads/sides)
+  int64_t seg_wgs = 0;        // per-segment work-groups (all levels/heads/sides)
+  int64_t att_wgs = 0;        // bucket attention work-groups
+  LevelTable table{};
+  int64_t off[HA_WS_COUNT] = {};
+  int64_t bytes[HA_WS_COUNT] = {};
+  size_t total = 0;
+};
+
+constexpr int kVnormBlock = 256;     // rows per V-norm work-group
+constexpr int kAttnQ = 128;          // query rows per attention work-group
+
+int make_plan(Plan& p, int64_t n, int d, int heads, int causal, int b, int m,
+              int base, int r, int dtype, bool product);
+int check_workspace(const Plan& p, const void* ws, size_t ws_bytes);
+
+// Hyperplanes on the device for (seed, heads, r, d); cached per device.
+int device_hyperplanes(uint64_t seed, int heads, int r, int d, const float** out);
+void host_hyperplanes(uint64_t seed, int heads, int r, int d, float* G);
+
+// --------------------------------------------------------------- launchers
+// All return HA_OK or HA_ERR_HIP; arguments are validated by the caller.
+int launch_hash(const Plan& p, const void* Q, const void* K, const void* V,
+                const float* G, void* ws, hipStream_t s);
+int launch_hash_one(const void* X, int64_t n, int d, int heads, int r, int dtype,
+                    const float* G, uint8_t* codes, hipStream_t s);
+int launch_vnorm_scan(const Plan& p, void* ws, hipStream_t s);
+int launch_sort(const Plan& p, void* ws, int sides, hipStream_t s);
+int launch_sort_single(const uint8_t* codes, int64_t n, int heads, int32_t* perm,
+                       void* scratch, hipStream_t s);
+int launch_samples(const Plan& p, uint64_t seed, void* ws, hipStream_t s);
+int launch_bucket_attention(const Plan& p, const void* Q, const void* K,
+                            const void* V, void* O, float* lse, void* ws,
+                            hipStream_t s);
+int launch_exact(const void* Q, const void* K, const void* V, void* O, float* lse,
+                 int64_t n, int d, int heads, int causal, int dtype,
+                 int64_t block, const Plan* merge, const void* ws, hipStream_t s);
+
+size_t sort_single_scratch_bytes(int64_t n, int heads);
+
+inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace ha

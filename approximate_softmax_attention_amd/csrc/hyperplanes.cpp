@@ -1,0 +1,104 @@
+// The r Gaussian hyperplanes per head that the hash uses (HA page,
+// "Algorithm", Definition 1: a Hamming-sorted LSH; read here as signs of
+// projections on Gaussian hyperplanes).
+//
+// Each element comes from two counter-based draws of SplitMix64 (Steele, Lea
+// and Flood, OOPSLA 2014), turned into one normal by the Box-Muller transform
+// (Box and Muller, 1958) in fp64 with the C library's log, sqrt and cos, and
+// rounded to fp32. They are generated on the host so that the values are
+// fixed by the C library, and kept on each device in a small cache keyed by
+// (seed, heads, r, d).
+#include <cmath>
+#include <mutex>
+#include <vector>
+
+#include "common.h"
+
+namespace ha {
+
+namespace {
+
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+
+uint64_t mix64(uint64_t x) {
+  uint64_t z = x + kGamma;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+uint64_t draw(uint64_t key, uint64_t purpose, uint64_t head, uint64_t node,
+              uint64_t counter) {
+  return mix64(key ^ ((purpose << 60) | (head << 44) | (node << 24) | counter));
+}
+
+struct Entry {
+  int device;
+  uint64_t seed;
+  int heads, r, d;
+  float* ptr;
+  uint64_t stamp;
+};
+
+std::mutex g_mu;
+std::vector<Entry> g_cache;
+uint64_t g_clock = 0;
+constexpr size_t kCacheEntries = 16;
+
+}  // namespace
+
+void host_hyperplanes(uint64_t seed, int heads, int r, int d, float* G) {
+#pragma clang fp contract(off)
+  const uint64_t key = mix64(seed);
+  const double two_pi = 2.0 * M_PI;
+  for (int h = 0; h < heads; ++h)
+    for (int k = 0; k < r; ++k)
+      for (int t = 0; t < d; ++t) {
+        const uint64_t e = uint64_t(k) * d + t;
+        const uint64_t a = draw(key, 1, h, 0, 2 * e);
+        const uint64_t b = draw(key, 1, h, 0, 2 * e + 1);
+        const double u1 = double((a >> 11) + 1) * 0x1p-53;
+        const double u2 = double(b >> 11) * 0x1p-53;
+        const double g = std::sqrt(-2.0 * std::log(u1)) * std::cos(two_pi * u2);
+        G[(int64_t(h) * r + k) * d + t] = static_cast<float>(g);
+      }
+}
+
+int device_hyperplanes(uint64_t seed, int heads, int r, int d, const float** out) {
+  int dev = 0;
+  HA_HIP_TRY(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lock(g_mu);
+  for (Entry& e : g_cache)
+    if (e.device == dev && e.seed == seed && e.heads == heads && e.r == r && e.d == d) {
+      e.stamp = ++g_clock;
+      *out = e.ptr;
+      return HA_OK;
+    }
+  if (g_cache.size() >= kCacheEntries) {
+    size_t old = 0;
+    for (size_t i = 1; i < g_cache.size(); ++i)
+      if (g_cache[i].stamp < g_cache[old].stamp) old = i;
+    // earlier launches may still read the evicted table
+    int cur = dev;
+    HA_HIP_TRY(hipSetDevice(g_cache[old].device));
+    HA_HIP_TRY(hipDeviceSynchronize());
+    HA_HIP_TRY(hipFree(g_cache[old].ptr));
+    HA_HIP_TRY(hipSetDevice(cur));
+    g_cache.erase(g_cache.begin() + old);
+  }
+  const size_t count = size_t(heads) * r * d;
+  std::vector<float> host(count);
+  host_hyperplanes(seed, heads, r, d, host.data());
+  float* ptr = nullptr;
+  HA_HIP_TRY(hipMalloc(&ptr, count * sizeof(float)));
+  hipError_t e = hipMemcpy(ptr, host.data(), count * sizeof(float), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(ptr);
+    return fail(HA_ERR_HIP, "hipMemcpy of hyperplanes failed: %s", hipGetErrorString(e));
+  }
+  g_cache.push_back(Entry{dev, seed, heads, r, d, ptr, ++g_clock});
+  *out = ptr;
+  return HA_OK;
+}
+
+}  // namespace ha

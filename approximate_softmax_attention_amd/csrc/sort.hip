@@ -1,0 +1,260 @@
+// sortLSH ordering (HA page, "Algorithm", Algorithm 1: keys and queries are
+// sorted by their Hamming-sorted hash and cut into equal-size buckets).
+//
+// Every (level, head, side, sub-problem) segment is sorted stably by
+// (code, index) with a counting sort over the 2^r <= 256 code values. All
+// segments of all levels are independent once the codes exist, so each of
+// the three passes covers every segment in one launch:
+//   1. per chunk of 2048 elements: a 256-bin histogram (LDS counters);
+//   2. per segment: exclusive offsets, bin-major then chunk-minor;
+//   3. per chunk: stable ranks (wave ballots find the earlier lanes with the
+//      same code, LDS counts carry the order across waves and batches) and
+//      the scatter of perm (sorted position -> row) and rank (slot -> sorted
+//      position, keys only).
+#include "common.h"
+#include "device_util.h"
+
+namespace ha {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+struct SortArgs {
+  LevelTable table;
+  int heads;
+  int sides;
+  int64_t n;
+  int64_t S;                    // slots per level per head
+  const uint8_t* codes[2];      // [heads][n] per side
+  int32_t* perm[2];             // [L][heads][S] per side
+  int32_t* rank;                // [L][heads][S] for side 1, or null
+  uint32_t* hist;               // [chunks][256]
+  uint32_t* offs;               // [chunks][256]
+};
+
+struct ChunkRef {
+  int lv, head, side;
+  int64_t seg, chunk, h;
+};
+
+__device__ __forceinline__ int find_level(const LevelTable& t, int64_t w, int which) {
+  int lv = 0;
+  for (int l = 1; l < t.count; ++l) {
+    const int64_t s = which == 0 ? t.lv[l].sort_wg0 : t.lv[l].seg_wg0;
+    if (w >= s) lv = l;
+  }
+  return lv;
+}
+
+__device__ __forceinline__ ChunkRef decode_chunk(const SortArgs& a, int64_t w) {
+  ChunkRef c;
+  c.lv = find_level(a.table, w, 0);
+  const Level& L = a.table.lv[c.lv];
+  int64_t rem = w - L.sort_wg0;
+  c.chunk = rem % L.sort_cps;
+  rem /= L.sort_cps;
+  c.seg = rem % L.nseg;
+  rem /= L.nseg;
+  c.side = int(rem % a.sides);
+  c.head = int(rem / a.sides);
+  c.h = L.h;
+  return c;
+}
+
+// Global row of element t of a segment: queries sit in the second half of
+// their block, keys in the first (non-causal: both cover [0, n)).
+__device__ __forceinline__ int64_t seg_row(const SortArgs& a, int side, int64_t seg,
+                                           int64_t h, int64_t t) {
+  if (!a.table.causal) return t;
+  return 2 * seg * h + (side == 0 ? h : 0) + t;
+}
+
+__global__ __launch_bounds__(kThreads) void sort_hist_kernel(SortArgs a) {
+  __shared__ uint32_t hist[kSortBins];
+  const int64_t w = blockIdx.x;
+  const ChunkRef c = decode_chunk(a, w);
+  hist[threadIdx.x] = 0;
+  __syncthreads();
+  const uint8_t* codes = a.codes[c.side] + int64_t(c.head) * a.n;
+  const int64_t t0 = c.chunk * kSortChunk;
+  const int64_t t1 = t0 + kSortChunk < c.h ? t0 + kSortChunk : c.h;
+  for (int64_t t = t0 + threadIdx.x; t < t1; t += kThreads)
+    atomicAdd(&hist[codes[seg_row(a, c.side, c.seg, c.h, t)]], 1u);
+  __syncthreads();
+  a.hist[w * kSortBins + threadIdx.x] = hist[threadIdx.x];
+}
+
+__global__ __launch_bounds__(kThreads) void sort_offsets_kernel(SortArgs a) {
+  __shared__ uint32_t wtot[kThreads / 64];
+  const int64_t w = blockIdx.x;
+  const int lv = find_level(a.table, w, 1);
+  const Level& L = a.table.lv[lv];
+  int64_t rem = w - L.seg_wg0;
+  const int64_t seg = rem % L.nseg;
+  rem /= L.nseg;
+  const int side = int(rem % a.sides);
+  const int head = int(rem / a.sides);
+  const int64_t cw0 = L.sort_wg0 + ((int64_t(head) * a.sides + side) * L.nseg + seg) * L.sort_cps;
+  const int bin = threadIdx.x;
+  uint32_t running = 0;
+  for (int64_t c = 0; c < L.sort_cps; ++c) {
+    const uint32_t v = a.hist[(cw0 + c) * kSortBins + bin];
+    a.offs[(cw0 + c) * kSortBins + bin] = running;
+    running += v;
+  }
+  // exclusive scan of the per-bin totals across the block
+  uint64_t incl = wave_incl_scan(uint64_t(running));
+  const int wave = threadIdx.x >> 6;
+  if (lane_id() == 63) wtot[wave] = uint32_t(incl);
+  __syncthreads();
+  uint32_t before = 0;
+  for (int i = 0; i < wave; ++i) before += wtot[i];
+  const uint32_t base = before + uint32_t(incl) - running;
+  for (int64_t c = 0; c < L.sort_cps; ++c) a.offs[(cw0 + c) * kSortBins + bin] += base;
+}
+
+__global__ __launch_bounds__(kThreads) void sort_scatter_kernel(SortArgs a) {
+  __shared__ uint32_t run[kSortBins];
+  __shared__ uint32_t wcnt[kThreads / 64][kSortBins];
+  const int64_t w = blockIdx.x;
+  const ChunkRef c = decode_chunk(a, w);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = lane_id();
+  run[tid] = a.offs[w * kSortBins + tid];
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) wcnt[i][tid] = 0;
+  __syncthreads();
+  const uint8_t* codes = a.codes[c.side] + int64_t(c.head) * a.n;
+  const int64_t slot0 = (int64_t(c.lv) * a.heads + c.head) * a.S + c.seg * c.h;
+  int32_t* perm = a.perm[c.side] + slot0;
+  int32_t* rank = (a.rank && c.side == 1) ? a.rank + slot0 : nullptr;
+  const int64_t t0 = c.chunk * kSortChunk;
+  const int64_t t1 = t0 + kSortChunk < c.h ? t0 + kSortChunk : c.h;
+  const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
+  for (int64_t base = t0; base < t1; base += kThreads) {
+    const int64_t t = base + tid;
+    const bool valid = t < t1;
+    const int64_t row = seg_row(a, c.side, c.seg, c.h, t);
+    const uint32_t code = valid ? codes[row] : 0u;
+    uint64_t eq = __ballot(valid);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const bool bit = (code >> k) & 1u;
+      const uint64_t bk = __ballot(valid && bit);
+      eq &= bit ? bk : ~bk;
+    }
+    const uint32_t local = __popcll(eq & lt_mask);
+    if (valid && local == 0) wcnt[wave][code] = uint32_t(__popcll(eq));
+    __syncthreads();
+    if (valid) {
+      uint32_t pos = run[code] + local;
+      for (int i = 0; i < wave; ++i) pos += wcnt[i][code];
+      perm[pos] = int32_t(row);
+      if (rank) rank[t] = int32_t(pos);
+    }
+    __syncthreads();
+    uint32_t add = 0;
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) {
+      add += wcnt[i][tid];
+      wcnt[i][tid] = 0;
+    }
+    run[tid] += add;
+    __syncthreads();
+  }
+}
+
+// Recompute the work-group offsets of the table for the given side count.
+int64_t retable(LevelTable& t, int heads, int sides, int64_t* seg_total) {
+  int64_t chunks = 0, segs = 0;
+  for (int l = 0; l < t.count; ++l) {
+    Level& v = t.lv[l];
+    v.sort_wg0 = chunks;
+    chunks += int64_t(heads) * sides * v.nseg * v.sort_cps;
+    v.seg_wg0 = segs;
+    segs += int64_t(heads) * sides * v.nseg;
+  }
+  *seg_total = segs;
+  return chunks;
+}
+
+int run_sort(SortArgs& a, int64_t chunks, int64_t segs, hipStream_t s) {
+  if (chunks == 0) return HA_OK;
+  {
+    ProfRange pr("sort_hist", s);
+    hipLaunchKernelGGL(sort_hist_kernel, dim3(unsigned(chunks)), dim3(kThreads), 0, s, a);
+    HA_LAUNCH_CHECK("sort_hist");
+  }
+  {
+    ProfRange pr("sort_offsets", s);
+    hipLaunchKernelGGL(sort_offsets_kernel, dim3(unsigned(segs)), dim3(kThreads), 0, s, a);
+    HA_LAUNCH_CHECK("sort_offsets");
+  }
+  {
+    ProfRange pr("sort_scatter", s);
+    hipLaunchKernelGGL(sort_scatter_kernel, dim3(unsigned(chunks)), dim3(kThreads), 0, s, a);
+    HA_LAUNCH_CHECK("sort_scatter");
+  }
+  return HA_OK;
+}
+
+}  // namespace
+
+int launch_sort(const Plan& p, void* ws, int sides, hipStream_t s) {
+  char* w = static_cast<char*>(ws);
+  SortArgs a;
+  a.table = p.table;
+  a.heads = p.heads;
+  a.sides = sides;
+  a.n = p.n;
+  a.S = p.S;
+  a.codes[0] = reinterpret_cast<const uint8_t*>(w + p.off[HA_WS_CODES_Q]);
+  a.codes[1] = reinterpret_cast<const uint8_t*>(w + p.off[HA_WS_CODES_K]);
+  a.perm[0] = reinterpret_cast<int32_t*>(w + p.off[HA_WS_PERM_Q]);
+  a.perm[1] = reinterpret_cast<int32_t*>(w + p.off[HA_WS_PERM_K]);
+  a.rank = reinterpret_cast<int32_t*>(w + p.off[HA_WS_RANK_K]);
+  a.hist = reinterpret_cast<uint32_t*>(w + p.off[HA_WS_SORT_HIST]);
+  a.offs = reinterpret_cast<uint32_t*>(w + p.off[HA_WS_SORT_OFFS]);
+  int64_t segs = 0;
+  const int64_t chunks = retable(a.table, p.heads, sides, &segs);
+  return run_sort(a, chunks, segs, s);
+}
+
+size_t sort_single_scratch_bytes(int64_t n, int heads) {
+  const int64_t chunks = int64_t(heads) * ceil_div(n, kSortChunk);
+  return size_t(2 * align256(chunks * kSortBins * 4));
+}
+
+int launch_sort_single(const uint8_t* codes, int64_t n, int heads, int32_t* perm,
+                       void* scratch, hipStream_t s) {
+  SortArgs a;
+  a.table.count = 1;
+  a.table.causal = 0;
+  a.table.n = n;
+  Level& v = a.table.lv[0];
+  v.h = n;
+  v.nseg = 1;
+  v.b_eff = 1;
+  v.nbucket = n;
+  v.sort_cps = ceil_div(n, kSortChunk);
+  v.att_wg0 = 0;
+  v.att_qch = 0;
+  a.heads = heads;
+  a.sides = 1;
+  a.n = n;
+  a.S = n;
+  a.codes[0] = a.codes[1] = codes;
+  a.perm[0] = a.perm[1] = perm;
+  a.rank = nullptr;
+  const int64_t chunks = int64_t(heads) * v.sort_cps;
+  a.hist = static_cast<uint32_t*>(scratch);
+  a.offs = reinterpret_cast<uint32_t*>(static_cast<char*>(scratch) +
+                                       align256(chunks * kSortBins * 4));
+  int64_t segs = 0;
+  const int64_t c2 = retable(a.table, heads, 1, &segs);
+  return run_sort(a, c2, segs, s);
+}
+
+}  // namespace ha

@@ -1,0 +1,221 @@
+"""Benchmark: causal HyperAttention forward on one MI355X.
+
+One step is one full hyperattn_forward (hash, V-norm weights, sortLSH sorts,
+samples, bucket/sample attention on every recursion level, exact base case
+with the merge) over one batch of synthetic inputs already resident in HBM.
+Default workload: batch 1, 32 heads, n = 131072, d = 128, bf16, b = m = 256,
+r = 8, recursion base 4096 (RoPE on Q and K).
+
+Prints one JSON line: tokens/s, the roofline of the dominant kernel (timed
+live with the library's hipEvents on the launch stream), the library's own
+exact causal attention at the same shape, and the CPU oracle timed on a
+bounded sample (one head of the same workload).
+"""
+
+import argparse
+import concurrent.futures as cf
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal HyperAttention fwd tokens/s at n=131k,d=128,32 heads; % MFMA peak"
+PEAK_BF16 = 2.5e15        # MI355X dense bf16 MFMA, FLOP/s
+PEAK_FP32_MFMA = 157.3e12
+PEAK_HBM = 8.0e12         # bytes/s
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_flops(w):
+    """MFMA flops the method must do, per kernel (per launch)."""
+    H, n, d, b, m = w.heads, w.n, w.d, w.b, w.m
+    out = {}
+    if w.causal:
+        L, size = 0, n
+        while size > w.recursion_base:
+            size //= 2
+            L += 1
+        rows = 0
+        per_row = 0.0
+        for lv in range(L):
+            h = n >> (lv + 1)
+            be = min(b, h)
+            mm = min(m, h)
+            per_row += (n // 2) * (4 * be * d + 2 * mm * d + 4 * mm * d)
+        out["bucket_attention"] = H * per_row
+        B = size
+        out["exact_base_merge"] = H * (n // B) * 4.0 * d * B * (B + 1) / 2
+    else:
+        be, mm = min(b, n), min(m, n)
+        out["bucket_attention"] = H * n * (4 * be * d + 2 * mm * d + 4 * mm * d)
+    return out
+
+
+def exact_flops(w):
+    H, n, d = w.heads, w.n, w.d
+    return H * 4.0 * d * (n * (n + 1) / 2 if w.causal else n * n)
+
+
+def make_device_inputs(w, torch):
+    from approximate_softmax_attention_amd import workloads as wl
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    Q = torch.empty((w.heads, w.n, w.d), dtype=dt, device="cuda")
+    K, V = torch.empty_like(Q), torch.empty_like(Q)
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+
+    def one(h):
+        q, k, v, _ = wl.make_head(w, h)
+        return h, q, k, v
+
+    with cf.ThreadPoolExecutor(workers) as ex:
+        for h, q, k, v in ex.map(one, range(w.heads)):
+            Q[h].copy_(torch.from_numpy(q).to(dt))
+            K[h].copy_(torch.from_numpy(k).to(dt))
+            V[h].copy_(torch.from_numpy(v).to(dt))
+    torch.cuda.synchronize()
+    return Q, K, V
+
+
+def cpu_baseline(w):
+    """The oracle as it stands, on one head of the workload, scaled to all heads."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from approximate_softmax_attention_amd import workloads as wl
+    from oracle import hyperattention as oha
+    q, k, v, _ = wl.make_head(w, 0)
+    t0 = time.perf_counter()
+    oha.hyperattention(q[None], k[None], v[None], causal=w.causal, b=w.b, m=w.m, r=w.r,
+                       recursion_base=w.recursion_base, seed=w.method_seed)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    per_forward = dt * w.heads
+    return {"value": w.n / per_forward, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"1 of {w.heads} heads of the same workload (full n={w.n} "
+                      f"forward, fp64 numpy), {dt:.1f} s, scaled x{w.heads}",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-exact", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "HyperAttention shards by head with no communication, so the "
+              "whole-job rate at N GPUs is not measured here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from approximate_softmax_attention_amd import api, workloads as wl
+    from approximate_softmax_attention_amd._lib import HA_BF16, HA_F32
+
+    w = wl.WORKLOADS[args.workload or wl.HEADLINE]
+    log(f"workload {w.name}: generating inputs")
+    Q, K, V = make_device_inputs(w, torch)
+    dtc = HA_BF16 if w.dtype == "bf16" else HA_F32
+    nb = api.workspace_bytes(w.n, w.d, w.heads, causal=w.causal, b=w.b, m=w.m, r=w.r,
+                             recursion_base=w.recursion_base, dtype=dtc)
+    ws = api.alloc_workspace(nb, "cuda")
+    O = torch.empty_like(Q)
+    lse = torch.empty((w.heads, w.n), dtype=torch.float32, device="cuda")
+    kw = dict(causal=w.causal, b=w.b, m=w.m, r=w.r, recursion_base=w.recursion_base,
+              seed=w.method_seed, workspace=ws, out=O, lse_out=lse)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        api.forward(Q, K, V, **kw)
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with api.KernelTimer() as kt:
+        torch.cuda.synchronize()
+        e0.record(stream)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            api.forward(Q, K, V, **kw)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    tokens_per_s = w.n / (ms / 1e3)
+    log(f"{ms:.3f} ms/step, {tokens_per_s:.4g} tokens/s (wall {wall / args.steps * 1e3:.3f} ms)")
+
+    flops = algorithmic_flops(w)
+    kernels = {}
+    for name, (launches, total) in kt.stats.items():
+        kernels[name] = {"launches": launches, "avg_ms": total / launches}
+    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches"])
+    peak = PEAK_BF16 if w.dtype == "bf16" else PEAK_FP32_MFMA
+    for name, f in flops.items():
+        if name in kernels:
+            kernels[name]["tflops"] = f / (kernels[name]["avg_ms"] / 1e3) / 1e12
+            kernels[name]["mfma_frac"] = f / (kernels[name]["avg_ms"] / 1e3) / peak
+    if dom in flops:
+        ach = flops[dom] / (kernels[dom]["avg_ms"] / 1e3)
+        roofline = {"bound": "mfma", "achieved": ach / 1e12, "peak": peak / 1e12,
+                    "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
+                    "kernel": dom, "flops_per_launch": flops[dom]}
+    else:
+        roofline = {"bound": "hbm", "achieved": None, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                    "frac": None, "traffic": None, "kernel": dom}
+    total_flops = sum(flops.values())
+
+    result = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded iid N(0,1), RoPE on Q,K)",
+        "config": {"workload": w.name, "batch": 1, "heads": w.heads, "seq_len": w.n,
+                   "head_dim": w.d, "causal": w.causal, "b": w.b, "m": w.m, "r": w.r,
+                   "recursion_base": w.recursion_base, "parallelism": "single-gpu"},
+        "mfma_frac_whole_forward": total_flops / (ms / 1e3) / peak,
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+
+    if not args.no_exact:
+        log("timing the library's exact attention at the same shape")
+        Oe = torch.empty_like(Q)
+        api.exact(Q, K, V, causal=w.causal, out=Oe)
+        torch.cuda.synchronize()
+        reps = 2
+        e0.record(stream)
+        for _ in range(reps):
+            api.exact(Q, K, V, causal=w.causal, out=Oe)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ems = e0.elapsed_time(e1) / reps
+        diff = (O.float() - Oe.float()).pow(2).sum().sqrt() / Oe.float().pow(2).sum().sqrt()
+        result["exact_baseline"] = {
+            "ms": ems, "tokens_per_s": w.n / (ems / 1e3),
+            "tflops": exact_flops(w) / (ems / 1e3) / 1e12,
+            "mfma_frac": exact_flops(w) / (ems / 1e3) / peak,
+            "speedup_of_hyperattention": ems / ms,
+            "rel_frobenius_err_vs_exact": float(diff)}
+        del Oe
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on one head")
+        result["cpu_baseline"] = cpu_baseline(w)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

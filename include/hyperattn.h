@@ -1,0 +1,219 @@
+/*
+ * hyperattn.h — C ABI of the MI355X (gfx950) HyperAttention library.
+ *
+ * Source of every operation below: the Japanese article on HyperAttention at
+ * nearauto.com/p/20145.html (a summary of arXiv 2310.05869), cited as
+ * "HA page" with its section:
+ *   "Method overview"  — Att = D^-1 A V, A = exp(QK^T), D = diag(A 1);
+ *                        product sampled by the row norms of V; D estimated
+ *                        with uniform column sampling.
+ *   "Algorithm"        — Definition 1 (Hamming-sorted LSH), Algorithm 1
+ *                        (sortLSH buckets), Algorithm 2 (ApproxD), Algorithm 3
+ *                        (HyperAttention), Figure 2 / Algorithm 4 (causal
+ *                        recursion into two diagonal blocks and A_21).
+ *   "Monkey-patching"  — recursion to a small exact base case; b = m = 256.
+ *   "Single self-attention layer" — causal mode splits Q, K, V and merges
+ *                        the attention outputs.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are [heads][n][d], row-major, d contiguous, batch folded into
+ *   heads. Element type is given by `dtype`: HA_F32 (float) or HA_BF16
+ *   (bfloat16 bit patterns, 2 bytes). d must be 64 or 128.
+ * - Scores are s_ij = <q_i, k_j> / sqrt(d). lse outputs are the natural log
+ *   of the row's normaliser in these units (fp32, [heads][n]).
+ * - Pointers named Q, K, V, O, lse, codes, perm, log_d and workspace are
+ *   DEVICE pointers owned by the caller; the library never frees them and
+ *   keeps no pointer to them after the call returns. G_host is a host pointer.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *   device work is enqueued on it asynchronously; entry points return once
+ *   the work is enqueued. The caller synchronises before reading outputs.
+ * - Return value: HA_OK (0) or a negative HA_ERR_* code. Arguments are
+ *   validated on the host before anything is enqueued; on error nothing is
+ *   enqueued and hyperattn_last_error() describes the problem. No C++
+ *   exception crosses this boundary.
+ * - Results are deterministic: the same inputs, sizes and seed give
+ *   bit-identical outputs (no floating-point atomics are used).
+ * - Workspaces must be 256-byte aligned and at least the size the matching
+ *   *_workspace_bytes function returns; their contents on entry do not matter.
+ * - n == 0 or heads == 0 is valid and enqueues nothing.
+ */
+#ifndef HYPERATTN_H
+#define HYPERATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum ha_dtype { HA_F32 = 0, HA_BF16 = 1 };
+
+enum ha_status {
+  HA_OK = 0,
+  HA_ERR_NULL = -1,        /* a required pointer is NULL                     */
+  HA_ERR_SHAPE = -2,       /* sizes inconsistent (see each entry point)      */
+  HA_ERR_UNSUPPORTED = -3, /* d not in {64,128}, r not in [1,8], bad dtype   */
+  HA_ERR_WORKSPACE = -4,   /* workspace NULL/too small/misaligned            */
+  HA_ERR_HIP = -5          /* a HIP runtime call failed (message has detail) */
+};
+
+/*
+ * hyperattn_forward — HyperAttention forward pass (HA page, "Algorithm",
+ * Algorithms 1-3; causal: Figure 2 / Algorithm 4 with the base case of
+ * "Monkey-patching" and the merge of "Single self-attention layer").
+ *
+ * Per head, with r Gaussian hyperplanes drawn from `seed`:
+ *  1. sortLSH: hash every row of Q and K (Gray rank of the hyperplane sign
+ *     pattern), then, per sub-problem, sort queries and keys stably by
+ *     (code, index) and cut both into buckets of b_eff = min(b, n_k) rows.
+ *  2. ApproxD: d~_i = sum over the keys in i's bucket of e^{s_ij}
+ *       + (n_k/m) * sum over m uniform key samples outside i's bucket.
+ *  3. Product: N_i = sum over bucket keys of e^{s_ij} V_j
+ *       + sum over m V-row-norm samples j_t (p_j ∝ |V_j|^2) outside i's
+ *         bucket of (1/(m p_j)) e^{s_ij} V_j;   O_i = N_i / d~_i.
+ *     When m >= n_k both samples are every key of the range, weight 1.
+ *  Non-causal: one sub-problem with queries and keys [0, n).
+ *  Causal: while a diagonal block is larger than recursion_base, split it in
+ *  halves; the lower-left block (queries of the second half, keys of the
+ *  first) is a sub-problem as above; blocks of size <= recursion_base get
+ *  exact causal attention; every row merges its partial results by
+ *  log-sum-exp.
+ *
+ * Q, K, V: inputs [heads][n][d]. O: output [heads][n][d], same dtype.
+ * lse: optional output [heads][n] fp32 (log d~ merged over the row's parts).
+ * b >= 1 bucket size; m >= 1 samples per estimator; recursion_base >= 1
+ * (ignored when causal == 0); r in [1, 8] hyperplanes; seed selects
+ * hyperplanes and samples.
+ * HA_ERR_SHAPE if b_eff does not divide a sub-problem size, if a causal block
+ * to be split has odd size, or if n >= 2^31.
+ * workspace: >= hyperattn_workspace_bytes(...) with the same arguments.
+ */
+int hyperattn_forward(const void* Q, const void* K, const void* V, void* O,
+                      float* lse, int64_t n, int d, int heads, int causal,
+                      int b, int m, int recursion_base, int r, uint64_t seed,
+                      int dtype, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Bytes of workspace hyperattn_forward needs for these sizes (0 on invalid
+ * arguments; hyperattn_last_error() then says why). */
+size_t hyperattn_workspace_bytes(int64_t n, int d, int heads, int causal,
+                                 int b, int m, int recursion_base, int r,
+                                 int dtype);
+
+/*
+ * sortlsh_hash — the Hamming-sorted LSH of Definition 1 (HA page,
+ * "Algorithm") applied to every row of X, and optionally Algorithm 1's
+ * stable sort of each head's rows by (code, index).
+ * codes[h][i] = GrayRank(sum_k [<x_i, g_hk> > 0] 2^k), where the sign is that
+ * of the fp64 sum of x_it * g_hkt taken in order t = 0..d-1 and g_hk are the
+ * hyperplanes sortlsh_hyperplanes(seed, heads, r, d) returns.
+ * codes: output [heads][n] uint8. perm: optional output [heads][n] int32,
+ * perm[h][p] = the row at sorted position p.
+ * workspace: >= sortlsh_hash_workspace_bytes(n, heads, perm != NULL).
+ */
+int sortlsh_hash(const void* X, int64_t n, int d, int heads, int r,
+                 uint64_t seed, int dtype, uint8_t* codes, int32_t* perm,
+                 void* workspace, size_t workspace_bytes, void* stream);
+size_t sortlsh_hash_workspace_bytes(int64_t n, int heads, int with_perm);
+
+/*
+ * exact_attention_forward — Att = D^-1 A V with A = exp(QK^T / sqrt(d)) and
+ * D = diag(A 1) (HA page, "Method overview"); causal == 1 applies the mask
+ * j <= i (Figure 2's M^C). Needs no workspace.
+ * O: output [heads][n][d], same dtype; lse: optional output [heads][n].
+ */
+int exact_attention_forward(const void* Q, const void* K, const void* V,
+                            void* O, float* lse, int64_t n, int d, int heads,
+                            int causal, int dtype, void* stream);
+
+/*
+ * rowsum_estimate — Algorithm 2 (ApproxD) alone, non-causal (HA page,
+ * "Algorithm"): log_d[h][i] = log d~_i with d~ as in hyperattn_forward step 2
+ * (same hyperplanes, buckets and uniform samples for the same seed).
+ * log_d: output [heads][n] fp32.
+ * workspace: >= hyperattn_workspace_bytes(n, d, heads, 0, b, m, 1, r, dtype).
+ */
+int rowsum_estimate(const void* Q, const void* K, int64_t n, int d, int heads,
+                    int b, int m, int r, uint64_t seed, int dtype,
+                    float* log_d, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * sortlsh_hyperplanes — host-only: the r Gaussian hyperplanes per head the
+ * hash uses (HA page, "Algorithm", Definition 1; hash family as read here).
+ * G_host[h][k][t] (fp32) = Box-Muller normal from two counter-based
+ * SplitMix64 draws (purpose 1, head h, node 0, counters 2e and 2e+1 with
+ * e = k*d + t): sqrt(-2 ln u1) cos(2 pi u2), u1 in (0,1], u2 in [0,1).
+ * Touches no device. G_host must hold heads*r*d floats.
+ */
+int sortlsh_hyperplanes(uint64_t seed, int heads, int r, int d, float* G_host);
+
+/*
+ * hyperattn_workspace_layout — where hyperattn_forward keeps its
+ * intermediate results inside the workspace (for inspection after a call:
+ * hash codes, sorts and sample lists). Fills offsets[i] and bytes[i] for
+ * i < HA_WS_COUNT (bytes 0 for a region the call does not use).
+ * Returns HA_OK or an error as hyperattn_workspace_bytes would.
+ *
+ * Region contents (L = number of levels: 1 if non-causal, else the number
+ * of halvings; S = n if non-causal, else n/2; node ids run 1 .. 2^L-1;
+ * regions not listed are scratch):
+ *   HA_WS_CODES_Q, HA_WS_CODES_K  uint8 [heads][n]
+ *   HA_WS_VNORM_W                 uint64 [heads][n]   integer weights W_j
+ *   HA_WS_VNORM_P                 uint64 [heads][n+1] exclusive prefix of W
+ *   HA_WS_PERM_Q, HA_WS_PERM_K    int32 [L][heads][S] global row at each sorted
+ *                                 position; level l's segments of size
+ *                                 h = n >> (l+1) (n if non-causal) are stored
+ *                                 one after another
+ *   HA_WS_RANK_K                  int32 [L][heads][S] sorted position (within
+ *                                 its segment) of each key slot
+ *   HA_WS_U_IDX, HA_WS_U_BKT      int32 [heads][nodes][m] uniform samples and
+ *                                 the key bucket of each
+ *   HA_WS_V_IDX, HA_WS_V_BKT      int32 [heads][nodes][m] V-norm samples, bucket
+ *   HA_WS_V_W                     float [heads][nodes][m] V-norm sample weights
+ *   HA_WS_NODE_META               int32 [heads][nodes][4]: uniform count,
+ *                                 V-norm count, alpha (float bits), b_eff
+ * The hyperplanes themselves are not in the workspace: the library keeps
+ * them per device, keyed by (seed, heads, r, d); sortlsh_hyperplanes returns
+ * the same values on the host.
+ */
+enum ha_ws_region {
+  HA_WS_CODES_Q = 0, HA_WS_CODES_K,
+  HA_WS_VNORM_A, HA_WS_VNORM_W, HA_WS_VNORM_P, HA_WS_VNORM_BLK,
+  HA_WS_PERM_Q, HA_WS_PERM_K, HA_WS_RANK_K,
+  HA_WS_SORT_HIST, HA_WS_SORT_OFFS,
+  HA_WS_U_IDX, HA_WS_U_BKT, HA_WS_V_IDX, HA_WS_V_BKT, HA_WS_V_W,
+  HA_WS_NODE_META,
+  HA_WS_PART_O, HA_WS_PART_LSE,
+  HA_WS_COUNT
+};
+int hyperattn_workspace_layout(int64_t n, int d, int heads, int causal, int b,
+                               int m, int recursion_base, int r, int dtype,
+                               int64_t* offsets, int64_t* bytes);
+
+/* Message for the last error on the calling thread ("" if none); valid until
+ * the next call into the library on this thread. */
+const char* hyperattn_last_error(void);
+
+/*
+ * Kernel timing for measurement. When enabled, every kernel the library
+ * launches is bracketed by two hipEvents recorded on the launch stream.
+ * hyperattn_profile_collect() waits for all recorded events, adds their
+ * durations to per-kernel totals and recycles them. Totals persist until
+ * hyperattn_profile_reset(). Not meant to be used from several threads.
+ */
+int hyperattn_profile_enable(int on);
+int hyperattn_profile_collect(void);
+int hyperattn_profile_reset(void);
+int hyperattn_profile_count(void);                 /* number of kernel names */
+const char* hyperattn_profile_name(int i);
+int64_t hyperattn_profile_launches(int i);
+double hyperattn_profile_total_ms(int i);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYPERATTN_H */

@@ -1,0 +1,170 @@
+"""The C ABI on the CPU: the library loads, exports what the header declares,
+validates arguments before touching a device, sizes workspaces, and its host
+hyperplanes equal the oracle's bit for bit. No GPU is needed."""
+
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+from approximate_softmax_attention_amd import _lib
+
+LIB = _lib.LIB_PATH
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB),
+                                reason="libhyperattn.so not built (run __graft_entry__.build())")
+
+
+def L():
+    return _lib.lib()
+
+
+def test_exports_every_declared_function():
+    declared = _lib.header_functions()
+    assert "hyperattn_forward" in declared and "sortlsh_hash" in declared
+    assert "exact_attention_forward" in declared and "rowsum_estimate" in declared
+    raw = ctypes.CDLL(LIB)
+    for name in declared:
+        assert hasattr(raw, name), name
+    assert sorted(_lib.SIGNATURES) == declared
+
+
+def test_library_has_gfx950_code_only():
+    data = open(LIB, "rb").read()
+    assert b"gfx950" in data
+    for other in (b"gfx942", b"gfx90a", b"gfx1100"):
+        assert other not in data
+
+
+@pytest.mark.parametrize("seed,heads,r,d", [(0, 1, 8, 64), (1004, 2, 8, 128), (7, 3, 3, 64)])
+def test_hyperplanes_equal_oracle(seed, heads, r, d):
+    from approximate_softmax_attention_amd import api
+    from oracle import sortlsh
+    assert np.array_equal(api.hyperplanes(seed, heads, r, d),
+                          sortlsh.hyperplanes(seed, heads, r, d))
+
+
+def ws_bytes(n=1024, d=64, heads=1, causal=0, b=128, m=128, base=4096, r=8, dt=1):
+    return L().hyperattn_workspace_bytes(n, d, heads, causal, b, m, base, r, dt)
+
+
+def test_workspace_sizes_and_validation_messages():
+    assert ws_bytes() > 0
+    assert ws_bytes(n=0) == 0 and _lib.last_error() == ""
+    assert ws_bytes(d=96) == 0 and "d=96" in _lib.last_error()
+    assert ws_bytes(r=9) == 0 and "r=9" in _lib.last_error()
+    assert ws_bytes(b=100) == 0 and "divide" in _lib.last_error()
+    assert ws_bytes(n=96, causal=1, b=1, base=2) == 0 and "odd" in _lib.last_error()
+    assert ws_bytes(m=0) == 0
+    assert ws_bytes(dt=7) == 0
+    # causal partial buffers scale with levels: n=2^17, base 4096 -> 5 levels
+    big = ws_bytes(n=131072, d=128, heads=32, causal=1, b=256, m=256, base=4096)
+    noncausal = ws_bytes(n=131072, d=128, heads=32, causal=0, b=256, m=256)
+    assert big > noncausal > 0
+    part = 5 * 32 * 65536 * 128 * 2
+    assert big > part
+
+
+def test_layout_regions_disjoint_and_aligned():
+    from approximate_softmax_attention_amd import api
+    for causal in (0, 1):
+        lay = api.workspace_layout(8192, 128, 4, causal=causal, b=256, m=256,
+                                   recursion_base=1024)
+        total = ws_bytes(n=8192, d=128, heads=4, causal=causal, b=256, m=256, base=1024)
+        spans = sorted((o, o + nb) for o, nb in lay.values() if nb > 0)
+        for (a0, a1), (b0, _) in zip(spans, spans[1:]):
+            assert a1 <= b0
+        assert spans[-1][1] <= total
+        assert all(o % 256 == 0 for o, nb in lay.values() if nb > 0)
+        S = 8192 if not causal else 4096
+        levels = 1 if not causal else 3
+        assert lay["PERM_Q"][1] == levels * 4 * S * 4
+        assert lay["VNORM_P"][1] == 4 * 8193 * 8
+        assert (lay["PART_O"][1] > 0) == bool(causal)
+
+
+def _vp(x):
+    return ctypes.c_void_p(x)
+
+
+def test_entry_points_validate_before_any_device_call():
+    lib = L()
+    p = _vp(256)    # never dereferenced: validation fails first
+    # null pointers
+    rc = lib.hyperattn_forward(None, p, p, p, None, 1024, 64, 1, 0, 128, 128, 4096, 8, 1, 1,
+                               p, 1 << 20, None)
+    assert rc == -1 and "NULL" in _lib.last_error()
+    rc = lib.exact_attention_forward(p, None, p, p, None, 10, 64, 1, 0, 1, None)
+    assert rc == -1
+    # unsupported
+    rc = lib.exact_attention_forward(p, p, p, p, None, 10, 80, 1, 0, 1, None)
+    assert rc == -3
+    rc = lib.sortlsh_hash(p, 10, 64, 1, 0, 1, 1, p, None, None, 0, None)
+    assert rc == -3
+    rc = lib.hyperattn_forward(p, p, p, p, None, 1024, 64, 1, 0, 128, 128, 4096, 8, 1, 5,
+                               p, 1 << 20, None)
+    assert rc == -3
+    # shape
+    rc = lib.hyperattn_forward(p, p, p, p, None, 1000, 64, 1, 0, 128, 128, 4096, 8, 1, 1,
+                               p, 1 << 20, None)
+    assert rc == -2 and "divide" in _lib.last_error()
+    rc = lib.rowsum_estimate(p, p, 1000, 64, 1, 128, 1, 8, 1, 1, p, p, 1 << 20, None)
+    assert rc == -2
+    # workspace: too small, misaligned, missing
+    need = ws_bytes()
+    rc = lib.hyperattn_forward(p, p, p, p, None, 1024, 64, 1, 0, 128, 128, 4096, 8, 1, 1,
+                               p, need - 1, None)
+    assert rc == -4 and "needed" in _lib.last_error()
+    rc = lib.hyperattn_forward(p, p, p, p, None, 1024, 64, 1, 0, 128, 128, 4096, 8, 1, 1,
+                               _vp(512 + 8), need, None)
+    assert rc == -4 and "aligned" in _lib.last_error()
+    rc = lib.hyperattn_forward(p, p, p, p, None, 1024, 64, 1, 0, 128, 128, 4096, 8, 1, 1,
+                               None, need, None)
+    assert rc == -4
+    rc = lib.sortlsh_hash(p, 5000, 64, 1, 8, 1, 1, p, p, None, 0, None)
+    assert rc == -4
+    # empty problems are valid and touch nothing
+    assert lib.hyperattn_forward(None, None, None, None, None, 0, 64, 4, 1, 256, 256, 4096,
+                                 8, 1, 1, None, 0, None) == 0
+    assert lib.exact_attention_forward(None, None, None, None, None, 0, 128, 2, 1, 1,
+                                       None) == 0
+
+
+def test_no_device_reports_hip_error():
+    """With valid arguments the first device call fails here (no GPU): HA_ERR_HIP."""
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+    except ImportError:
+        pass
+    lib = L()
+    p = _vp(256)
+    rc = lib.sortlsh_hash(p, 64, 64, 1, 8, 1, 1, p, None, None, 0, None)
+    assert rc == -5 and _lib.last_error()
+
+
+def test_profile_api_without_launches():
+    lib = L()
+    assert lib.hyperattn_profile_enable(1) == 0
+    assert lib.hyperattn_profile_enable(0) == 0
+    assert lib.hyperattn_profile_reset() == 0
+    assert lib.hyperattn_profile_count() >= 0
+    assert lib.hyperattn_profile_name(-1) == b""
+
+
+def test_product_path_has_no_cpu_fallback():
+    """The binding refuses to run without the HIP library instead of computing
+    anything itself."""
+    import importlib
+    src = open(os.path.join(os.path.dirname(LIB), "api.py")).read()
+    assert "oracle" not in src and "numpy.linalg" not in src
+    mod = importlib.import_module("approximate_softmax_attention_amd._lib")
+    saved = mod._LIB, mod.LIB_PATH
+    try:
+        mod._LIB, mod.LIB_PATH = None, "/nonexistent/libhyperattn.so"
+        with pytest.raises(RuntimeError, match="missing"):
+            mod.lib()
+    finally:
+        mod._LIB, mod.LIB_PATH = saved

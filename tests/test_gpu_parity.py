@@ -1,0 +1,280 @@
+"""GPU parity: the HIP library through its C ABI against the CPU oracle.
+
+Integer artefacts (hash codes, V-norm weights and prefix sums, sortLSH
+permutations and ranks, sample lists) must be bit-exact; O and lse must be
+within the max-relative tolerance of gpu_util.TOL. Inputs come from the shared
+seeded generators in approximate_softmax_attention_amd.workloads.
+"""
+
+import numpy as np
+import pytest
+
+from approximate_softmax_attention_amd import workloads as wl
+from oracle import exact as oexact
+from oracle import hyperattention as oha
+from oracle import sortlsh as osl
+from tests.gpu_util import TOL, banner, max_rel, region, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _api():
+    from approximate_softmax_attention_amd import api
+    return api
+
+
+def _inputs(name, **changes):
+    w = wl.scaled(wl.WORKLOADS[name], **changes) if changes else wl.WORKLOADS[name]
+    Q, K, V, pairs = wl.make_inputs(w)
+    return w, Q, K, V, pairs
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------ exact attention
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [1, 77, 300])
+def test_exact_attention(dtype, d, causal, n):
+    banner(f"exact dtype={dtype} d={d} causal={causal} n={n}")
+    w, Q, K, V, _ = _inputs("single_head_noncausal_n1024_d64_fp32", heads=2, n=n, d=d,
+                            dtype=dtype)
+    api = _api()
+    O, L = api.exact(to_dev(Q, dtype), to_dev(K, dtype), to_dev(V, dtype), causal=causal,
+                     return_lse=True)
+    _sync()
+    ref = [oexact.exact_attention(Q[h], K[h], V[h], causal=causal) for h in range(2)]
+    Oref = np.stack([r[0] for r in ref])
+    Lref = np.stack([r[1] for r in ref])
+    assert max_rel(to_np(O), Oref) <= TOL[dtype]
+    assert np.abs(to_np(L) - Lref).max() <= TOL[dtype]
+
+
+# ----------------------------------------------------------------- the hash
+
+@pytest.mark.parametrize("dtype,d", [("fp32", 64), ("bf16", 64), ("bf16", 128), ("fp32", 128)])
+def test_sortlsh_hash_bit_exact(dtype, d):
+    banner(f"hash dtype={dtype} d={d}")
+    w, Q, K, V, _ = _inputs("single_head_noncausal_n1024_d64_fp32", heads=3, n=4099, d=d,
+                            dtype=dtype)
+    Q[0, 5] = 0.0                      # a zero row hashes to code 0
+    api = _api()
+    for r in (1, 5, 8):
+        codes, perm = api.sortlsh_hash(to_dev(Q, dtype), r=r, seed=31, with_perm=True)
+        _sync()
+        G = osl.hyperplanes(31, 3, r, d)
+        for h in range(3):
+            ref = osl.hash_codes(Q[h], G[h])
+            assert np.array_equal(codes[h].cpu().numpy(), ref)
+            rp, _ = osl.sort_segment(ref)
+            assert np.array_equal(perm[h].cpu().numpy(), rp)
+        assert codes[0, 5].item() == 0
+
+
+def test_hash_near_zero_projections_use_exact_sign():
+    """Rows almost orthogonal to a hyperplane exercise the fp64 re-check."""
+    banner("hash near-zero")
+    d, H = 64, 1
+    G = osl.hyperplanes(5, H, 8, d)[0].astype(np.float64)
+    rs = np.random.default_rng(0)
+    X = rs.standard_normal((512, d))
+    for i in range(512):                         # project out hyperplane i % 8
+        g = G[i % 8]
+        X[i] -= (X[i] @ g) / (g @ g) * g
+        X[i] += rs.standard_normal() * 1e-7 * g   # tiny signed residue
+    X = X.astype(np.float32)[None]
+    api = _api()
+    codes = api.sortlsh_hash(to_dev(X, "fp32"), r=8, seed=5)
+    _sync()
+    ref = osl.hash_codes(X[0], osl.hyperplanes(5, H, 8, d)[0])
+    assert np.array_equal(codes[0].cpu().numpy(), ref)
+
+
+# ------------------------------------------------- forward: integer artefacts
+
+def _check_artifacts(w, Q, K, V, ws, layout, art):
+    H, n = w.heads, w.n
+    cq = region(ws, layout, "CODES_Q", np.uint8).reshape(H, n)
+    ck = region(ws, layout, "CODES_K", np.uint8).reshape(H, n)
+    Wg = region(ws, layout, "VNORM_W", np.uint64).reshape(H, n)
+    Pg = region(ws, layout, "VNORM_P", np.uint64).reshape(H, n + 1)
+    subs = art["subs"]
+    L = max(s[0] for s in subs)
+    S = n if not w.causal else n // 2
+    permq = region(ws, layout, "PERM_Q", np.int32).reshape(L, H, S)
+    permk = region(ws, layout, "PERM_K", np.int32).reshape(L, H, S)
+    rankk = region(ws, layout, "RANK_K", np.int32).reshape(L, H, S)
+    nodes = 2 ** L - 1 if w.causal else 1
+    m = w.m
+    uidx = region(ws, layout, "U_IDX", np.int32).reshape(H, nodes, m)
+    ubkt = region(ws, layout, "U_BKT", np.int32).reshape(H, nodes, m)
+    vidx = region(ws, layout, "V_IDX", np.int32).reshape(H, nodes, m)
+    vbkt = region(ws, layout, "V_BKT", np.int32).reshape(H, nodes, m)
+    vw = region(ws, layout, "V_W", np.float32).reshape(H, nodes, m)
+    meta = region(ws, layout, "NODE_META", np.int32).reshape(H, nodes, 4)
+    for h in range(H):
+        assert np.array_equal(cq[h], art["codes_q"][h])
+        assert np.array_equal(ck[h], art["codes_k"][h])
+        assert np.array_equal(Wg[h], art["W"][h])
+        assert np.array_equal(Pg[h], art["P"][h])
+        for a in art["sub"][h]:
+            lv, node, size = a["level"] - 1, a["node"], a["size"]
+            s = node - (1 << lv)
+            sl = slice(s * size, (s + 1) * size)
+            assert np.array_equal(permq[lv, h, sl], a["perm_q"])
+            assert np.array_equal(permk[lv, h, sl], a["perm_k"])
+            assert np.array_equal(rankk[lv, h, sl], a["rank_k"])
+            mt = meta[h, node - 1]
+            assert mt[0] == len(a["u_idx"]) and mt[1] == len(a["v_idx"])
+            assert mt[2] == np.float32(a["alpha"]).view(np.int32)
+            assert mt[3] == a["b_eff"]
+            assert np.array_equal(uidx[h, node - 1, :mt[0]], a["u_idx"])
+            assert np.array_equal(ubkt[h, node - 1, :mt[0]], a["u_bucket"])
+            assert np.array_equal(vidx[h, node - 1, :mt[1]], a["v_idx"])
+            assert np.array_equal(vbkt[h, node - 1, :mt[1]], a["v_bucket"])
+            assert np.array_equal(vw[h, node - 1, :mt[1]].view(np.uint32),
+                                  a["v_w"].view(np.uint32))
+
+
+def _run_forward(w, Q, K, V):
+    import torch
+    api = _api()
+    dt = 1 if w.dtype == "bf16" else 0
+    layout = api.workspace_layout(w.n, w.d, w.heads, causal=w.causal, b=w.b, m=w.m, r=w.r,
+                                  recursion_base=w.recursion_base, dtype=dt)
+    nb = api.workspace_bytes(w.n, w.d, w.heads, causal=w.causal, b=w.b, m=w.m, r=w.r,
+                             recursion_base=w.recursion_base, dtype=dt)
+    ws = api.alloc_workspace(nb, "cuda")
+    ws.fill_(0xAB)
+    O, L = api.forward(to_dev(Q, w.dtype), to_dev(K, w.dtype), to_dev(V, w.dtype),
+                       causal=w.causal, b=w.b, m=w.m, r=w.r, recursion_base=w.recursion_base,
+                       seed=w.method_seed, return_lse=True, workspace=ws)
+    torch.cuda.synchronize()
+    return O, L, ws, layout
+
+
+FORWARD_CASES = {
+    # name: (workload, changes)
+    "c1_full": ("single_head_noncausal_n1024_d64_fp32", {}),
+    "noncausal_bf16_d128_ragged_bucket": ("single_head_noncausal_n1024_d64_fp32",
+                                          dict(heads=2, n=1000, d=128, dtype="bf16", b=100,
+                                               m=37)),
+    "causal_fp32_d64": ("chatglm2_causal_n32768_d128_h32_bf16",
+                        dict(heads=2, n=2048, d=64, dtype="fp32", b=64, m=48,
+                             recursion_base=256)),
+    "causal_bf16_d128": ("chatglm2_causal_n32768_d128_h32_bf16",
+                         dict(heads=2, n=4096, b=128, m=100, recursion_base=512)),
+    "causal_bf16_ragged_base": ("chatglm2_causal_n32768_d128_h32_bf16",
+                                dict(heads=1, n=1536, b=96, m=300, recursion_base=200)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(FORWARD_CASES))
+def test_forward_matches_oracle(case):
+    name, changes = FORWARD_CASES[case]
+    banner(f"forward {case}")
+    w, Q, K, V, _ = _inputs(name, **changes)
+    O, L, ws, layout = _run_forward(w, Q, K, V)
+    art = {}
+    Oref, Lref = oha.hyperattention(Q, K, V, causal=w.causal, b=w.b, m=w.m, r=w.r,
+                                    recursion_base=w.recursion_base, seed=w.method_seed,
+                                    artifacts=art)
+    _check_artifacts(w, Q, K, V, ws, layout, art)
+    assert max_rel(to_np(O), Oref) <= TOL[w.dtype]
+    assert np.abs(to_np(L) - Lref).max() <= TOL[w.dtype]
+
+
+def test_planted_workload_full():
+    """8 heads, n = 8192, d = 64, bf16, planted heavy keys: full parity."""
+    banner("forward planted n=8192")
+    w, Q, K, V, pairs = _inputs("planted_noncausal_n8192_d64_h8_bf16")
+    O, L, ws, layout = _run_forward(w, Q, K, V)
+    art = {}
+    Oref, Lref = oha.hyperattention(Q, K, V, causal=False, b=w.b, m=w.m, r=w.r,
+                                    seed=w.method_seed, artifacts=art)
+    _check_artifacts(w, Q, K, V, ws, layout, art)
+    assert max_rel(to_np(O), Oref) <= TOL["bf16"]
+    assert np.abs(to_np(L) - Lref).max() <= TOL["bf16"]
+    # planted recall (reported): fraction of planted pairs sharing a bucket
+    hits = tot = 0
+    for h in range(w.heads):
+        a = art["sub"][h][0]
+        bq = np.empty(w.n, dtype=np.int64)
+        bq[a["perm_q"]] = np.arange(w.n) // a["b_eff"]
+        bk = np.empty(w.n, dtype=np.int64)
+        bk[a["perm_k"]] = np.arange(w.n) // a["b_eff"]
+        p = pairs[h]
+        hits += int((bq[p[:, 0]] == bk[p[:, 1]]).sum())
+        tot += len(p)
+    print(f"planted recall {hits / tot:.3f} over {tot} pairs")
+    assert hits / tot > 0.5
+
+
+def test_rowsum_estimate_matches_oracle():
+    banner("rowsum")
+    w, Q, K, V, _ = _inputs("single_head_noncausal_n1024_d64_fp32", heads=2, n=2048, d=128,
+                            dtype="bf16", b=128, m=96)
+    api = _api()
+    ld = api.rowsum_estimate(to_dev(Q, "bf16"), to_dev(K, "bf16"), b=w.b, m=w.m, r=w.r,
+                             seed=w.method_seed)
+    _sync()
+    ref = oha.rowsum_estimate(Q, K, b=w.b, m=w.m, r=w.r, seed=w.method_seed)
+    assert np.abs(to_np(ld) - ref).max() <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------- edge cases
+
+def test_reductions_to_exact_on_gpu():
+    banner("reductions")
+    api = _api()
+    w, Q, K, V, _ = _inputs("single_head_noncausal_n1024_d64_fp32", heads=2, n=512, d=64)
+    q, k, v = (to_dev(x, "fp32") for x in (Q, K, V))
+    Oe = np.stack([oexact.exact_attention(Q[h], K[h], V[h])[0] for h in range(2)])
+    Oc = np.stack([oexact.exact_attention(Q[h], K[h], V[h], causal=True)[0] for h in range(2)])
+    O1 = api.forward(q, k, v, causal=False, b=512, m=5, seed=3)       # one bucket
+    O2 = api.forward(q, k, v, causal=False, b=16, m=512, seed=3)      # exhaustive samples
+    O3 = api.forward(q, k, v, causal=True, b=256, m=3, recursion_base=64, seed=3)
+    O4 = api.forward(q, k, v, causal=True, b=8, m=2, recursion_base=512, seed=3)
+    _sync()
+    assert max_rel(to_np(O1), Oe) <= 1e-3
+    assert max_rel(to_np(O2), Oe) <= 1e-3
+    assert max_rel(to_np(O3), Oc) <= 1e-3
+    assert max_rel(to_np(O4), Oc) <= 1e-3
+
+
+def test_empty_and_error_paths():
+    banner("edge")
+    import torch
+    api = _api()
+    from approximate_softmax_attention_amd._lib import HyperAttnError
+    z = torch.empty((2, 0, 64), device="cuda", dtype=torch.bfloat16)
+    assert api.forward(z, z, z, causal=True).shape == (2, 0, 64)
+    assert api.exact(z, z, z).shape == (2, 0, 64)
+    q = torch.randn((1, 96, 64), device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(HyperAttnError, match="HA_ERR_SHAPE"):
+        api.forward(q, q, q, causal=False, b=40, m=8)              # 40 does not divide 96
+    with pytest.raises(HyperAttnError, match="HA_ERR_SHAPE"):
+        api.forward(q, q, q, causal=True, b=1, m=8, recursion_base=2)   # 96->...->6->3: 3 > 2 is odd
+    q3 = torch.randn((1, 96, 32), device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(HyperAttnError, match="HA_ERR_UNSUPPORTED"):
+        api.exact(q3, q3, q3)
+
+
+def test_deterministic_repeat():
+    banner("determinism")
+    import torch
+    api = _api()
+    w, Q, K, V, _ = _inputs("chatglm2_causal_n32768_d128_h32_bf16", heads=2, n=4096, b=128,
+                            m=128, recursion_base=512)
+    q, k, v = (to_dev(x, "bf16") for x in (Q, K, V))
+    a = api.forward(q, k, v, causal=True, b=128, m=128, recursion_base=512, seed=9)
+    b = api.forward(q, k, v, causal=True, b=128, m=128, recursion_base=512, seed=9)
+    c = api.forward(q, k, v, causal=True, b=128, m=128, recursion_base=512, seed=10)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert not torch.equal(a, c)
