@@ -23,6 +23,14 @@
 // then feed O^T += V^T P^T directly as the B operand (same lane layout), with
 // V^T staged transposed in LDS. fp32 inputs use v_mfma_f32_32x32x2f32 with the
 // same structure.
+//
+// Pipelining: key tiles are double-buffered in LDS. While a wave computes on
+// tile t, its share of tile t+1 is already in flight from HBM into registers
+// and the key indices of tile t+2 (gathered modes) are being fetched; one
+// barrier per tile. The running maximum is only moved (and O, l rescaled)
+// when a score exceeds it by more than 2^8, so most tiles skip the rescale.
+// Work-group ids are remapped so that consecutive logical tiles (which share
+// key blocks or sample lists) run on the same XCD and share its L2.
 #include <cmath>
 
 #include "common.h"
@@ -39,8 +47,10 @@ constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kQW = 32;   // queries per wave; kAttnQ = kWaves * kQW
 static_assert(kAttnQ == kWaves * kQW, "query tile");
+constexpr float kTau = 8.f;   // lazy-rescale threshold (log2 units)
 
 enum { MODE_EXACT = 0, MODE_BUCKET = 1, MODE_ROWSUM = 2 };
+enum { KIND_PLAIN = 0, KIND_SUM_W = 1, KIND_PV_W = 2 };
 
 template <typename T, int D> struct TileCfg;
 template <> struct TileCfg<bf16_t, 128> { static constexpr int KT = 64, KPAD = 8, VPAD = 4; };
@@ -49,20 +59,43 @@ template <> struct TileCfg<float, 128> { static constexpr int KT = 32, KPAD = 4,
 template <> struct TileCfg<float, 64> { static constexpr int KT = 64, KPAD = 4, VPAD = 4; };
 
 template <typename T, int D>
-struct alignas(16) Smem {
+struct alignas(16) Buf {
   static constexpr int KT = TileCfg<T, D>::KT;
   static constexpr int KS = D + TileCfg<T, D>::KPAD;   // K row stride (elements)
   static constexpr int VS = KT + TileCfg<T, D>::VPAD;  // V^T row stride (elements)
+  static constexpr int EPC = 16 / int(sizeof(T));      // elements per 16-byte chunk
+  static constexpr int CPR = D / EPC;                  // chunks per row
+  static_assert((KT / 4) * CPR == kThreads, "one 4-key x 16-byte item per thread");
   alignas(16) T k[KT * KS];
   alignas(16) T vt[D * VS];
-  float wd[KT];
-  float wn[KT];
-  int valid[KT];
+  alignas(16) float w[KT];     // per-slot weight (sample segments)
 };
 
-struct KeySlot {
-  int64_t row;    // key row within the head, or -1 (masked, zero-filled)
-  float wd, wn;   // weight in the row sum and in the product
+constexpr int kSlotCap = 1024;   // key slots staged in LDS per window (gathered modes)
+
+template <typename T, int D>
+struct Smem {
+  Buf<T, D> buf[2];
+};
+
+template <typename T, int D>
+struct SmemG {
+  Buf<T, D> buf[2];
+  alignas(16) int32_t srow[kSlotCap];
+  alignas(16) float sw[kSlotCap];
+};
+
+struct SlotInfo {
+  int32_t row;   // key row within the head, or -1 (masked, zero-filled)
+  float w;       // weight of the slot in its segment
+};
+
+// One thread's share of a tile between HBM and LDS: 4 consecutive slots,
+// one 16-byte chunk of each K and V row.
+struct Staged {
+  uint4 k[4];
+  uint4 v[4];
+  float w[4];
 };
 
 struct AttnArgs {
@@ -103,76 +136,76 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Logical work-group index with consecutive indices placed on the same XCD
+// (work-groups are dealt to the 8 XCDs round-robin).
+__device__ __forceinline__ int64_t xcd_remap(int64_t x, int64_t n) {
+  constexpr int64_t kXcd = 8;
+  if (n % kXcd) return x;
+  return (x % kXcd) * (n / kXcd) + x / kXcd;
+}
+
 // ---------------------------------------------------------------- tiles
-// Loads key slots [0, KT) of a tile into LDS: K rows as they are, V rows
-// transposed, plus each slot's weights and validity. Threads take groups of
-// 4 consecutive slots x one 16-byte chunk of the row.
-template <typename T, int D, bool kV, typename Src>
-__device__ __forceinline__ void load_tile(Smem<T, D>& sm, const T* __restrict__ Kh,
-                                          const T* __restrict__ Vh, const Src& src) {
-  constexpr int KT = Smem<T, D>::KT;
-  constexpr int KS = Smem<T, D>::KS;
-  constexpr int VS = Smem<T, D>::VS;
-  constexpr int EPC = 16 / int(sizeof(T));   // elements per 16-byte chunk
-  constexpr int CPR = D / EPC;               // chunks per row
-  for (int u = threadIdx.x; u < (KT / 4) * CPR; u += kThreads) {
-    const int kg = u / CPR;
-    const int ch = u % CPR;
-    int64_t rows[4];
+template <typename T, int D>
+__device__ __forceinline__ void fetch(Staged& st, const SlotInfo* si, const T* __restrict__ Kh,
+                                      const T* __restrict__ Vh, bool with_v) {
+  constexpr int EPC = Buf<T, D>::EPC;
+  const int ch = threadIdx.x % Buf<T, D>::CPR;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    st.w[i] = si[i].w;
+    const int64_t r = si[i].row;
+    st.k[i] = r >= 0 ? *reinterpret_cast<const uint4*>(Kh + r * D + ch * EPC)
+                     : make_uint4(0, 0, 0, 0);
+  }
+  if (with_v) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const KeySlot s = src(4 * kg + i);
-      rows[i] = s.row;
-      if (ch == 0) {
-        sm.valid[4 * kg + i] = s.row >= 0;
-        sm.wd[4 * kg + i] = s.wd;
-        sm.wn[4 * kg + i] = s.wn;
-      }
+      const int64_t r = si[i].row;
+      st.v[i] = r >= 0 ? *reinterpret_cast<const uint4*>(Vh + r * D + ch * EPC)
+                       : make_uint4(0, 0, 0, 0);
     }
-    uint4 kv[4];
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void stash(Buf<T, D>& b, const Staged& st, bool with_v) {
+  constexpr int KS = Buf<T, D>::KS;
+  constexpr int VS = Buf<T, D>::VS;
+  constexpr int EPC = Buf<T, D>::EPC;
+  const int kg = threadIdx.x / Buf<T, D>::CPR;
+  const int ch = threadIdx.x % Buf<T, D>::CPR;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kv[i] = rows[i] >= 0 ? *reinterpret_cast<const uint4*>(Kh + rows[i] * D + ch * EPC)
-                           : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<uint4*>(&b.k[(4 * kg + i) * KS + ch * EPC]) = st.k[i];
+  if (ch == 0)
+    *reinterpret_cast<float4*>(&b.w[4 * kg]) = make_float4(st.w[0], st.w[1], st.w[2], st.w[3]);
+  if (!with_v) return;
+  if constexpr (sizeof(T) == 2) {
+    // V^T[d][key]: element j of the chunk is 16-bit half (j & 1) of word j/2
+#pragma unroll
+    for (int wi = 0; wi < 4; ++wi) {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = wi == 0 ? st.v[i].x : wi == 1 ? st.v[i].y : wi == 2 ? st.v[i].z : st.v[i].w;
+      const uint2 lo = make_uint2(__builtin_amdgcn_perm(w[1], w[0], 0x05040100u),
+                                  __builtin_amdgcn_perm(w[3], w[2], 0x05040100u));
+      const uint2 hi = make_uint2(__builtin_amdgcn_perm(w[1], w[0], 0x07060302u),
+                                  __builtin_amdgcn_perm(w[3], w[2], 0x07060302u));
+      *reinterpret_cast<uint2*>(&b.vt[(ch * 8 + 2 * wi) * VS + 4 * kg]) = lo;
+      *reinterpret_cast<uint2*>(&b.vt[(ch * 8 + 2 * wi + 1) * VS + 4 * kg]) = hi;
     }
-    uint4 vv[4];
-    if (kV) {
+  } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vv[i] = rows[i] >= 0 ? *reinterpret_cast<const uint4*>(Vh + rows[i] * D + ch * EPC)
-                             : make_uint4(0, 0, 0, 0);
-      }
-    }
+    for (int j = 0; j < 4; ++j) {
+      uint32_t e[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(&sm.k[(4 * kg + i) * KS + ch * EPC]) = kv[i];
-    if (kV) {
-      if constexpr (sizeof(T) == 2) {
-        // element j of the 8-element chunk of key i sits in 16-bit half
-        // (j & 1) of word (j >> 1); write the 4 keys' element j as 8 bytes
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          uint32_t e[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t wv = (j >> 1) == 0 ? vv[i].x : (j >> 1) == 1 ? vv[i].y
-                                : (j >> 1) == 2 ? vv[i].z : vv[i].w;
-            e[i] = (j & 1) ? (wv >> 16) : (wv & 0xFFFFu);
-          }
-          uint2 out = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
-          *reinterpret_cast<uint2*>(&sm.vt[(ch * 8 + j) * VS + 4 * kg]) = out;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t e[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            e[i] = j == 0 ? vv[i].x : j == 1 ? vv[i].y : j == 2 ? vv[i].z : vv[i].w;
-          *reinterpret_cast<uint4*>(&sm.vt[(ch * 4 + j) * VS + 4 * kg]) =
-              make_uint4(e[0], e[1], e[2], e[3]);
-        }
-      }
+      for (int i = 0; i < 4; ++i)
+        e[i] = j == 0 ? st.v[i].x : j == 1 ? st.v[i].y : j == 2 ? st.v[i].z : st.v[i].w;
+      *reinterpret_cast<uint4*>(&b.vt[(ch * 4 + j) * VS + 4 * kg]) =
+          make_uint4(e[0], e[1], e[2], e[3]);
     }
   }
 }
@@ -201,18 +234,26 @@ __device__ __forceinline__ void load_q(QFrag<T, D>& q, const T* __restrict__ Qh,
 template <typename T, int D>
 struct WaveState {
   f32x16 o[D / 32];
-  float m;      // running max (log2 units)
+  float m;      // running reference maximum (log2 units)
   float l;      // this lane's part of the row sum (its 16 keys per block)
 };
 
+template <typename T, int D>
+__device__ __forceinline__ void init_state(WaveState<T, D>& ws) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) ws.o[db] = zero16();
+  ws.m = -INFINITY;
+  ws.l = 0.f;
+}
+
 // S^T for key block kb of the tile: s[i] = score of key 32kb + 8(i/4) + 4g + i%4
 template <typename T, int D>
-__device__ __forceinline__ f32x16 scores(const Smem<T, D>& sm, const QFrag<T, D>& q, int kb) {
-  constexpr int KS = Smem<T, D>::KS;
+__device__ __forceinline__ f32x16 scores(const Buf<T, D>& b, const QFrag<T, D>& q, int kb) {
+  constexpr int KS = Buf<T, D>::KS;
   const int lane = lane_id();
   const int ql = lane & 31, g = lane >> 5;
   f32x16 acc = zero16();
-  const T* krow = &sm.k[(32 * kb + ql) * KS];
+  const T* krow = &b.k[(32 * kb + ql) * KS];
   if constexpr (sizeof(T) == 2) {
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
@@ -233,25 +274,25 @@ __device__ __forceinline__ int key_of(int kb, int i, int g) {
 
 // O^T += V^T P^T for key block kb, p[i] the (weighted) probability of key_of(kb, i)
 template <typename T, int D>
-__device__ __forceinline__ void accumulate_pv(const Smem<T, D>& sm, WaveState<T, D>& ws,
+__device__ __forceinline__ void accumulate_pv(const Buf<T, D>& b, WaveState<T, D>& ws,
                                               const f32x16& p, int kb) {
-  constexpr int VS = Smem<T, D>::VS;
+  constexpr int VS = Buf<T, D>::VS;
   const int lane = lane_id();
   const int ql = lane & 31, g = lane >> 5;
   if constexpr (sizeof(T) == 2) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      bf16x8_t b;
+      bf16x8_t pb;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) b[j] = (__bf16)p[8 * st + j];
+      for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[8 * st + j];
       const int k0 = 32 * kb + 16 * st + 4 * g;      // keys k0..k0+3, k0+8..k0+11
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const bf16_t* vr = &sm.vt[(32 * db + ql) * VS];
+        const bf16_t* vr = &b.vt[(32 * db + ql) * VS];
         const uint2 lo = *reinterpret_cast<const uint2*>(vr + k0);
         const uint2 hi = *reinterpret_cast<const uint2*>(vr + k0 + 8);
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        ws.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, ws.o[db], 0, 0, 0);
+        ws.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, ws.o[db], 0, 0, 0);
       }
     }
   } else {
@@ -260,73 +301,73 @@ __device__ __forceinline__ void accumulate_pv(const Smem<T, D>& sm, WaveState<T,
       const int key = key_of(kb, st, g);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const float a = sm.vt[(32 * db + ql) * VS + key];
+        const float a = b.vt[(32 * db + ql) * VS + key];
         ws.o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, p[st], ws.o[db], 0, 0, 0);
       }
     }
   }
 }
 
-// Process one LDS tile for this wave. kWeights: use the tile's wd/wn;
-// kPV: accumulate the product; kSum: accumulate the row sum.
-template <typename T, int D, bool kWeights, bool kPV, bool kSum, bool kCausal>
-__device__ __forceinline__ void process_tile(const Smem<T, D>& sm, const QFrag<T, D>& q,
-                                             WaveState<T, D>& ws, float scale_log2,
-                                             int64_t key0, int64_t qrow, int nvalid) {
-  constexpr int KT = Smem<T, D>::KT;
+// One LDS tile for this wave, processed as 32-key blocks, each with its own
+// online-softmax step (fewer live registers than one step per tile).
+//   KIND_PLAIN: row sum and product, weight 1; KIND_SUM_W: row sum only,
+//   weighted by b.w; KIND_PV_W: product only, weighted by b.w.
+// masked: keys >= nvalid (and, if causal, keys after the query) score -inf.
+template <typename T, int D, int KIND, bool kCausal>
+__device__ __forceinline__ void compute_tile(const Buf<T, D>& b, const QFrag<T, D>& q,
+                                             WaveState<T, D>& ws, float c, bool masked,
+                                             int nvalid, int64_t key0, int64_t qrow) {
+  constexpr int KT = Buf<T, D>::KT;
   constexpr int NB = KT / 32;
   const int g = lane_id() >> 5;
-  f32x16 s[NB];
-#pragma unroll
-  for (int kb = 0; kb < NB; ++kb) s[kb] = scores<T, D>(sm, q, kb);
-  float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < NB; ++kb) {
+    if (masked && 32 * kb >= nvalid) break;            // rest of the tile is empty
+    f32x16 s = scores<T, D>(b, q, kb);
+    if (masked) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = key_of(kb, i, g);
-      bool ok;
-      if (kWeights) ok = sm.valid[key] != 0;
-      else ok = key < nvalid;
-      if (kCausal) ok = ok && (key0 + key <= qrow);
-      const float x = ok ? s[kb][i] * scale_log2 : -INFINITY;
-      s[kb][i] = x;
-      mx = fmaxf(mx, x);
-    }
-  }
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  const float m_new = fmaxf(ws.m, mx);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float factor = exp2f(ws.m - m_use);
-  ws.m = m_new;
-  float lsum = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < NB; ++kb) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = exp2f(s[kb][i] - m_use);
-      if (kWeights) {
+      for (int i = 0; i < 16; ++i) {
         const int key = key_of(kb, i, g);
-        if (kSum) lsum += sm.wd[key] * p;
-        s[kb][i] = kPV ? sm.wn[key] * p : 0.f;
-      } else {
-        lsum += p;
-        s[kb][i] = p;
+        bool ok = key < nvalid;
+        if (kCausal) ok = ok && (key0 + key <= qrow);
+        s[i] = ok ? s[i] : -INFINITY;
       }
     }
-  }
-  ws.l = ws.l * factor + (kSum ? lsum : 0.f);
+    float mx = s[0];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+    const bool need = mx > ws.m + kTau;
+    if (__ballot(need)) {
+      const float m_new = need ? mx : ws.m;
+      const float f = (m_new == -INFINITY || m_new == ws.m) ? 1.f : fast_exp2(ws.m - m_new);
+      ws.l *= f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ws.o[db][i] *= factor;
-  if (kPV) {
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb) accumulate_pv<T, D>(sm, ws, s[kb], kb);
+        for (int i = 0; i < 16; ++i) ws.o[db][i] *= f;
+      ws.m = m_new;
+    }
+    const float mref = ws.m == -INFINITY ? 0.f : ws.m;
+    float lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(fmaf(s[i], c, -mref));
+      if (KIND == KIND_PLAIN) {
+        lsum += p;
+        s[i] = p;
+      } else if (KIND == KIND_SUM_W) {
+        lsum = fmaf(b.w[key_of(kb, i, g)], p, lsum);
+      } else {
+        s[i] = b.w[key_of(kb, i, g)] * p;
+      }
+    }
+    if (KIND != KIND_PV_W) ws.l += lsum;
+    if (KIND != KIND_SUM_W) accumulate_pv<T, D>(b, ws, s, kb);
   }
 }
 
-// Normalised output of this lane's query: fills out[db][i] and returns lse.
+// Normalised output of this lane's query; returns lse (natural log).
 template <typename T, int D>
 __device__ __forceinline__ float finalize(WaveState<T, D>& ws) {
   const float l = ws.l + __shfl_xor(ws.l, 32, 64);
@@ -335,7 +376,7 @@ __device__ __forceinline__ float finalize(WaveState<T, D>& ws) {
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) ws.o[db][i] *= inv;
-  return (ws.m + log2f(l)) * 0.69314718055994531f;
+  return (ws.m + __log2f(l)) * 0.69314718055994531f;
 }
 
 // d index of accumulator (db, i) for lane group g: 32db + 8(i/4) + 4g + i%4
@@ -393,32 +434,28 @@ __device__ __forceinline__ float merge_partial(WaveState<T, D>& ws, float lse,
   return mx + __logf(wa + wb);
 }
 
-template <typename T, int D>
-__device__ __forceinline__ void init_state(WaveState<T, D>& ws) {
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) ws.o[db] = zero16();
-  ws.m = -INFINITY;
-  ws.l = 0.f;
-}
-
 // ------------------------------------------------------------- EXACT kernel
 // grid: (blocks_per_head * tiles_per_block, heads). Causal tiles are visited
 // from the longest (last) to the shortest for load balance.
 template <typename T, int D, bool kCausal>
-__global__ __launch_bounds__(kThreads) void exact_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void exact_kernel(AttnArgs a) {
   __shared__ Smem<T, D> sm;
-  constexpr int KT = Smem<T, D>::KT;
-  const int head = blockIdx.y;
+  constexpr int KT = Buf<T, D>::KT;
+  const int64_t nx = int64_t(gridDim.x) * gridDim.y;
+  const int64_t lin = xcd_remap(int64_t(blockIdx.y) * gridDim.x + blockIdx.x, nx);
+  const int head = int(lin / gridDim.x);
+  const int64_t bx = lin % gridDim.x;
   const int64_t tpb = a.tiles_per_block;
-  const int64_t blk = int64_t(blockIdx.x) / tpb;
-  const int64_t tile = kCausal ? tpb - 1 - int64_t(blockIdx.x) % tpb : int64_t(blockIdx.x) % tpb;
+  const int64_t blk = bx / tpb;
+  const int64_t tile = kCausal ? tpb - 1 - bx % tpb : bx % tpb;
   const int64_t b_lo = blk * a.block;
   const int64_t b_hi = b_lo + a.block < a.n ? b_lo + a.block : a.n;
   const int64_t q0 = b_lo + tile * kAttnQ;
   const int64_t q_end = q0 + kAttnQ < b_hi ? q0 + kAttnQ : b_hi;
   const int wave = threadIdx.x >> 6;
   const int ql = lane_id() & 31;
-  const int64_t qr = q0 + wave * kQW + ql;
+  const int64_t qw0 = q0 + wave * kQW;              // first query of this wave
+  const int64_t qr = qw0 + ql;
   const int64_t qrow = qr < q_end ? qr : -1;
 
   const int64_t hoff = int64_t(head) * a.n * D;
@@ -429,14 +466,38 @@ __global__ __launch_bounds__(kThreads) void exact_kernel(AttnArgs a) {
   load_q<T, D>(q, Qh, qrow);
   WaveState<T, D> ws;
   init_state<T, D>(ws);
+
   const int64_t k_end = kCausal ? q_end : b_hi;
-  for (int64_t k0 = b_lo; k0 < k_end; k0 += KT) {
+  const int ntiles = int((k_end - b_lo + KT - 1) / KT);
+  const int kg = threadIdx.x / Buf<T, D>::CPR;
+  auto slots = [&](int t, SlotInfo* si) {
+    const int64_t k0 = b_lo + int64_t(t) * KT;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = k0 + 4 * kg + i;
+      si[i] = SlotInfo{r < k_end ? int32_t(r) : -1, 1.f};
+    }
+  };
+  Staged st;
+  SlotInfo si[4];
+  slots(0, si);
+  fetch<T, D>(st, si, Kh, Vh, true);
+  stash<T, D>(sm.buf[0], st, true);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) {
+      slots(t + 1, si);
+      fetch<T, D>(st, si, Kh, Vh, true);
+    }
+    const int64_t k0 = b_lo + int64_t(t) * KT;
     const int nvalid = int(k_end - k0 < KT ? k_end - k0 : KT);
-    load_tile<T, D, true>(sm, Kh, Vh, [&](int i) {
-      return KeySlot{i < nvalid ? k0 + i : -1, 1.f, 1.f};
-    });
-    __syncthreads();
-    process_tile<T, D, false, true, true, kCausal>(sm, q, ws, a.scale_log2, k0, qrow, nvalid);
+    const bool skip = kCausal && k0 > qw0 + kQW - 1;       // wholly above the diagonal
+    if (!skip) {
+      const bool masked = nvalid < KT || (kCausal && k0 + KT - 1 > qw0);
+      compute_tile<T, D, KIND_PLAIN, kCausal>(sm.buf[t & 1], q, ws, a.scale_log2, masked,
+                                              nvalid, k0, qrow);
+    }
+    if (t + 1 < ntiles) stash<T, D>(sm.buf[(t + 1) & 1], st, true);
     __syncthreads();
   }
   float lse = finalize<T, D>(ws);
@@ -456,12 +517,18 @@ __global__ __launch_bounds__(kThreads) void exact_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------ BUCKET / ROWSUM kernel
+// The key tiles of a work-group form one sequence: the bucket's own keys,
+// then the uniform sample, then (BUCKET) the V-norm sample, each segment
+// padded to whole tiles. The rows and weights of up to kSlotCap slots (a
+// window of tiles) are staged in LDS up front, so the tile loop issues no
+// dependent index loads.
 template <typename T, int D, int MODE>
-__global__ __launch_bounds__(kThreads) void bucket_kernel(AttnArgs a) {
-  __shared__ Smem<T, D> sm;
-  constexpr int KT = Smem<T, D>::KT;
+__global__ __launch_bounds__(kThreads, 2) void bucket_kernel(AttnArgs a) {
+  __shared__ SmemG<T, D> sm;
+  constexpr int KT = Buf<T, D>::KT;
+  constexpr int kWin = kSlotCap / KT;           // tiles per slot window
   constexpr bool kProduct = MODE == MODE_BUCKET;
-  const int64_t w = blockIdx.x;
+  const int64_t w = xcd_remap(blockIdx.x, gridDim.x);
   int lv = 0;
   for (int l = 1; l < a.table.count; ++l)
     if (w >= a.table.lv[l].att_wg0) lv = l;
@@ -498,45 +565,92 @@ __global__ __launch_bounds__(kThreads) void bucket_kernel(AttnArgs a) {
   WaveState<T, D> ws;
   init_state<T, D>(ws);
 
-  // (a) the bucket's own keys
-  const int32_t* pk = a.perm_k + slot0;
-  for (int k0 = 0; k0 < b_eff; k0 += KT) {
-    load_tile<T, D, kProduct>(sm, Kh, Vh, [&](int i) {
-      const int j = k0 + i;
-      return KeySlot{j < b_eff ? int64_t(pk[j]) : -1, 1.f, 1.f};
-    });
-    __syncthreads();
-    process_tile<T, D, true, kProduct, true, false>(sm, q, ws, a.scale_log2, 0, qrow, 0);
-    __syncthreads();
-  }
-  // (b) uniform column sample: row sum only
-  const int32_t* ui = a.u_idx + rec * a.m;
-  const int32_t* ub = a.u_bkt + rec * a.m;
-  for (int k0 = 0; k0 < ucount; k0 += KT) {
-    load_tile<T, D, false>(sm, Kh, Vh, [&](int i) {
-      const int j = k0 + i;
-      if (j >= ucount) return KeySlot{-1, 0.f, 0.f};
-      return KeySlot{int64_t(ui[j]), ub[j] != bucket ? alpha : 0.f, 0.f};
-    });
-    __syncthreads();
-    process_tile<T, D, true, false, true, false>(sm, q, ws, a.scale_log2, 0, qrow, 0);
-    __syncthreads();
-  }
-  // (c) V-row-norm sample: product only
-  if (kProduct) {
-    const int32_t* vi = a.v_idx + rec * a.m;
-    const int32_t* vb = a.v_bkt + rec * a.m;
-    const float* vw = a.v_w + rec * a.m;
-    for (int k0 = 0; k0 < vcount; k0 += KT) {
-      load_tile<T, D, true>(sm, Kh, Vh, [&](int i) {
-        const int j = k0 + i;
-        if (j >= vcount) return KeySlot{-1, 0.f, 0.f};
-        return KeySlot{int64_t(vi[j]), 0.f, vb[j] != bucket ? vw[j] : 0.f};
-      });
-      __syncthreads();
-      process_tile<T, D, true, true, false, false>(sm, q, ws, a.scale_log2, 0, qrow, 0);
-      __syncthreads();
+  const int t_b = (b_eff + KT - 1) / KT;
+  const int t_u = (ucount + KT - 1) / KT;
+  const int t_v = (vcount + KT - 1) / KT;
+  const int ntiles = t_b + t_u + t_v;
+  // segment of tile t (0 bucket, 1 uniform, 2 V-norm), its first slot, its size
+  auto seg_of = [&](int t, int& j0, int& cnt) {
+    if (t < t_b) { j0 = t * KT; cnt = b_eff; return 0; }
+    if (t < t_b + t_u) { j0 = (t - t_b) * KT; cnt = ucount; return 1; }
+    j0 = (t - t_b - t_u) * KT; cnt = vcount; return 2;
+  };
+  // stage slots of tiles [t0, t0 + kWin) in LDS
+  auto fill = [&](int t0) {
+    const int32_t* pk = a.perm_k + slot0;
+    const int32_t* ui = a.u_idx + rec * a.m;
+    const int32_t* ub = a.u_bkt + rec * a.m;
+    for (int e = threadIdx.x; e < kSlotCap; e += kThreads) {
+      const int t = t0 + e / KT;
+      int32_t row = -1;
+      float wt = 0.f;
+      if (t < ntiles) {
+        int j0, cnt;
+        const int sg = seg_of(t, j0, cnt);
+        const int j = j0 + e % KT;
+        if (j < cnt) {
+          if (sg == 0) {
+            row = pk[j];
+            wt = 1.f;
+          } else if (sg == 1) {
+            row = ui[j];
+            wt = ub[j] != bucket ? alpha : 0.f;
+          } else {
+            row = a.v_idx[rec * a.m + j];
+            wt = a.v_bkt[rec * a.m + j] != bucket ? a.v_w[rec * a.m + j] : 0.f;
+          }
+        }
+      }
+      sm.srow[e] = row;
+      sm.sw[e] = wt;
     }
+  };
+  const int kg = threadIdx.x / Buf<T, D>::CPR;
+  auto slots = [&](int t, SlotInfo* si) {
+    const int e0 = (t % kWin) * KT + 4 * kg;
+    const int4 r = *reinterpret_cast<const int4*>(&sm.srow[e0]);
+    const float4 wt = *reinterpret_cast<const float4*>(&sm.sw[e0]);
+    si[0] = SlotInfo{r.x, wt.x};
+    si[1] = SlotInfo{r.y, wt.y};
+    si[2] = SlotInfo{r.z, wt.z};
+    si[3] = SlotInfo{r.w, wt.w};
+  };
+  auto needs_v = [&](int t) { return kProduct && (t < t_b || t >= t_b + t_u); };
+
+  Staged st;
+  SlotInfo si[4];
+  fill(0);
+  __syncthreads();
+  slots(0, si);
+  fetch<T, D>(st, si, Kh, Vh, needs_v(0));
+  stash<T, D>(sm.buf[0], st, needs_v(0));
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) {
+      if ((t + 1) % kWin == 0) {      // next window of slots
+        fill(t + 1);
+        __syncthreads();
+      }
+      slots(t + 1, si);
+      fetch<T, D>(st, si, Kh, Vh, needs_v(t + 1));
+    }
+    int j0, cnt;
+    const int sg = seg_of(t, j0, cnt);
+    const int nvalid = cnt - j0 < KT ? cnt - j0 : KT;
+    const bool masked = nvalid < KT;
+    const Buf<T, D>& b = sm.buf[t & 1];
+    if (sg == 0) {
+      if (kProduct)
+        compute_tile<T, D, KIND_PLAIN, false>(b, q, ws, a.scale_log2, masked, nvalid, 0, qrow);
+      else
+        compute_tile<T, D, KIND_SUM_W, false>(b, q, ws, a.scale_log2, masked, nvalid, 0, qrow);
+    } else if (sg == 1) {
+      compute_tile<T, D, KIND_SUM_W, false>(b, q, ws, a.scale_log2, masked, nvalid, 0, qrow);
+    } else if (kProduct) {
+      compute_tile<T, D, KIND_PV_W, false>(b, q, ws, a.scale_log2, masked, nvalid, 0, qrow);
+    }
+    if (t + 1 < ntiles) stash<T, D>(sm.buf[(t + 1) & 1], st, needs_v(t + 1));
+    __syncthreads();
   }
   const float lse = finalize<T, D>(ws);
   if (qrow < 0) return;
