@@ -151,6 +151,8 @@ int exact_attention_forward(const void* Q, const void* K, const void* V, void* O
   if (d != 64 && d != 128) return fail(HA_ERR_UNSUPPORTED, "d=%d not 64 or 128", d);
   if (n < 0 || n >= (int64_t(1) << 31)) return fail(HA_ERR_SHAPE, "n=%lld out of range", (long long)n);
   if (heads < 0 || heads >= (1 << 16)) return fail(HA_ERR_SHAPE, "heads=%d out of range", heads);
+  if (n * d * (dtype == HA_BF16 ? 2 : 4) >= (int64_t(1) << 31))
+    return fail(HA_ERR_SHAPE, "one head of n=%lld rows exceeds 2 GiB", (long long)n);
   if (n == 0 || heads == 0) return HA_OK;
   if (!Q || !K || !V || !O) return fail(HA_ERR_NULL, "Q, K, V and O must not be NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -15,22 +15,32 @@
 //           that lie in the query's own bucket.
 //  ROWSUM — (a) and (b) only, producing log d~ (Algorithm 2 alone).
 //
-// Layout: a work-group of 4 waves owns 128 query rows, 32 per wave. Each
+// Layout: a work-group of 8 waves owns 256 query rows, 32 per wave. Each
 // wave computes S^T = K Q^T for a key tile with v_mfma_f32_32x32x16_bf16
 // (A = K rows from LDS, B = the wave's Q rows held in registers), so every
 // lane owns one query column of S^T and the softmax statistics of that query
-// need only one cross-lane exchange (lane l with lane l^32). The probabilities
-// then feed O^T += V^T P^T directly as the B operand (same lane layout), with
-// V^T staged transposed in LDS. fp32 inputs use v_mfma_f32_32x32x2f32 with the
-// same structure.
+// need only one cross-lane exchange (lane l with lane l^32, a permlane swap).
+// The probabilities then feed O^T += V^T P^T directly as the B operand (same
+// lane layout).
 //
-// Pipelining: key tiles are double-buffered in LDS. While a wave computes on
-// tile t, its share of tile t+1 is already in flight from HBM into registers
-// and the key indices of tile t+2 (gathered modes) are being fetched; one
-// barrier per tile. The running maximum is only moved (and O, l rescaled)
-// when a score exceeds it by more than 2^8, so most tiles skip the rescale.
-// Work-group ids are remapped so that consecutive logical tiles (which share
-// key blocks or sample lists) run on the same XCD and share its L2.
+// bf16 tiles: K and V rows go from HBM straight into LDS (buffer loads with
+// the LDS destination, 16 bytes per lane, no register staging), unpadded with
+// the 16-byte chunks of each row XOR-swizzled by the row index so that the
+// fragment reads of 16 consecutive rows hit distinct banks. V's A operand is
+// read with gfx950's transposing LDS read (ds_read_b64_tr_b16): within each
+// 16-lane group, lane i receives element i%4 of what lane 4j + i/4 addressed
+// as its element j, so pointing lane L at V[key0 + L/4][d0 + 4(L%4)] hands
+// lane i the four keys key0..key0+3 of column d0 + i. All per-lane LDS byte
+// offsets are computed once per kernel.
+// fp32 tiles (a correctness path): v_mfma_f32_32x32x2f32, K padded, V
+// transposed through registers.
+//
+// Pipelining: key tiles are double-buffered in LDS; while a wave computes on
+// tile t the loads of tile t+1 are in flight; one barrier per tile. The
+// running maximum is only moved (and O, l rescaled) when a score exceeds it
+// by more than 2^8, so most tiles skip the rescale. Work-group ids are
+// remapped so that consecutive logical tiles (which share key blocks or
+// sample lists) run on the same XCD and share its L2.
 #include <cmath>
 
 #include "common.h"
@@ -42,36 +52,47 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
 constexpr int kQW = 32;   // queries per wave; kAttnQ = kWaves * kQW
 static_assert(kAttnQ == kWaves * kQW, "query tile");
 constexpr float kTau = 8.f;   // lazy-rescale threshold (log2 units)
+constexpr int kSlotCap = 1024;   // key slots staged in LDS per window (gathered modes)
 
 enum { MODE_EXACT = 0, MODE_BUCKET = 1, MODE_ROWSUM = 2 };
 enum { KIND_PLAIN = 0, KIND_SUM_W = 1, KIND_PV_W = 2 };
 
-template <typename T, int D> struct TileCfg;
-template <> struct TileCfg<bf16_t, 128> { static constexpr int KT = 64, KPAD = 8, VPAD = 4; };
-template <> struct TileCfg<bf16_t, 64> { static constexpr int KT = 128, KPAD = 8, VPAD = 4; };
-template <> struct TileCfg<float, 128> { static constexpr int KT = 32, KPAD = 4, VPAD = 4; };
-template <> struct TileCfg<float, 64> { static constexpr int KT = 64, KPAD = 4, VPAD = 4; };
+// ------------------------------------------------------------ tile buffers
+template <typename T, int D> struct Buf;
 
-template <typename T, int D>
-struct alignas(16) Buf {
-  static constexpr int KT = TileCfg<T, D>::KT;
-  static constexpr int KS = D + TileCfg<T, D>::KPAD;   // K row stride (elements)
-  static constexpr int VS = KT + TileCfg<T, D>::VPAD;  // V^T row stride (elements)
-  static constexpr int EPC = 16 / int(sizeof(T));      // elements per 16-byte chunk
-  static constexpr int CPR = D / EPC;                  // chunks per row
-  static_assert((KT / 4) * CPR == kThreads, "one 4-key x 16-byte item per thread");
-  alignas(16) T k[KT * KS];
-  alignas(16) T vt[D * VS];
-  alignas(16) float w[KT];     // per-slot weight (sample segments)
+// bf16: KT rows of K and V, D elements each, 16-byte chunks XOR-swizzled.
+template <int D>
+struct alignas(16) Buf<bf16_t, D> {
+  static constexpr int KT = 128;
+  static constexpr int CPR = D / 8;                    // 16-byte chunks per row
+  static constexpr int SHIFT = D == 128 ? 0 : 1;
+  __device__ static int swz(int row) { return (row >> SHIFT) & (CPR - 1); }
+  bf16_t k[KT * D];
+  bf16_t v[KT * D];
+  float w[KT];                                         // per-slot weight
 };
 
-constexpr int kSlotCap = 1024;   // key slots staged in LDS per window (gathered modes)
+// fp32: padded K rows and a padded V^T tile.
+template <int D>
+struct alignas(16) Buf<float, D> {
+  static constexpr int KT = D == 128 ? 64 : 128;
+  static constexpr int KS = D + 4;
+  static constexpr int VS = KT + 4;
+  static constexpr int CPR = D / 4;                    // 16-byte chunks per row
+  static_assert((KT / 4) * CPR == kThreads, "one 4-key x 16-byte item per thread");
+  float k[KT * KS];
+  float v[D * VS];
+  float w[KT];
+};
 
 template <typename T, int D>
 struct Smem {
@@ -85,19 +106,6 @@ struct SmemG {
   alignas(16) float sw[kSlotCap];
 };
 
-struct SlotInfo {
-  int32_t row;   // key row within the head, or -1 (masked, zero-filled)
-  float w;       // weight of the slot in its segment
-};
-
-// One thread's share of a tile between HBM and LDS: 4 consecutive slots,
-// one 16-byte chunk of each K and V row.
-struct Staged {
-  uint4 k[4];
-  uint4 v[4];
-  float w[4];
-};
-
 struct AttnArgs {
   const void* Q;
   const void* K;
@@ -109,7 +117,7 @@ struct AttnArgs {
   float scale_log2;        // log2(e) / sqrt(d)
   // EXACT
   int64_t block;           // key/query block size (n for plain exact attention)
-  int64_t tiles_per_block; // ceil(block / 128)
+  int64_t tiles_per_block; // ceil(block / kAttnQ)
   int causal;
   int merge_levels;        // base case: number of levels to merge (0: none)
   const void* part_o;      // [L][heads][S][d]
@@ -138,6 +146,29 @@ __device__ __forceinline__ f32x16 zero16() {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max(x[l], x[l ^ 32]) for every lane l
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// Raw buffer resource over one head's [n][d] tensor: loads take 32-bit byte
+// offsets, and offsets past the end return zeros (used for masked rows).
+constexpr uint32_t kOob = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 // Logical work-group index with consecutive indices placed on the same XCD
 // (work-groups are dealt to the 8 XCDs round-robin).
 __device__ __forceinline__ int64_t xcd_remap(int64_t x, int64_t n) {
@@ -146,69 +177,86 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t x, int64_t n) {
   return (x % kXcd) * (n / kXcd) + x / kXcd;
 }
 
-// ---------------------------------------------------------------- tiles
-template <typename T, int D>
-__device__ __forceinline__ void fetch(Staged& st, const SlotInfo* si, const T* __restrict__ Kh,
-                                      const T* __restrict__ Vh, bool with_v) {
-  constexpr int EPC = Buf<T, D>::EPC;
-  const int ch = threadIdx.x % Buf<T, D>::CPR;
+// ---------------------------------------------------------------- loaders
+// Pipe<T, D>::issue(buf, ...) starts loading one key tile; commit(buf) makes
+// it complete in LDS (before the barrier that publishes it). RowFn maps a tile
+// row to a key row of the head (-1: masked, zero-filled); WFn gives the
+// slot's weight.
+template <typename T, int D> struct Pipe;
+
+template <int D>
+struct Pipe<bf16_t, D> {
+  using B = Buf<bf16_t, D>;
+  template <typename RowFn, typename WFn>
+  __device__ __forceinline__ void issue(B& b, __amdgpu_buffer_rsrc_t Kr, __amdgpu_buffer_rsrc_t Vr,
+                                        bool with_v, const RowFn& rowidx, const WFn& weight) {
+    constexpr int PER = B::KT * B::CPR / kThreads;
+    constexpr uint32_t RB = D * 2;
+    const int wave = threadIdx.x >> 6;
+    const int lane = lane_id();
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    st.w[i] = si[i].w;
-    const int64_t r = si[i].row;
-    st.k[i] = r >= 0 ? *reinterpret_cast<const uint4*>(Kh + r * D + ch * EPC)
-                     : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < PER; ++i) {
+      const int p0 = i * kThreads + wave * 64;           // wave-uniform chunk index
+      const int p = p0 + lane;
+      const int row = p / B::CPR;
+      const int c = (p % B::CPR) ^ B::swz(row);          // global chunk landing here
+      const int r = rowidx(row);
+      const uint32_t off = r >= 0 ? uint32_t(r) * RB + uint32_t(c) * 16u : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(Kr, (lds_void_t*)(b.k + p0 * 8), 16, off, 0, 0, 0);
+      if (with_v)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(Vr, (lds_void_t*)(b.v + p0 * 8), 16, off, 0, 0,
+                                                 0);
+    }
+    if (threadIdx.x < B::KT) b.w[threadIdx.x] = weight(int(threadIdx.x));
   }
-  if (with_v) {
+  __device__ __forceinline__ void commit(B&, bool) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+};
+
+template <int D>
+struct Pipe<float, D> {
+  using B = Buf<float, D>;
+  uint4 k[4], v[4];
+  float w[4];
+  template <typename RowFn, typename WFn>
+  __device__ __forceinline__ void issue(B&, __amdgpu_buffer_rsrc_t Kr, __amdgpu_buffer_rsrc_t Vr,
+                                        bool with_v, const RowFn& rowidx, const WFn& weight) {
+    const int kg = threadIdx.x / B::CPR;
+    const uint32_t cb = (threadIdx.x % B::CPR) * 16u;
+    uint32_t off[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t r = si[i].row;
-      st.v[i] = r >= 0 ? *reinterpret_cast<const uint4*>(Vh + r * D + ch * EPC)
-                       : make_uint4(0, 0, 0, 0);
+      const int r = rowidx(4 * kg + i);
+      w[i] = weight(4 * kg + i);
+      off[i] = r >= 0 ? uint32_t(r) * (D * 4u) + cb : kOob;
+      k[i] = buf_load16(Kr, off[i]);
+    }
+    if (with_v) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = buf_load16(Vr, off[i]);
     }
   }
-}
-
-template <typename T, int D>
-__device__ __forceinline__ void stash(Buf<T, D>& b, const Staged& st, bool with_v) {
-  constexpr int KS = Buf<T, D>::KS;
-  constexpr int VS = Buf<T, D>::VS;
-  constexpr int EPC = Buf<T, D>::EPC;
-  const int kg = threadIdx.x / Buf<T, D>::CPR;
-  const int ch = threadIdx.x % Buf<T, D>::CPR;
+  __device__ __forceinline__ void commit(B& b, bool with_v) {
+    const int kg = threadIdx.x / B::CPR;
+    const int ch = threadIdx.x % B::CPR;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<uint4*>(&b.k[(4 * kg + i) * KS + ch * EPC]) = st.k[i];
-  if (ch == 0)
-    *reinterpret_cast<float4*>(&b.w[4 * kg]) = make_float4(st.w[0], st.w[1], st.w[2], st.w[3]);
-  if (!with_v) return;
-  if constexpr (sizeof(T) == 2) {
-    // V^T[d][key]: element j of the chunk is 16-bit half (j & 1) of word j/2
-#pragma unroll
-    for (int wi = 0; wi < 4; ++wi) {
-      uint32_t w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w[i] = wi == 0 ? st.v[i].x : wi == 1 ? st.v[i].y : wi == 2 ? st.v[i].z : st.v[i].w;
-      const uint2 lo = make_uint2(__builtin_amdgcn_perm(w[1], w[0], 0x05040100u),
-                                  __builtin_amdgcn_perm(w[3], w[2], 0x05040100u));
-      const uint2 hi = make_uint2(__builtin_amdgcn_perm(w[1], w[0], 0x07060302u),
-                                  __builtin_amdgcn_perm(w[3], w[2], 0x07060302u));
-      *reinterpret_cast<uint2*>(&b.vt[(ch * 8 + 2 * wi) * VS + 4 * kg]) = lo;
-      *reinterpret_cast<uint2*>(&b.vt[(ch * 8 + 2 * wi + 1) * VS + 4 * kg]) = hi;
-    }
-  } else {
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(&b.k[(4 * kg + i) * B::KS + ch * 4]) = k[i];
+    if (ch == 0) *reinterpret_cast<float4*>(&b.w[4 * kg]) = make_float4(w[0], w[1], w[2], w[3]);
+    if (!with_v) return;
+    // V^T[d][key]: the four keys' element j of this chunk as one 16-byte piece
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t e[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        e[i] = j == 0 ? st.v[i].x : j == 1 ? st.v[i].y : j == 2 ? st.v[i].z : st.v[i].w;
-      *reinterpret_cast<uint4*>(&b.vt[(ch * 4 + j) * VS + 4 * kg]) =
+        e[i] = j == 0 ? v[i].x : j == 1 ? v[i].y : j == 2 ? v[i].z : v[i].w;
+      *reinterpret_cast<uint4*>(&b.v[(ch * 4 + j) * B::VS + 4 * kg]) =
           make_uint4(e[0], e[1], e[2], e[3]);
     }
   }
-}
+};
 
 // ------------------------------------------------------------ per-wave core
 template <typename T, int D> struct QFrag;
@@ -216,20 +264,54 @@ template <int D> struct QFrag<bf16_t, D> { bf16x8_t v[D / 16]; };
 template <int D> struct QFrag<float, D> { float v[D / 2]; };
 
 template <typename T, int D>
-__device__ __forceinline__ void load_q(QFrag<T, D>& q, const T* __restrict__ Qh, int64_t row) {
+__device__ __forceinline__ void load_q(QFrag<T, D>& q, __amdgpu_buffer_rsrc_t Qr, int64_t row) {
   const int g = lane_id() >> 5;
+  constexpr uint32_t RB = D * sizeof(T);
+  const uint32_t base = row >= 0 ? uint32_t(row) * RB : kOob;
   if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-      uint4 raw = row >= 0 ? *reinterpret_cast<const uint4*>(Qh + row * D + 16 * st + 8 * g)
-                           : make_uint4(0, 0, 0, 0);
-      q.v[st] = __builtin_bit_cast(bf16x8_t, raw);
-    }
+    for (int st = 0; st < D / 16; ++st)
+      q.v[st] = __builtin_bit_cast(bf16x8_t, buf_load16(Qr, base + (16 * st + 8 * g) * 2));
   } else {
 #pragma unroll
-    for (int st = 0; st < D / 2; ++st) q.v[st] = row >= 0 ? Qh[row * D + 2 * st + g] : 0.f;
+    for (int st = 0; st < D / 2; ++st)
+      q.v[st] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                              Qr, base + (2 * st + g) * 4, 0, 0));
   }
 }
+
+// Per-lane LDS byte offsets of the MFMA fragments within one bf16 tile:
+//   k[st]:    K row ql of key block 0, chunk 2st+g (key block kb adds kb*32*D*2)
+//   v[h][db]: transposing-read address for keys 4g + (i16>>2) + 8h of a
+//             16-key step, columns 32db + 16*((lane>>4)&1) + 4*(i16&3)
+//             (step st of key block kb adds (32kb + 16st)*D*2)
+template <typename T, int D> struct LaneOffs { };
+template <int D>
+struct LaneOffs<bf16_t, D> {
+  using B = Buf<bf16_t, D>;
+  uint32_t k[D / 16];
+  uint32_t v[2][D / 32];
+  __device__ __forceinline__ void init() {
+    const int lane = lane_id();
+    const int ql = lane & 31, g = lane >> 5, i16 = lane & 15;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st)
+      k[st] = uint32_t(ql * B::CPR + ((2 * st + g) ^ B::swz(ql))) * 16u;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 4 * g + (i16 >> 2) + 8 * h;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int d = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+        v[h][db] = uint32_t(row * B::CPR + ((d >> 3) ^ B::swz(row))) * 16u + uint32_t(d & 7) * 2u;
+      }
+    }
+  }
+};
+template <int D>
+struct LaneOffs<float, D> {
+  __device__ __forceinline__ void init() {}
+};
 
 template <typename T, int D>
 struct WaveState {
@@ -248,22 +330,23 @@ __device__ __forceinline__ void init_state(WaveState<T, D>& ws) {
 
 // S^T for key block kb of the tile: s[i] = score of key 32kb + 8(i/4) + 4g + i%4
 template <typename T, int D>
-__device__ __forceinline__ f32x16 scores(const Buf<T, D>& b, const QFrag<T, D>& q, int kb) {
-  constexpr int KS = Buf<T, D>::KS;
-  const int lane = lane_id();
-  const int ql = lane & 31, g = lane >> 5;
+__device__ __forceinline__ f32x16 scores(const Buf<T, D>& b, const LaneOffs<T, D>& lo,
+                                         const QFrag<T, D>& q, int kb) {
   f32x16 acc = zero16();
-  const T* krow = &b.k[(32 * kb + ql) * KS];
   if constexpr (sizeof(T) == 2) {
+    const char* base = reinterpret_cast<const char*>(b.k) + kb * 32 * D * 2;
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(krow + 16 * st + 8 * g);
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(base + lo.k[st]);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q.v[st], acc, 0, 0, 0);
     }
   } else {
+    const int lane = lane_id();
+    const float* krow = &b.k[(32 * kb + (lane & 31)) * Buf<T, D>::KS];
 #pragma unroll
     for (int st = 0; st < D / 2; ++st)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * st + g], q.v[st], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * st + (lane >> 5)], q.v[st], acc, 0,
+                                                 0, 0);
   }
   return acc;
 }
@@ -274,34 +357,35 @@ __device__ __forceinline__ int key_of(int kb, int i, int g) {
 
 // O^T += V^T P^T for key block kb, p[i] the (weighted) probability of key_of(kb, i)
 template <typename T, int D>
-__device__ __forceinline__ void accumulate_pv(const Buf<T, D>& b, WaveState<T, D>& ws,
-                                              const f32x16& p, int kb) {
-  constexpr int VS = Buf<T, D>::VS;
-  const int lane = lane_id();
-  const int ql = lane & 31, g = lane >> 5;
+__device__ __forceinline__ void accumulate_pv(const Buf<T, D>& b, const LaneOffs<T, D>& lo,
+                                              WaveState<T, D>& ws, const f32x16& p, int kb) {
   if constexpr (sizeof(T) == 2) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       bf16x8_t pb;
 #pragma unroll
       for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[8 * st + j];
-      const int k0 = 32 * kb + 16 * st + 4 * g;      // keys k0..k0+3, k0+8..k0+11
+      const char* base = reinterpret_cast<const char*>(b.v) + (32 * kb + 16 * st) * D * 2;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const bf16_t* vr = &b.vt[(32 * db + ql) * VS];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr + k0);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + k0 + 8);
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        const v4i16_t x0 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + lo.v[0][db]));
+        const v4i16_t x1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + lo.v[1][db]));
+        const bf16x8_t a = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
         ws.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, ws.o[db], 0, 0, 0);
       }
     }
   } else {
+    const int lane = lane_id();
+    const int ql = lane & 31, g = lane >> 5;
 #pragma unroll
     for (int st = 0; st < 16; ++st) {
       const int key = key_of(kb, st, g);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const float a = b.vt[(32 * db + ql) * VS + key];
+        const float a = b.v[(32 * db + ql) * Buf<T, D>::VS + key];
         ws.o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, p[st], ws.o[db], 0, 0, 0);
       }
     }
@@ -309,34 +393,38 @@ __device__ __forceinline__ void accumulate_pv(const Buf<T, D>& b, WaveState<T, D
 }
 
 // One LDS tile for this wave, processed as 32-key blocks, each with its own
-// online-softmax step (fewer live registers than one step per tile).
+// online-softmax step.
 //   KIND_PLAIN: row sum and product, weight 1; KIND_SUM_W: row sum only,
 //   weighted by b.w; KIND_PV_W: product only, weighted by b.w.
-// masked: keys >= nvalid (and, if causal, keys after the query) score -inf.
+// masked: a key is valid iff its index in the tile is < nvalid and, if causal,
+// at most lim (= query row - first key row of the tile).
 template <typename T, int D, int KIND, bool kCausal>
-__device__ __forceinline__ void compute_tile(const Buf<T, D>& b, const QFrag<T, D>& q,
-                                             WaveState<T, D>& ws, float c, bool masked,
-                                             int nvalid, int64_t key0, int64_t qrow) {
-  constexpr int KT = Buf<T, D>::KT;
-  constexpr int NB = KT / 32;
+__device__ __forceinline__ void compute_tile(const Buf<T, D>& b, const LaneOffs<T, D>& lo,
+                                             const QFrag<T, D>& q, WaveState<T, D>& ws, float c,
+                                             bool masked, int nvalid, int lim) {
+  constexpr int NB = Buf<T, D>::KT / 32;
   const int g = lane_id() >> 5;
 #pragma unroll
   for (int kb = 0; kb < NB; ++kb) {
     if (masked && 32 * kb >= nvalid) break;            // rest of the tile is empty
-    f32x16 s = scores<T, D>(b, q, kb);
+    f32x16 s = scores<T, D>(b, lo, q, kb);
     if (masked) {
+      // key_of(kb, i, g) = 32kb + 4g + (8(i/4) + i%4): compare the immediate
+      // part against per-lane limits
+      const int vlim = nvalid - 32 * kb - 4 * g;
+      const int clim = lim - 32 * kb - 4 * g;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int key = key_of(kb, i, g);
-        bool ok = key < nvalid;
-        if (kCausal) ok = ok && (key0 + key <= qrow);
+        const int kk = 8 * (i >> 2) + (i & 3);
+        bool ok = kk < vlim;
+        if (kCausal) ok = ok && kk <= clim;
         s[i] = ok ? s[i] : -INFINITY;
       }
     }
-    float mx = s[0];
+    float mx = fmaxf(s[0], s[1]);
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+    for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = half_swap_max(mx) * c;
     const bool need = mx > ws.m + kTau;
     if (__ballot(need)) {
       const float m_new = need ? mx : ws.m;
@@ -349,28 +437,29 @@ __device__ __forceinline__ void compute_tile(const Buf<T, D>& b, const QFrag<T, 
       ws.m = m_new;
     }
     const float mref = ws.m == -INFINITY ? 0.f : ws.m;
-    float lsum = 0.f;
+    float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float p = fast_exp2(fmaf(s[i], c, -mref));
       if (KIND == KIND_PLAIN) {
-        lsum += p;
+        if (i & 1) ls1 += p; else ls0 += p;
         s[i] = p;
       } else if (KIND == KIND_SUM_W) {
-        lsum = fmaf(b.w[key_of(kb, i, g)], p, lsum);
+        if (i & 1) ls1 = fmaf(b.w[key_of(kb, i, g)], p, ls1);
+        else ls0 = fmaf(b.w[key_of(kb, i, g)], p, ls0);
       } else {
         s[i] = b.w[key_of(kb, i, g)] * p;
       }
     }
-    if (KIND != KIND_PV_W) ws.l += lsum;
-    if (KIND != KIND_SUM_W) accumulate_pv<T, D>(b, ws, s, kb);
+    if (KIND != KIND_PV_W) ws.l += ls0 + ls1;
+    if (KIND != KIND_SUM_W) accumulate_pv<T, D>(b, lo, ws, s, kb);
   }
 }
 
 // Normalised output of this lane's query; returns lse (natural log).
 template <typename T, int D>
 __device__ __forceinline__ float finalize(WaveState<T, D>& ws) {
-  const float l = ws.l + __shfl_xor(ws.l, 32, 64);
+  const float l = half_swap_sum(ws.l);
   const float inv = 1.f / l;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -438,7 +527,7 @@ __device__ __forceinline__ float merge_partial(WaveState<T, D>& ws, float lse,
 // grid: (blocks_per_head * tiles_per_block, heads). Causal tiles are visited
 // from the longest (last) to the shortest for load balance.
 template <typename T, int D, bool kCausal>
-__global__ __launch_bounds__(kThreads, 2) void exact_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void exact_kernel(AttnArgs a) {
   __shared__ Smem<T, D> sm;
   constexpr int KT = Buf<T, D>::KT;
   const int64_t nx = int64_t(gridDim.x) * gridDim.y;
@@ -459,45 +548,43 @@ __global__ __launch_bounds__(kThreads, 2) void exact_kernel(AttnArgs a) {
   const int64_t qrow = qr < q_end ? qr : -1;
 
   const int64_t hoff = int64_t(head) * a.n * D;
-  const T* Qh = static_cast<const T*>(a.Q) + hoff;
-  const T* Kh = static_cast<const T*>(a.K) + hoff;
-  const T* Vh = static_cast<const T*>(a.V) + hoff;
+  const int64_t hbytes = a.n * D * int64_t(sizeof(T));
+  const auto Qr = head_rsrc(static_cast<const T*>(a.Q) + hoff, hbytes);
+  const auto Kr = head_rsrc(static_cast<const T*>(a.K) + hoff, hbytes);
+  const auto Vr = head_rsrc(static_cast<const T*>(a.V) + hoff, hbytes);
   QFrag<T, D> q;
-  load_q<T, D>(q, Qh, qrow);
+  load_q<T, D>(q, Qr, qrow);
+  LaneOffs<T, D> lo;
+  lo.init();
   WaveState<T, D> ws;
   init_state<T, D>(ws);
 
   const int64_t k_end = kCausal ? q_end : b_hi;
   const int ntiles = int((k_end - b_lo + KT - 1) / KT);
-  const int kg = threadIdx.x / Buf<T, D>::CPR;
-  auto slots = [&](int t, SlotInfo* si) {
+  Pipe<T, D> pipe;
+  auto issue = [&](int t) {
     const int64_t k0 = b_lo + int64_t(t) * KT;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t r = k0 + 4 * kg + i;
-      si[i] = SlotInfo{r < k_end ? int32_t(r) : -1, 1.f};
-    }
+    const int nv = int(k_end - k0 < KT ? k_end - k0 : KT);
+    pipe.issue(sm.buf[t & 1], Kr, Vr, true,
+               [&](int row) { return row < nv ? int(k0 + row) : -1; },
+               [](int) { return 1.f; });
   };
-  Staged st;
-  SlotInfo si[4];
-  slots(0, si);
-  fetch<T, D>(st, si, Kh, Vh, true);
-  stash<T, D>(sm.buf[0], st, true);
+  issue(0);
+  pipe.commit(sm.buf[0], true);
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) {
-      slots(t + 1, si);
-      fetch<T, D>(st, si, Kh, Vh, true);
-    }
+    if (t + 1 < ntiles) issue(t + 1);
     const int64_t k0 = b_lo + int64_t(t) * KT;
     const int nvalid = int(k_end - k0 < KT ? k_end - k0 : KT);
     const bool skip = kCausal && k0 > qw0 + kQW - 1;       // wholly above the diagonal
     if (!skip) {
       const bool masked = nvalid < KT || (kCausal && k0 + KT - 1 > qw0);
-      compute_tile<T, D, KIND_PLAIN, kCausal>(sm.buf[t & 1], q, ws, a.scale_log2, masked,
-                                              nvalid, k0, qrow);
+      const int64_t dl = qrow - k0;
+      const int lim = dl < 0 ? -1 : (dl > KT ? KT : int(dl));
+      compute_tile<T, D, KIND_PLAIN, kCausal>(sm.buf[t & 1], lo, q, ws, a.scale_log2, masked,
+                                              nvalid, lim);
     }
-    if (t + 1 < ntiles) stash<T, D>(sm.buf[(t + 1) & 1], st, true);
+    if (t + 1 < ntiles) pipe.commit(sm.buf[(t + 1) & 1], true);
     __syncthreads();
   }
   float lse = finalize<T, D>(ws);
@@ -523,7 +610,7 @@ __global__ __launch_bounds__(kThreads, 2) void exact_kernel(AttnArgs a) {
 // window of tiles) are staged in LDS up front, so the tile loop issues no
 // dependent index loads.
 template <typename T, int D, int MODE>
-__global__ __launch_bounds__(kThreads, 2) void bucket_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void bucket_kernel(AttnArgs a) {
   __shared__ SmemG<T, D> sm;
   constexpr int KT = Buf<T, D>::KT;
   constexpr int kWin = kSlotCap / KT;           // tiles per slot window
@@ -557,11 +644,15 @@ __global__ __launch_bounds__(kThreads, 2) void bucket_kernel(AttnArgs a) {
   const float alpha = __int_as_float(meta[2]);
 
   const int64_t hoff = int64_t(head) * a.n * D;
-  const T* Qh = static_cast<const T*>(a.Q) + hoff;
-  const T* Kh = static_cast<const T*>(a.K) + hoff;
-  const T* Vh = kProduct ? static_cast<const T*>(a.V) + hoff : nullptr;
+  const int64_t hbytes = a.n * D * int64_t(sizeof(T));
+  const auto Qr = head_rsrc(static_cast<const T*>(a.Q) + hoff, hbytes);
+  const auto Kr = head_rsrc(static_cast<const T*>(a.K) + hoff, hbytes);
+  const auto Vr = head_rsrc(kProduct ? static_cast<const T*>(a.V) + hoff
+                                     : static_cast<const T*>(a.K) + hoff, hbytes);
   QFrag<T, D> q;
-  load_q<T, D>(q, Qh, qrow);
+  load_q<T, D>(q, Qr, qrow);
+  LaneOffs<T, D> lo;
+  lo.init();
   WaveState<T, D> ws;
   init_state<T, D>(ws);
 
@@ -605,25 +696,19 @@ __global__ __launch_bounds__(kThreads, 2) void bucket_kernel(AttnArgs a) {
       sm.sw[e] = wt;
     }
   };
-  const int kg = threadIdx.x / Buf<T, D>::CPR;
-  auto slots = [&](int t, SlotInfo* si) {
-    const int e0 = (t % kWin) * KT + 4 * kg;
-    const int4 r = *reinterpret_cast<const int4*>(&sm.srow[e0]);
-    const float4 wt = *reinterpret_cast<const float4*>(&sm.sw[e0]);
-    si[0] = SlotInfo{r.x, wt.x};
-    si[1] = SlotInfo{r.y, wt.y};
-    si[2] = SlotInfo{r.z, wt.z};
-    si[3] = SlotInfo{r.w, wt.w};
-  };
   auto needs_v = [&](int t) { return kProduct && (t < t_b || t >= t_b + t_u); };
+  Pipe<T, D> pipe;
+  auto issue = [&](int t) {
+    const int e0 = (t % kWin) * KT;
+    pipe.issue(sm.buf[t & 1], Kr, Vr, needs_v(t),
+               [&](int row) { return int(sm.srow[e0 + row]); },
+               [&](int slot) { return sm.sw[e0 + slot]; });
+  };
 
-  Staged st;
-  SlotInfo si[4];
   fill(0);
   __syncthreads();
-  slots(0, si);
-  fetch<T, D>(st, si, Kh, Vh, needs_v(0));
-  stash<T, D>(sm.buf[0], st, needs_v(0));
+  issue(0);
+  pipe.commit(sm.buf[0], needs_v(0));
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     if (t + 1 < ntiles) {
@@ -631,8 +716,7 @@ __global__ __launch_bounds__(kThreads, 2) void bucket_kernel(AttnArgs a) {
         fill(t + 1);
         __syncthreads();
       }
-      slots(t + 1, si);
-      fetch<T, D>(st, si, Kh, Vh, needs_v(t + 1));
+      issue(t + 1);
     }
     int j0, cnt;
     const int sg = seg_of(t, j0, cnt);
@@ -641,15 +725,15 @@ __global__ __launch_bounds__(kThreads, 2) void bucket_kernel(AttnArgs a) {
     const Buf<T, D>& b = sm.buf[t & 1];
     if (sg == 0) {
       if (kProduct)
-        compute_tile<T, D, KIND_PLAIN, false>(b, q, ws, a.scale_log2, masked, nvalid, 0, qrow);
+        compute_tile<T, D, KIND_PLAIN, false>(b, lo, q, ws, a.scale_log2, masked, nvalid, KT);
       else
-        compute_tile<T, D, KIND_SUM_W, false>(b, q, ws, a.scale_log2, masked, nvalid, 0, qrow);
+        compute_tile<T, D, KIND_SUM_W, false>(b, lo, q, ws, a.scale_log2, masked, nvalid, KT);
     } else if (sg == 1) {
-      compute_tile<T, D, KIND_SUM_W, false>(b, q, ws, a.scale_log2, masked, nvalid, 0, qrow);
+      compute_tile<T, D, KIND_SUM_W, false>(b, lo, q, ws, a.scale_log2, masked, nvalid, KT);
     } else if (kProduct) {
-      compute_tile<T, D, KIND_PV_W, false>(b, q, ws, a.scale_log2, masked, nvalid, 0, qrow);
+      compute_tile<T, D, KIND_PV_W, false>(b, lo, q, ws, a.scale_log2, masked, nvalid, KT);
     }
-    if (t + 1 < ntiles) stash<T, D>(sm.buf[(t + 1) & 1], st, needs_v(t + 1));
+    if (t + 1 < ntiles) pipe.commit(sm.buf[(t + 1) & 1], needs_v(t + 1));
     __syncthreads();
   }
   const float lse = finalize<T, D>(ws);

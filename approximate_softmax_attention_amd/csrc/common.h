@@ -88,7 +88,7 @@ struct Plan {
 };
 
 constexpr int kVnormBlock = 256;     // rows per V-norm work-group
-constexpr int kAttnQ = 128;          // query rows per attention work-group
+constexpr int kAttnQ = 256;          // query rows per attention work-group
 
 int make_plan(Plan& p, int64_t n, int d, int heads, int causal, int b, int m,
               int base, int r, int dtype, bool product);

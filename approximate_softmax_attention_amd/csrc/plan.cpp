@@ -33,6 +33,8 @@ int make_plan(Plan& p, int64_t n, int d, int heads, int causal, int b, int m,
     return fail(HA_ERR_SHAPE, "n=%lld out of range [0, 2^31)", (long long)n);
   if (heads < 0 || heads >= (1 << 16))
     return fail(HA_ERR_SHAPE, "heads=%d out of range [0, 65536)", heads);
+  if (n * d * (dtype == HA_BF16 ? 2 : 4) >= (int64_t(1) << 31))
+    return fail(HA_ERR_SHAPE, "one head of n=%lld rows exceeds 2 GiB", (long long)n);
   if (b < 1) return fail(HA_ERR_SHAPE, "bucket size b=%d must be >= 1", b);
   if (m < 1 || m >= (1 << 24))
     return fail(HA_ERR_SHAPE, "sample count m=%d out of range [1, 2^24)", m);

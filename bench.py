@@ -111,6 +111,9 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-exact", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (torch elementwise kernel) "
+                         "so that HBM byte counters can be scaled against known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
@@ -209,6 +212,14 @@ def main():
             "speedup_of_hyperattention": ems / ms,
             "rel_frobenius_err_vs_exact": float(diff)}
         del Oe
+
+    if args.copy_calibration:
+        log("plain copy of 1 GiB (reads 1 GiB, writes 1 GiB)")
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one head")

@@ -87,7 +87,7 @@ enum ha_status {
  * (ignored when causal == 0); r in [1, 8] hyperplanes; seed selects
  * hyperplanes and samples.
  * HA_ERR_SHAPE if b_eff does not divide a sub-problem size, if a causal block
- * to be split has odd size, or if n >= 2^31.
+ * to be split has odd size, or if one head (n * d elements) exceeds 2 GiB.
  * workspace: >= hyperattn_workspace_bytes(...) with the same arguments.
  */
 int hyperattn_forward(const void* Q, const void* K, const void* V, void* O,
