@@ -143,6 +143,18 @@ def make_inputs(w, heads=None):
     return np.stack(Qs), np.stack(Ks), np.stack(Vs), P
 
 
+def make_inputs_parallel(w, heads=None, workers=None):
+    """make_inputs with heads generated on a thread pool (numpy releases the GIL)."""
+    import concurrent.futures as cf
+    import os
+    hs = list(range(w.heads)) if heads is None else list(heads)
+    workers = workers or max(1, min(16, len(os.sched_getaffinity(0))))
+    with cf.ThreadPoolExecutor(workers) as ex:
+        res = list(ex.map(lambda h: make_head(w, h), hs))
+    return (np.stack([r[0] for r in res]), np.stack([r[1] for r in res]),
+            np.stack([r[2] for r in res]), [r[3] for r in res])
+
+
 def scaled(w, **changes):
     """A copy of a workload with some fields replaced (smaller test shapes)."""
     d = dict(w.__dict__)

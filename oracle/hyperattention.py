@@ -115,18 +115,21 @@ def _head_inputs(Q, K, V):
 
 
 def hyperattention(Q, K, V, *, causal, b, m, r=8, recursion_base=4096, seed=0,
-                   rows=None, artifacts=None, G=None):
+                   rows=None, artifacts=None, G=None, head_ids=None):
     """HyperAttention forward for all heads. Q, K, V: [H, n, d].
 
     rows: optional list of query rows to evaluate (all heads); others are NaN.
     artifacts: optional dict filled with codes, sorts and sample lists.
     G: optional hyperplanes [H, r, d] (defaults to sortlsh.hyperplanes(seed)).
+    head_ids: the head index of each entry of the first axis (default 0..H-1);
+    hyperplanes and random draws depend on it.
     Returns O [H, n, d] and lse [H, n] (fp64).
     """
     H, n, d = np.shape(Q)
     scale = 1.0 / np.sqrt(d)
+    hids = list(range(H)) if head_ids is None else list(head_ids)
     if G is None:
-        G = sortlsh.hyperplanes(seed, H, r, d)
+        G = sortlsh.hyperplanes(seed, max(hids) + 1, r, d)[hids]
     subs, blocks = schedule(n, causal, recursion_base)
     want = None
     if rows is not None:
@@ -138,6 +141,7 @@ def hyperattention(Q, K, V, *, causal, b, m, r=8, recursion_base=4096, seed=0,
         artifacts.update(G=G, codes_q=[], codes_k=[], W=[], P=[], subs=subs,
                          blocks=blocks, sub=[])
     for h in range(H):
+        hid = hids[h]
         Qh, Kh, Vh = _head_inputs(Q[h], K[h], V[h])
         codes_q = sortlsh.hash_codes(Qh, G[h])
         codes_k = sortlsh.hash_codes(Kh, G[h])
@@ -159,8 +163,8 @@ def hyperattention(Q, K, V, *, causal, b, m, r=8, recursion_base=4096, seed=0,
             I = slice(q_lo, q_lo + size)
             J = slice(k_lo, k_lo + size)
             srt = sortlsh.sortlsh(codes_q[I], codes_k[J], b)
-            u_idx, alpha = sampling.uniform_samples(seed, h, node, k_lo, size, m)
-            v_idx, v_w = sampling.vnorm_samples(seed, h, node, k_lo, size, P, W, m)
+            u_idx, alpha = sampling.uniform_samples(seed, hid, node, k_lo, size, m)
+            v_idx, v_w = sampling.vnorm_samples(seed, hid, node, k_lo, size, P, W, m)
             w_sub = None if want is None else want[I]
             if w_sub is None or w_sub.any():
                 Op, lp = estimate_block(Qh[I], Kh[J], Vh[J], srt, u_idx - k_lo,

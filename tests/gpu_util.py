@@ -45,3 +45,67 @@ def region(ws, layout, name, dtype):
 
 def banner(msg):
     print(f"[gpu-case] {msg}", flush=True)
+
+
+def check_artifacts(w, ws, layout, art, gpu_heads):
+    """Compare the library's integer artefacts for the listed heads (bit-exact)
+    with the oracle's artefact dict (oracle head index k <-> gpu_heads[k])."""
+    H, n = w.heads, w.n
+    cq = region(ws, layout, "CODES_Q", np.uint8).reshape(H, n)
+    ck = region(ws, layout, "CODES_K", np.uint8).reshape(H, n)
+    Wg = region(ws, layout, "VNORM_W", np.uint64).reshape(H, n)
+    Pg = region(ws, layout, "VNORM_P", np.uint64).reshape(H, n + 1)
+    subs = art["subs"]
+    L = max(s[0] for s in subs)
+    S = n if not w.causal else n // 2
+    permq = region(ws, layout, "PERM_Q", np.int32).reshape(L, H, S)
+    permk = region(ws, layout, "PERM_K", np.int32).reshape(L, H, S)
+    rankk = region(ws, layout, "RANK_K", np.int32).reshape(L, H, S)
+    nodes = 2 ** L - 1 if w.causal else 1
+    m = w.m
+    uidx = region(ws, layout, "U_IDX", np.int32).reshape(H, nodes, m)
+    ubkt = region(ws, layout, "U_BKT", np.int32).reshape(H, nodes, m)
+    vidx = region(ws, layout, "V_IDX", np.int32).reshape(H, nodes, m)
+    vbkt = region(ws, layout, "V_BKT", np.int32).reshape(H, nodes, m)
+    vw = region(ws, layout, "V_W", np.float32).reshape(H, nodes, m)
+    meta = region(ws, layout, "NODE_META", np.int32).reshape(H, nodes, 4)
+    for k, h in enumerate(gpu_heads):
+        assert np.array_equal(cq[h], art["codes_q"][k]), f"codes_q head {h}"
+        assert np.array_equal(ck[h], art["codes_k"][k]), f"codes_k head {h}"
+        assert np.array_equal(Wg[h], art["W"][k]), f"W head {h}"
+        assert np.array_equal(Pg[h], art["P"][k]), f"P head {h}"
+        for a in art["sub"][k]:
+            lv, node, size = a["level"] - 1, a["node"], a["size"]
+            s = node - (1 << lv)
+            sl = slice(s * size, (s + 1) * size)
+            assert np.array_equal(permq[lv, h, sl], a["perm_q"]), f"perm_q {h} node {node}"
+            assert np.array_equal(permk[lv, h, sl], a["perm_k"]), f"perm_k {h} node {node}"
+            assert np.array_equal(rankk[lv, h, sl], a["rank_k"]), f"rank_k {h} node {node}"
+            mt = meta[h, node - 1]
+            assert mt[0] == len(a["u_idx"]) and mt[1] == len(a["v_idx"])
+            assert mt[2] == np.float32(a["alpha"]).view(np.int32)
+            assert mt[3] == a["b_eff"]
+            assert np.array_equal(uidx[h, node - 1, :mt[0]], a["u_idx"])
+            assert np.array_equal(ubkt[h, node - 1, :mt[0]], a["u_bucket"])
+            assert np.array_equal(vidx[h, node - 1, :mt[1]], a["v_idx"])
+            assert np.array_equal(vbkt[h, node - 1, :mt[1]], a["v_bucket"])
+            assert np.array_equal(vw[h, node - 1, :mt[1]].view(np.uint32),
+                                  a["v_w"].view(np.uint32))
+
+
+def run_forward(w, Q, K, V, fill=True):
+    """hyperattn_forward through the C ABI with a visible workspace."""
+    import torch
+    from approximate_softmax_attention_amd import api
+    dt = 1 if w.dtype == "bf16" else 0
+    kw = dict(causal=w.causal, b=w.b, m=w.m, r=w.r, recursion_base=w.recursion_base, dtype=dt)
+    layout = api.workspace_layout(w.n, w.d, w.heads, **kw)
+    ws = api.alloc_workspace(api.workspace_bytes(w.n, w.d, w.heads, **kw), "cuda")
+    if fill:
+        ws.fill_(0xAB)
+    q, k, v = (to_dev(x, w.dtype) for x in (Q, K, V))
+    O, L = api.forward(q, k, v, causal=w.causal, b=w.b, m=w.m, r=w.r,
+                       recursion_base=w.recursion_base, seed=w.method_seed, return_lse=True,
+                       workspace=ws)
+    torch.cuda.synchronize()
+    return O, L, ws, layout

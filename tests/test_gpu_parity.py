@@ -13,7 +13,8 @@ from approximate_softmax_attention_amd import workloads as wl
 from oracle import exact as oexact
 from oracle import hyperattention as oha
 from oracle import sortlsh as osl
-from tests.gpu_util import TOL, banner, max_rel, region, to_dev, to_np
+from tests.gpu_util import (TOL, banner, check_artifacts, max_rel, region, run_forward,
+                            to_dev, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -98,64 +99,11 @@ def test_hash_near_zero_projections_use_exact_sign():
 # ------------------------------------------------- forward: integer artefacts
 
 def _check_artifacts(w, Q, K, V, ws, layout, art):
-    H, n = w.heads, w.n
-    cq = region(ws, layout, "CODES_Q", np.uint8).reshape(H, n)
-    ck = region(ws, layout, "CODES_K", np.uint8).reshape(H, n)
-    Wg = region(ws, layout, "VNORM_W", np.uint64).reshape(H, n)
-    Pg = region(ws, layout, "VNORM_P", np.uint64).reshape(H, n + 1)
-    subs = art["subs"]
-    L = max(s[0] for s in subs)
-    S = n if not w.causal else n // 2
-    permq = region(ws, layout, "PERM_Q", np.int32).reshape(L, H, S)
-    permk = region(ws, layout, "PERM_K", np.int32).reshape(L, H, S)
-    rankk = region(ws, layout, "RANK_K", np.int32).reshape(L, H, S)
-    nodes = 2 ** L - 1 if w.causal else 1
-    m = w.m
-    uidx = region(ws, layout, "U_IDX", np.int32).reshape(H, nodes, m)
-    ubkt = region(ws, layout, "U_BKT", np.int32).reshape(H, nodes, m)
-    vidx = region(ws, layout, "V_IDX", np.int32).reshape(H, nodes, m)
-    vbkt = region(ws, layout, "V_BKT", np.int32).reshape(H, nodes, m)
-    vw = region(ws, layout, "V_W", np.float32).reshape(H, nodes, m)
-    meta = region(ws, layout, "NODE_META", np.int32).reshape(H, nodes, 4)
-    for h in range(H):
-        assert np.array_equal(cq[h], art["codes_q"][h])
-        assert np.array_equal(ck[h], art["codes_k"][h])
-        assert np.array_equal(Wg[h], art["W"][h])
-        assert np.array_equal(Pg[h], art["P"][h])
-        for a in art["sub"][h]:
-            lv, node, size = a["level"] - 1, a["node"], a["size"]
-            s = node - (1 << lv)
-            sl = slice(s * size, (s + 1) * size)
-            assert np.array_equal(permq[lv, h, sl], a["perm_q"])
-            assert np.array_equal(permk[lv, h, sl], a["perm_k"])
-            assert np.array_equal(rankk[lv, h, sl], a["rank_k"])
-            mt = meta[h, node - 1]
-            assert mt[0] == len(a["u_idx"]) and mt[1] == len(a["v_idx"])
-            assert mt[2] == np.float32(a["alpha"]).view(np.int32)
-            assert mt[3] == a["b_eff"]
-            assert np.array_equal(uidx[h, node - 1, :mt[0]], a["u_idx"])
-            assert np.array_equal(ubkt[h, node - 1, :mt[0]], a["u_bucket"])
-            assert np.array_equal(vidx[h, node - 1, :mt[1]], a["v_idx"])
-            assert np.array_equal(vbkt[h, node - 1, :mt[1]], a["v_bucket"])
-            assert np.array_equal(vw[h, node - 1, :mt[1]].view(np.uint32),
-                                  a["v_w"].view(np.uint32))
+    check_artifacts(w, ws, layout, art, list(range(w.heads)))
 
 
 def _run_forward(w, Q, K, V):
-    import torch
-    api = _api()
-    dt = 1 if w.dtype == "bf16" else 0
-    layout = api.workspace_layout(w.n, w.d, w.heads, causal=w.causal, b=w.b, m=w.m, r=w.r,
-                                  recursion_base=w.recursion_base, dtype=dt)
-    nb = api.workspace_bytes(w.n, w.d, w.heads, causal=w.causal, b=w.b, m=w.m, r=w.r,
-                             recursion_base=w.recursion_base, dtype=dt)
-    ws = api.alloc_workspace(nb, "cuda")
-    ws.fill_(0xAB)
-    O, L = api.forward(to_dev(Q, w.dtype), to_dev(K, w.dtype), to_dev(V, w.dtype),
-                       causal=w.causal, b=w.b, m=w.m, r=w.r, recursion_base=w.recursion_base,
-                       seed=w.method_seed, return_lse=True, workspace=ws)
-    torch.cuda.synchronize()
-    return O, L, ws, layout
+    return run_forward(w, Q, K, V)
 
 
 FORWARD_CASES = {
