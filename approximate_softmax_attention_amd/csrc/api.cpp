@@ -175,8 +175,9 @@ int hyperattn_forward(const void* Q, const void* K, const void* V, void* O, floa
   rc = check_workspace(p, workspace, workspace_bytes);
   if (rc != HA_OK) return rc;
   const float* G = nullptr;
-  if ((rc = device_hyperplanes(seed, heads, r, d, &G)) != HA_OK) return rc;
-  if ((rc = launch_hash(p, Q, K, V, G, workspace, s)) != HA_OK) return rc;
+  const uint16_t* Gb = nullptr;
+  if ((rc = device_hyperplanes(seed, heads, r, d, &G, &Gb)) != HA_OK) return rc;
+  if ((rc = launch_hash(p, Q, K, V, G, Gb, workspace, s)) != HA_OK) return rc;
   if ((rc = launch_vnorm_scan(p, workspace, s)) != HA_OK) return rc;
   if ((rc = launch_sort(p, workspace, 2, s)) != HA_OK) return rc;
   if ((rc = launch_samples(p, seed, workspace, s)) != HA_OK) return rc;
@@ -204,8 +205,9 @@ int rowsum_estimate(const void* Q, const void* K, int64_t n, int d, int heads, i
   if (rc != HA_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float* G = nullptr;
-  if ((rc = device_hyperplanes(seed, heads, r, d, &G)) != HA_OK) return rc;
-  if ((rc = launch_hash(p, Q, K, nullptr, G, workspace, s)) != HA_OK) return rc;
+  const uint16_t* Gb = nullptr;
+  if ((rc = device_hyperplanes(seed, heads, r, d, &G, &Gb)) != HA_OK) return rc;
+  if ((rc = launch_hash(p, Q, K, nullptr, G, Gb, workspace, s)) != HA_OK) return rc;
   if ((rc = launch_sort(p, workspace, 2, s)) != HA_OK) return rc;
   if ((rc = launch_samples(p, seed, workspace, s)) != HA_OK) return rc;
   return launch_bucket_attention(p, Q, K, nullptr, nullptr, log_d, workspace, s);
@@ -239,9 +241,10 @@ int sortlsh_hash(const void* X, int64_t n, int d, int heads, int r, uint64_t see
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float* G = nullptr;
+  const uint16_t* Gb = nullptr;
   int rc;
-  if ((rc = device_hyperplanes(seed, heads, r, d, &G)) != HA_OK) return rc;
-  if ((rc = launch_hash_one(X, n, d, heads, r, dtype, G, codes, s)) != HA_OK) return rc;
+  if ((rc = device_hyperplanes(seed, heads, r, d, &G, &Gb)) != HA_OK) return rc;
+  if ((rc = launch_hash_one(X, n, d, heads, r, dtype, G, Gb, codes, s)) != HA_OK) return rc;
   if (perm) rc = launch_sort_single(codes, n, heads, perm, workspace, s);
   return rc;
 }

@@ -95,15 +95,18 @@ int make_plan(Plan& p, int64_t n, int d, int heads, int causal, int b, int m,
 int check_workspace(const Plan& p, const void* ws, size_t ws_bytes);
 
 // Hyperplanes on the device for (seed, heads, r, d); cached per device.
-int device_hyperplanes(uint64_t seed, int heads, int r, int d, const float** out);
+// *out: fp32 values [heads][r][d]; *out_bf16 (optional): the same values as
+// bf16 bit patterns in [heads][16][d], hyperplanes r..15 zero.
+int device_hyperplanes(uint64_t seed, int heads, int r, int d, const float** out,
+                       const uint16_t** out_bf16 = nullptr);
 void host_hyperplanes(uint64_t seed, int heads, int r, int d, float* G);
 
 // --------------------------------------------------------------- launchers
 // All return HA_OK or HA_ERR_HIP; arguments are validated by the caller.
 int launch_hash(const Plan& p, const void* Q, const void* K, const void* V,
-                const float* G, void* ws, hipStream_t s);
+                const float* G, const uint16_t* Gb, void* ws, hipStream_t s);
 int launch_hash_one(const void* X, int64_t n, int d, int heads, int r, int dtype,
-                    const float* G, uint8_t* codes, hipStream_t s);
+                    const float* G, const uint16_t* Gb, uint8_t* codes, hipStream_t s);
 int launch_vnorm_scan(const Plan& p, void* ws, hipStream_t s);
 int launch_sort(const Plan& p, void* ws, int sides, hipStream_t s);
 int launch_sort_single(const uint8_t* codes, int64_t n, int heads, int32_t* perm,

@@ -4,11 +4,13 @@
 //
 // Each element comes from two counter-based draws of SplitMix64 (Steele, Lea
 // and Flood, OOPSLA 2014), turned into one normal by the Box-Muller transform
-// (Box and Muller, 1958) in fp64 with the C library's log, sqrt and cos, and
-// rounded to fp32. They are generated on the host so that the values are
+// (Box and Muller, 1958) in fp64 with the C library's log, sqrt and cos,
+// rounded to fp32 and then to the nearest bfloat16 (a bf16 input times a
+// hyperplane entry is then exact in fp32). They are generated on the host so that the values are
 // fixed by the C library, and kept on each device in a small cache keyed by
 // (seed, heads, r, d).
 #include <cmath>
+#include <cstring>
 #include <mutex>
 #include <vector>
 
@@ -36,7 +38,8 @@ struct Entry {
   int device;
   uint64_t seed;
   int heads, r, d;
-  float* ptr;
+  float* ptr;          // fp32 [heads][r][d]
+  uint16_t* ptr_bf16;  // bf16 [heads][16][d], rows >= r zero
   uint64_t stamp;
 };
 
@@ -44,6 +47,16 @@ std::mutex g_mu;
 std::vector<Entry> g_cache;
 uint64_t g_clock = 0;
 constexpr size_t kCacheEntries = 16;
+
+// Nearest bfloat16 of an fp32 value (ties to even), kept as an fp32 value.
+float round_bf16(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, 4);
+  u = ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16) << 16;
+  float y;
+  std::memcpy(&y, &u, 4);
+  return y;
+}
 
 }  // namespace
 
@@ -60,11 +73,12 @@ void host_hyperplanes(uint64_t seed, int heads, int r, int d, float* G) {
         const double u1 = double((a >> 11) + 1) * 0x1p-53;
         const double u2 = double(b >> 11) * 0x1p-53;
         const double g = std::sqrt(-2.0 * std::log(u1)) * std::cos(two_pi * u2);
-        G[(int64_t(h) * r + k) * d + t] = static_cast<float>(g);
+        G[(int64_t(h) * r + k) * d + t] = round_bf16(static_cast<float>(g));
       }
 }
 
-int device_hyperplanes(uint64_t seed, int heads, int r, int d, const float** out) {
+int device_hyperplanes(uint64_t seed, int heads, int r, int d, const float** out,
+                       const uint16_t** out_bf16) {
   int dev = 0;
   HA_HIP_TRY(hipGetDevice(&dev));
   std::lock_guard<std::mutex> lock(g_mu);
@@ -72,6 +86,7 @@ int device_hyperplanes(uint64_t seed, int heads, int r, int d, const float** out
     if (e.device == dev && e.seed == seed && e.heads == heads && e.r == r && e.d == d) {
       e.stamp = ++g_clock;
       *out = e.ptr;
+      if (out_bf16) *out_bf16 = e.ptr_bf16;
       return HA_OK;
     }
   if (g_cache.size() >= kCacheEntries) {
@@ -83,21 +98,39 @@ int device_hyperplanes(uint64_t seed, int heads, int r, int d, const float** out
     HA_HIP_TRY(hipSetDevice(g_cache[old].device));
     HA_HIP_TRY(hipDeviceSynchronize());
     HA_HIP_TRY(hipFree(g_cache[old].ptr));
+    HA_HIP_TRY(hipFree(g_cache[old].ptr_bf16));
     HA_HIP_TRY(hipSetDevice(cur));
     g_cache.erase(g_cache.begin() + old);
   }
   const size_t count = size_t(heads) * r * d;
   std::vector<float> host(count);
   host_hyperplanes(seed, heads, r, d, host.data());
+  const size_t count16 = size_t(heads) * 16 * d;
+  std::vector<uint16_t> host16(count16, 0);
+  for (int h = 0; h < heads; ++h)
+    for (int k = 0; k < r; ++k)
+      for (int t = 0; t < d; ++t) {
+        uint32_t u;
+        std::memcpy(&u, &host[(size_t(h) * r + k) * d + t], 4);
+        host16[(size_t(h) * 16 + k) * d + t] = uint16_t(u >> 16);   // exact: bf16 values
+      }
   float* ptr = nullptr;
+  uint16_t* ptr16 = nullptr;
   HA_HIP_TRY(hipMalloc(&ptr, count * sizeof(float)));
-  hipError_t e = hipMemcpy(ptr, host.data(), count * sizeof(float), hipMemcpyHostToDevice);
+  hipError_t e = hipMalloc(&ptr16, count16 * sizeof(uint16_t));
+  if (e == hipSuccess)
+    e = hipMemcpy(ptr, host.data(), count * sizeof(float), hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(ptr16, host16.data(), count16 * sizeof(uint16_t), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(ptr);
-    return fail(HA_ERR_HIP, "hipMemcpy of hyperplanes failed: %s", hipGetErrorString(e));
+    if (ptr16) (void)hipFree(ptr16);
+    return fail(HA_ERR_HIP, "copy of hyperplanes to the device failed: %s",
+                hipGetErrorString(e));
   }
-  g_cache.push_back(Entry{dev, seed, heads, r, d, ptr, ++g_clock});
+  g_cache.push_back(Entry{dev, seed, heads, r, d, ptr, ptr16, ++g_clock});
   *out = ptr;
+  if (out_bf16) *out_bf16 = ptr16;
   return HA_OK;
 }
 

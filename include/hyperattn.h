@@ -143,9 +143,10 @@ int rowsum_estimate(const void* Q, const void* K, int64_t n, int d, int heads,
 /*
  * sortlsh_hyperplanes — host-only: the r Gaussian hyperplanes per head the
  * hash uses (HA page, "Algorithm", Definition 1; hash family as read here).
- * G_host[h][k][t] (fp32) = Box-Muller normal from two counter-based
- * SplitMix64 draws (purpose 1, head h, node 0, counters 2e and 2e+1 with
- * e = k*d + t): sqrt(-2 ln u1) cos(2 pi u2), u1 in (0,1], u2 in [0,1).
+ * G_host[h][k][t] (fp32 holding a bf16 value) = Box-Muller normal from two
+ * counter-based SplitMix64 draws (purpose 1, head h, node 0, counters 2e and
+ * 2e+1 with e = k*d + t): sqrt(-2 ln u1) cos(2 pi u2), u1 in (0,1],
+ * u2 in [0,1), rounded to fp32 and then to the nearest bf16 (ties to even).
  * Touches no device. G_host must hold heads*r*d floats.
  */
 int sortlsh_hyperplanes(uint64_t seed, int heads, int r, int d, float* G_host);

@@ -23,9 +23,11 @@ The definition and the algorithm were lost in extraction. Readings taken:
 * Hyperplanes are Gaussian via Box-Muller (Box and Muller, 1958) from two
   counter-based uniforms: u1 = (draw >> 11 + 1) 2^-53 in (0, 1],
   u2 = (draw >> 11) 2^-53 in [0, 1); g = sqrt(-2 ln u1) cos(2 pi u2), rounded
-  to fp32. Element (k, t) of head h uses counters 2(k d + t) and 2(k d + t)+1
-  of purpose "hyperplane" with node 0. Python's math module (the C library)
-  evaluates log, sqrt and cos.
+  to fp32 and then to the nearest bfloat16 (ties to even), so that the
+  product of a bf16 input with a hyperplane entry is exact in fp32. Element
+  (k, t) of head h uses counters 2(k d + t) and 2(k d + t)+1 of purpose
+  "hyperplane" with node 0. Python's math module (the C library) evaluates
+  log, sqrt and cos.
 """
 
 import math
@@ -35,8 +37,17 @@ import numpy as np
 from . import rng
 
 
+def round_bf16(x32):
+    """Nearest bfloat16 of an fp32 value (ties to even), returned as fp32."""
+    bits = int(np.array(x32, dtype=np.float32).view(np.uint32))
+    lsb = (bits >> 16) & 1
+    bits = ((bits + 0x7FFF + lsb) >> 16) << 16
+    return np.array(bits & 0xFFFFFFFF, dtype=np.uint32).view(np.float32)
+
+
 def hyperplanes(seed, heads, r, d):
-    """G[h, k, t]: r Gaussian hyperplanes of dimension d per head, fp32."""
+    """G[h, k, t]: r Gaussian hyperplanes of dimension d per head (bf16 values
+    held in fp32)."""
     G = np.empty((heads, r, d), dtype=np.float32)
     for h in range(heads):
         for k in range(r):
@@ -47,7 +58,7 @@ def hyperplanes(seed, heads, r, d):
                 u1 = ((a >> 11) + 1) * 2.0 ** -53
                 u2 = (b >> 11) * 2.0 ** -53
                 g = math.sqrt(-2.0 * math.log(u1)) * math.cos(2.0 * math.pi * u2)
-                G[h, k, t] = np.float32(g)
+                G[h, k, t] = round_bf16(np.float32(g))
     return G
 
 

@@ -96,6 +96,29 @@ def test_hash_near_zero_projections_use_exact_sign():
     assert np.array_equal(codes[0].cpu().numpy(), ref)
 
 
+def test_hash_bf16_cancelling_rows_use_exact_sign():
+    """bf16 rows built so that <x, g_k> is exactly 0 or a tiny fraction of
+    sum |x_t g_kt> (far below the fp32 certainty bound) must take the fp64
+    re-check and agree with the sequential definition."""
+    banner("hash bf16 cancellation")
+    d, r = 128, 8
+    G = osl.hyperplanes(17, 1, r, d)[0]
+    rs = np.random.default_rng(3)
+    X = np.zeros((512, d), dtype=np.float32)
+    for i in range(512):
+        k = i % r
+        a, b, c = rs.choice(d, 3, replace=False)
+        X[i, a], X[i, b] = G[k, b], -G[k, a]            # cancels exactly on g_k
+        if i % 3:
+            X[i, c] = np.float32(2.0 ** -30) * (1 if i % 2 else -1)
+        X[i] += 0.0
+    api = _api()
+    codes = api.sortlsh_hash(to_dev(X[None], "bf16"), r=r, seed=17)
+    _sync()
+    ref = osl.hash_codes(X, G)
+    assert np.array_equal(codes[0].cpu().numpy(), ref)
+
+
 # ------------------------------------------------- forward: integer artefacts
 
 def _check_artifacts(w, Q, K, V, ws, layout, art):

@@ -74,6 +74,15 @@ def test_hyperplane_gaussian_moments():
     assert stats.kstest(G, "norm").pvalue > 1e-4
 
 
+def test_hyperplanes_are_bf16_values():
+    G = sortlsh.hyperplanes(3, 2, 8, 64)
+    bits = G.view(np.uint32)
+    assert not (bits & 0xFFFF).any()
+    # rounding to nearest: the fp32 Gaussian is within half a bf16 ulp
+    assert sortlsh.round_bf16(np.float32(1.0 + 2 ** -9)) == np.float32(1.0)
+    assert sortlsh.round_bf16(np.float32(1.0 + 3 * 2 ** -9)) == np.float32(1.0 + 2 ** -7)
+
+
 def test_hyperplanes_differ_by_head_and_seed():
     a = sortlsh.hyperplanes(1, 2, 2, 16)
     b = sortlsh.hyperplanes(2, 2, 2, 16)
