@@ -90,4 +90,4 @@ def header_functions():
 WS_REGIONS = ["CODES_Q", "CODES_K", "VNORM_A", "VNORM_W", "VNORM_P", "VNORM_BLK",
               "PERM_Q", "PERM_K", "RANK_K", "SORT_HIST", "SORT_OFFS",
               "U_IDX", "U_BKT", "V_IDX", "V_BKT", "V_W", "NODE_META",
-              "PART_O", "PART_LSE"]
+              "PART_O", "PART_LSE", "SCHED"]

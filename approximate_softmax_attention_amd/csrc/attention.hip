@@ -42,6 +42,7 @@
 // remapped so that consecutive logical tiles (which share key blocks or
 // sample lists) run on the same XCD and share its L2.
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 #include "device_util.h"
@@ -74,8 +75,17 @@ template <int D>
 struct alignas(16) Buf<bf16_t, D> {
   static constexpr int KT = 128;
   static constexpr int CPR = D / 8;                    // 16-byte chunks per row
-  static constexpr int SHIFT = D == 128 ? 0 : 1;
-  __device__ static int swz(int row) { return (row >> SHIFT) & (CPR - 1); }
+  // Physical chunk = logical chunk XOR swz(row). swz is a bijection on the
+  // rows that share one 256-byte bank window pattern (16 rows for d = 128,
+  // 8 row pairs for d = 64), so the rows of a K fragment read hit distinct
+  // banks; its high bits follow the row's low bits, so the four consecutive
+  // rows of one transposing V read fall in four different 64-byte bank
+  // groups.
+  __device__ static int swz(int row) {
+    if (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    const int u = (row >> 1) & 7;
+    return ((u & 1) << 2) | (((u >> 2) & 1) << 1) | ((u >> 1) & 1);
+  }
   bf16_t k[KT * D];
   bf16_t v[KT * D];
   float w[KT];                                         // per-slot weight
@@ -97,6 +107,7 @@ struct alignas(16) Buf<float, D> {
 template <typename T, int D>
 struct Smem {
   Buf<T, D> buf[2];
+  int64_t item;            // next work item (persistent launches)
 };
 
 template <typename T, int D>
@@ -104,6 +115,7 @@ struct SmemG {
   Buf<T, D> buf[2];
   alignas(16) int32_t srow[kSlotCap];
   alignas(16) float sw[kSlotCap];
+  int64_t item;            // next work item (persistent launches)
 };
 
 struct AttnArgs {
@@ -118,6 +130,7 @@ struct AttnArgs {
   // EXACT
   int64_t block;           // key/query block size (n for plain exact attention)
   int64_t tiles_per_block; // ceil(block / kAttnQ)
+  uint32_t items_per_head; // blocks per head * tiles_per_block
   int causal;
   int merge_levels;        // base case: number of levels to merge (0: none)
   const void* part_o;      // [L][heads][S][d]
@@ -135,6 +148,9 @@ struct AttnArgs {
   const int32_t* v_bkt;
   const float* v_w;
   const int32_t* meta;
+  // work queue of a persistent launch
+  uint32_t* queue;         // [kQueues] counters, zero at launch; nullptr: one item per group
+  uint32_t items;          // total work items
 };
 
 __device__ __forceinline__ f32x16 zero16() {
@@ -491,29 +507,50 @@ __device__ __forceinline__ void store_row(const WaveState<T, D>& ws, T* __restri
     }
 }
 
-// Merge a normalised partial (po, plse) into (ws.o, lse).
+// A normalised partial result of this lane's query: its half of the output
+// row (the lane's d positions, as store_row writes them) and its lse.
+template <typename T, int D> struct Partial;
+template <int D> struct Partial<bf16_t, D> { uint2 raw[D / 8]; float lse; };
+template <int D> struct Partial<float, D> { float4 raw[D / 8]; float lse; };
+
 template <typename T, int D>
-__device__ __forceinline__ float merge_partial(WaveState<T, D>& ws, float lse,
-                                               const T* __restrict__ po, float plse) {
+__device__ __forceinline__ void load_partial(Partial<T, D>& pt, const T* __restrict__ po,
+                                             const float* plse) {
   const int g = lane_id() >> 5;
-  const float mx = fmaxf(lse, plse);
-  const float wa = __expf(lse - mx);
-  const float wb = __expf(plse - mx);
-  const float inv = 1.f / (wa + wb);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int d0 = 32 * db + 8 * q4 + 4 * g;
+      if constexpr (sizeof(T) == 2)
+        pt.raw[4 * db + q4] = *reinterpret_cast<const uint2*>(po + d0);
+      else
+        pt.raw[4 * db + q4] = *reinterpret_cast<const float4*>(po + d0);
+    }
+  pt.lse = *plse;
+}
+
+// Merge a partial into (ws.o, lse) by log-sum-exp weights; returns the new lse.
+template <typename T, int D>
+__device__ __forceinline__ float merge_partial(WaveState<T, D>& ws, float lse,
+                                               const Partial<T, D>& pt) {
+  const float mx = fmaxf(lse, pt.lse);
+  const float wa = __expf(lse - mx);
+  const float wb = __expf(pt.lse - mx);
+  const float inv = 1.f / (wa + wb);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
       float v[4];
       if constexpr (sizeof(T) == 2) {
-        const uint2 raw = *reinterpret_cast<const uint2*>(po + d0);
+        const uint2 raw = pt.raw[4 * db + q4];
         v[0] = __uint_as_float(raw.x << 16);
         v[1] = __uint_as_float(raw.x & 0xFFFF0000u);
         v[2] = __uint_as_float(raw.y << 16);
         v[3] = __uint_as_float(raw.y & 0xFFFF0000u);
       } else {
-        const float4 raw = *reinterpret_cast<const float4*>(po + d0);
+        const float4 raw = pt.raw[4 * db + q4];
         v[0] = raw.x; v[1] = raw.y; v[2] = raw.z; v[3] = raw.w;
       }
 #pragma unroll
@@ -523,20 +560,91 @@ __device__ __forceinline__ float merge_partial(WaveState<T, D>& ws, float lse,
   return mx + __logf(wa + wb);
 }
 
+// Waves per SIMD to aim for: with bf16 and d = 64 two work-groups fit a
+// CU's LDS, so those kernels keep to the 128 registers that four waves per
+// SIMD allow.
+template <typename T, int D> struct WavesPerEu {
+  static constexpr int value = sizeof(T) == 2 && D == 64 ? 4 : 2;
+};
+
+// ------------------------------------------------------------- work queues
+// A persistent launch runs one work-group per resident slot of the device.
+// Work items are split into kQueues contiguous ranges, one per XCD; a
+// work-group takes items from the queue of the XCD it runs on and, once that
+// one is empty, from the others in turn. Neighbouring items (which share key
+// blocks or sample lists) so run on the same XCD and share its L2, and no
+// work-group waits for the in-order dispatch of others. The next item's
+// counter is fetched while the current item runs.
+__device__ __forceinline__ int hw_xcc() {
+  // HW_REG_XCC_ID (hardware register 20), all 32 bits
+  return int(__builtin_amdgcn_s_getreg((31 << 11) | 20)) & (kQueues - 1);
+}
+
+// Item for counter value `taken` of queue qi, or the next free item of the
+// following queues; -1 when every queue is empty. Called by one thread.
+__device__ __forceinline__ int64_t queue_resolve(uint32_t* ctr, uint32_t items, int& qi,
+                                              uint32_t taken) {
+  const uint32_t per = (items + kQueues - 1) / kQueues;
+  for (int k = 0; k < kQueues; ++k) {
+    const uint32_t lo = min(items, uint32_t(qi) * per);
+    const uint32_t hi = min(items, lo + per);
+    if (taken < hi - lo) return int64_t(lo + taken);
+    if (k + 1 == kQueues) break;
+    qi = (qi + 1) & (kQueues - 1);
+    taken = atomicAdd(&ctr[qi], 1u);
+  }
+  return -1;
+}
+
+// Runs item_fn over this work-group's items: one (from the linear block
+// index, remapped so that neighbouring items share an XCD) when the launch
+// has no queue, else
+// items taken from the queues until all are done. item_fn must contain a
+// barrier before it returns.
+template <typename ItemFn>
+__device__ __forceinline__ void run_items(const AttnArgs& a, int64_t& s_item,
+                                          const ItemFn& item_fn) {
+  int qi = hw_xcc();
+  int64_t item;
+  if (!a.queue) {
+    item = xcd_remap(int64_t(blockIdx.y) * gridDim.x + blockIdx.x,
+                     int64_t(gridDim.x) * gridDim.y);
+  } else {
+    if (threadIdx.x == 0)
+      s_item = queue_resolve(a.queue, a.items, qi, atomicAdd(&a.queue[qi], 1u));
+    __syncthreads();
+    item = s_item;
+  }
+  while (item >= 0) {
+    uint32_t pre = 0;
+    if (a.queue && threadIdx.x == 0) pre = atomicAdd(&a.queue[qi], 1u);
+    item_fn(item);
+    if (!a.queue) break;
+    if (threadIdx.x == 0) s_item = queue_resolve(a.queue, a.items, qi, pre);
+    __syncthreads();
+    item = s_item;
+  }
+}
+
+__global__ void queue_reset_kernel(uint32_t* ctr) {
+  if (threadIdx.x < kQueues) ctr[threadIdx.x] = 0u;
+}
+
 // ------------------------------------------------------------- EXACT kernel
-// grid: (blocks_per_head * tiles_per_block, heads). Causal tiles are visited
-// from the longest (last) to the shortest for load balance.
+// Work item lin = head * items_per_head + blk * tiles_per_block + t: query
+// tile t of key block blk. Causal tiles are taken from the longest (last) to
+// the shortest for load balance.
 template <typename T, int D, bool kCausal>
-__global__ __launch_bounds__(kThreads, 1) void exact_kernel(AttnArgs a) {
-  __shared__ Smem<T, D> sm;
+__device__ __forceinline__ void exact_item(const AttnArgs& a, Smem<T, D>& sm, uint32_t lin) {
   constexpr int KT = Buf<T, D>::KT;
-  const int64_t nx = int64_t(gridDim.x) * gridDim.y;
-  const int64_t lin = xcd_remap(int64_t(blockIdx.y) * gridDim.x + blockIdx.x, nx);
-  const int head = int(lin / gridDim.x);
-  const int64_t bx = lin % gridDim.x;
-  const int64_t tpb = a.tiles_per_block;
-  const int64_t blk = bx / tpb;
-  const int64_t tile = kCausal ? tpb - 1 - bx % tpb : bx % tpb;
+  // 32-bit division: far cheaper than 64-bit, and the counts fit
+  const uint32_t gx = a.items_per_head;
+  const int head = int(lin / gx);
+  const uint32_t bx = lin - uint32_t(head) * gx;
+  const uint32_t tpb = uint32_t(a.tiles_per_block);
+  const uint32_t blk = bx / tpb;
+  const uint32_t tl = bx - blk * tpb;
+  const int64_t tile = kCausal ? int64_t(tpb - 1 - tl) : int64_t(tl);
   const int64_t b_lo = blk * a.block;
   const int64_t b_hi = b_lo + a.block < a.n ? b_lo + a.block : a.n;
   const int64_t q0 = b_lo + tile * kAttnQ;
@@ -590,46 +698,83 @@ __global__ __launch_bounds__(kThreads, 1) void exact_kernel(AttnArgs a) {
   float lse = finalize<T, D>(ws);
   if (qrow < 0) return;
   if (a.merge_levels > 0) {
-    for (int lv = 0; lv < a.merge_levels; ++lv) {
-      const int64_t hl = a.n >> (lv + 1);
-      if (((qrow / hl) & 1) == 0) continue;
-      const int64_t slot = (qrow / (2 * hl)) * hl + (qrow % hl);
-      const int64_t idx = (int64_t(lv) * a.heads + head) * a.S + slot;
-      lse = merge_partial<T, D>(ws, lse, static_cast<const T*>(a.part_o) + idx * D,
-                                a.part_lse[idx]);
+    // The base block blk lies in the second half of its level-lv node (and
+    // so has a partial there) iff bit L-1-lv of blk is set; the node's half
+    // size is block << (L-1-lv). All of this is uniform over the work-group.
+    const int L = a.merge_levels;
+    const int64_t r = qrow - b_lo;
+    auto slot_of = [&](int lv) {
+      const int sh = L - 1 - lv;
+      const int64_t hl = a.block << sh;
+      const int64_t slot = int64_t(blk >> (sh + 1)) * hl +
+                           int64_t(blk & ((1u << sh) - 1u)) * a.block + r;
+      return (int64_t(lv) * a.heads + head) * a.S + slot;
+    };
+    auto next_level = [&](int lv) {
+      for (++lv; lv < L; ++lv)
+        if ((blk >> (L - 1 - lv)) & 1u) return lv;
+      return L;
+    };
+    Partial<T, D> cur, nxt;
+    int lv = next_level(-1);
+    if (lv < L) {
+      int64_t idx = slot_of(lv);
+      load_partial<T, D>(cur, static_cast<const T*>(a.part_o) + idx * D, a.part_lse + idx);
+      while (lv < L) {
+        const int nl = next_level(lv);
+        if (nl < L) {
+          idx = slot_of(nl);
+          load_partial<T, D>(nxt, static_cast<const T*>(a.part_o) + idx * D, a.part_lse + idx);
+        }
+        lse = merge_partial<T, D>(ws, lse, cur);
+        cur = nxt;
+        lv = nl;
+      }
     }
   }
   store_row<T, D>(ws, static_cast<T*>(a.O) + hoff + qrow * D);
   if (a.lse && (lane_id() >> 5) == 0) a.lse[int64_t(head) * a.n + qrow] = lse;
 }
 
+template <typename T, int D, bool kCausal>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesPerEu<T, D>::value)))
+void exact_kernel(AttnArgs a) {
+  __shared__ Smem<T, D> sm;
+  run_items(a, sm.item, [&](int64_t item) __attribute__((always_inline)) {
+    exact_item<T, D, kCausal>(a, sm, uint32_t(item));
+  });
+}
+
 // ------------------------------------------------------ BUCKET / ROWSUM kernel
-// The key tiles of a work-group form one sequence: the bucket's own keys,
-// then the uniform sample, then (BUCKET) the V-norm sample, each segment
-// padded to whole tiles. The rows and weights of up to kSlotCap slots (a
-// window of tiles) are staged in LDS up front, so the tile loop issues no
-// dependent index loads.
+// Work item w (ordered by level, head, segment, bucket, query chunk): one
+// query chunk of one sortLSH bucket. Its key tiles form one sequence: the
+// bucket's own keys, then the uniform sample, then (BUCKET) the V-norm
+// sample, each segment padded to whole tiles. The rows and weights of up to
+// kSlotCap slots (a window of tiles) are staged in LDS up front, so the tile
+// loop issues no dependent index loads.
 template <typename T, int D, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void bucket_kernel(AttnArgs a) {
-  __shared__ SmemG<T, D> sm;
+__device__ __forceinline__ void bucket_item(const AttnArgs& a, SmemG<T, D>& sm, int64_t w) {
   constexpr int KT = Buf<T, D>::KT;
   constexpr int kWin = kSlotCap / KT;           // tiles per slot window
   constexpr bool kProduct = MODE == MODE_BUCKET;
-  const int64_t w = xcd_remap(blockIdx.x, gridDim.x);
   int lv = 0;
   for (int l = 1; l < a.table.count; ++l)
     if (w >= a.table.lv[l].att_wg0) lv = l;
   const Level& L = a.table.lv[lv];
-  int64_t rem = w - L.att_wg0;
-  const int64_t qc = rem % L.att_qch;
-  rem /= L.att_qch;
-  const int64_t bucket = rem % L.nbucket;
-  rem /= L.nbucket;
-  const int64_t seg = rem % L.nseg;
-  const int head = int(rem / L.nseg);
+  // 32-bit division: far cheaper than 64-bit, and the counts fit
+  uint32_t rem = uint32_t(w - L.att_wg0);
+  const uint32_t nq = uint32_t(L.att_qch), nbk = uint32_t(L.nbucket), nsg = uint32_t(L.nseg);
+  uint32_t quo = rem / nq;
+  const int64_t qc = rem - quo * nq;
+  rem = quo;
+  quo = rem / nbk;
+  const int64_t bucket = rem - quo * nbk;
+  rem = quo;
+  quo = rem / nsg;
+  const int64_t seg = rem - quo * nsg;
+  const int head = int(quo);
   const int b_eff = L.b_eff;
   const int64_t h = L.h;
-
   const int64_t slot0 = (int64_t(lv) * a.heads + head) * a.S + seg * h + bucket * b_eff;
   const int wave = threadIdx.x >> 6;
   const int ql = lane_id() & 31;
@@ -666,33 +811,51 @@ __global__ __launch_bounds__(kThreads, 1) void bucket_kernel(AttnArgs a) {
     if (t < t_b + t_u) { j0 = (t - t_b) * KT; cnt = ucount; return 1; }
     j0 = (t - t_b - t_u) * KT; cnt = vcount; return 2;
   };
-  // stage slots of tiles [t0, t0 + kWin) in LDS
+  // stage slots of tiles [t0, t0 + kWin) in LDS; all of a thread's index
+  // loads are issued before any of them is used
   auto fill = [&](int t0) {
+    constexpr int NI = kSlotCap / kThreads;
     const int32_t* pk = a.perm_k + slot0;
     const int32_t* ui = a.u_idx + rec * a.m;
     const int32_t* ub = a.u_bkt + rec * a.m;
-    for (int e = threadIdx.x; e < kSlotCap; e += kThreads) {
+    const int32_t* vi = a.v_idx + rec * a.m;
+    const int32_t* vb = a.v_bkt + rec * a.m;
+    const float* vw = a.v_w + rec * a.m;
+    int kind[NI], jj[NI];
+    int32_t row[NI], bk[NI];
+    float wv[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int e = int(threadIdx.x) + i * kThreads;
       const int t = t0 + e / KT;
-      int32_t row = -1;
-      float wt = 0.f;
+      kind[i] = -1;
+      jj[i] = 0;
       if (t < ntiles) {
         int j0, cnt;
         const int sg = seg_of(t, j0, cnt);
         const int j = j0 + e % KT;
         if (j < cnt) {
-          if (sg == 0) {
-            row = pk[j];
-            wt = 1.f;
-          } else if (sg == 1) {
-            row = ui[j];
-            wt = ub[j] != bucket ? alpha : 0.f;
-          } else {
-            row = a.v_idx[rec * a.m + j];
-            wt = a.v_bkt[rec * a.m + j] != bucket ? a.v_w[rec * a.m + j] : 0.f;
-          }
+          kind[i] = sg;
+          jj[i] = j;
         }
       }
-      sm.srow[e] = row;
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      row[i] = -1;
+      bk[i] = int32_t(bucket);
+      wv[i] = 1.f;
+      if (kind[i] >= 0) row[i] = (kind[i] == 0 ? pk : kind[i] == 1 ? ui : vi)[jj[i]];
+      if (kind[i] >= 1) bk[i] = (kind[i] == 1 ? ub : vb)[jj[i]];
+      if (kind[i] == 2) wv[i] = vw[jj[i]];
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int e = int(threadIdx.x) + i * kThreads;
+      float wt = 0.f;
+      if (kind[i] == 0) wt = 1.f;
+      else if (kind[i] >= 1 && bk[i] != bucket) wt = kind[i] == 1 ? alpha : wv[i];
+      sm.srow[e] = row[i];
       sm.sw[e] = wt;
     }
   };
@@ -710,7 +873,9 @@ __global__ __launch_bounds__(kThreads, 1) void bucket_kernel(AttnArgs a) {
   issue(0);
   pipe.commit(sm.buf[0], needs_v(0));
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
+  // one loop per segment, each with its own weighting of the tiles
+  auto step = [&](int t, auto kind) __attribute__((always_inline)) {
+    constexpr int KIND = decltype(kind)::value;
     if (t + 1 < ntiles) {
       if ((t + 1) % kWin == 0) {      // next window of slots
         fill(t + 1);
@@ -719,23 +884,24 @@ __global__ __launch_bounds__(kThreads, 1) void bucket_kernel(AttnArgs a) {
       issue(t + 1);
     }
     int j0, cnt;
-    const int sg = seg_of(t, j0, cnt);
+    seg_of(t, j0, cnt);
     const int nvalid = cnt - j0 < KT ? cnt - j0 : KT;
-    const bool masked = nvalid < KT;
-    const Buf<T, D>& b = sm.buf[t & 1];
-    if (sg == 0) {
-      if (kProduct)
-        compute_tile<T, D, KIND_PLAIN, false>(b, lo, q, ws, a.scale_log2, masked, nvalid, KT);
-      else
-        compute_tile<T, D, KIND_SUM_W, false>(b, lo, q, ws, a.scale_log2, masked, nvalid, KT);
-    } else if (sg == 1) {
-      compute_tile<T, D, KIND_SUM_W, false>(b, lo, q, ws, a.scale_log2, masked, nvalid, KT);
-    } else if (kProduct) {
-      compute_tile<T, D, KIND_PV_W, false>(b, lo, q, ws, a.scale_log2, masked, nvalid, KT);
-    }
+    compute_tile<T, D, KIND, false>(sm.buf[t & 1], lo, q, ws, a.scale_log2, nvalid < KT,
+                                    nvalid, KT);
     if (t + 1 < ntiles) pipe.commit(sm.buf[(t + 1) & 1], needs_v(t + 1));
     __syncthreads();
-  }
+  };
+  using Plain = std::integral_constant<int, KIND_PLAIN>;
+  using SumW = std::integral_constant<int, KIND_SUM_W>;
+  using PvW = std::integral_constant<int, KIND_PV_W>;
+  int t = 0;
+  if (kProduct)
+    for (; t < t_b; ++t) step(t, Plain{});
+  else
+    for (; t < t_b; ++t) step(t, SumW{});
+  for (; t < t_b + t_u; ++t) step(t, SumW{});
+  if (kProduct)
+    for (; t < ntiles; ++t) step(t, PvW{});
   const float lse = finalize<T, D>(ws);
   if (qrow < 0) return;
   const bool first = (lane_id() >> 5) == 0;
@@ -744,7 +910,9 @@ __global__ __launch_bounds__(kThreads, 1) void bucket_kernel(AttnArgs a) {
     return;
   }
   if (a.table.causal) {
-    const int64_t slot = (qrow / (2 * h)) * h + (qrow % h);
+    // the sub-problem's queries are rows [2 seg h + h, 2 seg h + 2h) of the
+    // head; their slot is seg h + (row - 2 seg h - h)
+    const int64_t slot = qrow - (seg + 1) * h;
     const int64_t idx = (int64_t(lv) * a.heads + head) * a.S + slot;
     store_row<T, D>(ws, static_cast<T*>(a.O) + idx * D);
     if (first) a.lse[idx] = lse;
@@ -754,20 +922,69 @@ __global__ __launch_bounds__(kThreads, 1) void bucket_kernel(AttnArgs a) {
   }
 }
 
-template <typename T, int D>
-void launch_exact_t(const AttnArgs& a, dim3 grid, hipStream_t s) {
-  if (a.causal)
-    hipLaunchKernelGGL((exact_kernel<T, D, true>), grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((exact_kernel<T, D, false>), grid, dim3(kThreads), 0, s, a);
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesPerEu<T, D>::value)))
+void bucket_kernel(AttnArgs a) {
+  __shared__ SmemG<T, D> sm;
+  run_items(a, sm.item, [&](int64_t item) __attribute__((always_inline)) {
+    bucket_item<T, D, MODE>(a, sm, item);
+  });
+}
+
+// Work-groups of kernel k that the device holds at once (cached per device).
+template <typename Kern>
+int resident_groups(Kern k) {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  const int r = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+  if (dev >= 0 && dev < 64) cache[dev] = r;
+  return r;
+}
+
+// Grid of a launch: every item when there is no queue (rows of `per_row`
+// items), else the resident work-groups (at most one per item).
+template <typename Kern>
+int launch_grid(Kern k, const AttnArgs& a, unsigned per_row, dim3& grid) {
+  if (!a.queue) {
+    grid = dim3(per_row, a.items / per_row);
+    return HA_OK;
+  }
+  const int r = resident_groups(k);
+  if (r <= 0) return fail(HA_ERR_HIP, "could not query the device's occupancy");
+  grid = dim3(unsigned(r) < a.items ? unsigned(r) : a.items);
+  return HA_OK;
 }
 
 template <typename T, int D>
-void launch_bucket_t(const AttnArgs& a, dim3 grid, bool product, hipStream_t s) {
-  if (product)
-    hipLaunchKernelGGL((bucket_kernel<T, D, MODE_BUCKET>), grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((bucket_kernel<T, D, MODE_ROWSUM>), grid, dim3(kThreads), 0, s, a);
+int launch_exact_t(const AttnArgs& a, hipStream_t s) {
+  auto k = a.causal ? exact_kernel<T, D, true> : exact_kernel<T, D, false>;
+  dim3 grid;
+  if (int rc = launch_grid(k, a, a.items_per_head, grid)) return rc;
+  hipLaunchKernelGGL(k, grid, dim3(kThreads), 0, s, a);
+  return HA_OK;
+}
+
+template <typename T, int D>
+int launch_bucket_t(const AttnArgs& a, bool product, hipStream_t s) {
+  auto k = product ? bucket_kernel<T, D, MODE_BUCKET> : bucket_kernel<T, D, MODE_ROWSUM>;
+  dim3 grid;
+  if (int rc = launch_grid(k, a, a.items, grid)) return rc;
+  hipLaunchKernelGGL(k, grid, dim3(kThreads), 0, s, a);
+  return HA_OK;
+}
+
+// Zeroes a queue's counters (a kernel rather than a memset, so that the
+// sequence may be captured in a graph).
+int reset_queue(uint32_t* ctr, hipStream_t s) {
+  hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, s, ctr);
+  HA_LAUNCH_CHECK("queue_reset");
+  return HA_OK;
 }
 
 }  // namespace
@@ -783,23 +1000,33 @@ int launch_exact(const void* Q, const void* K, const void* V, void* O, float* ls
   a.block = block;
   a.tiles_per_block = ceil_div(block, kAttnQ);
   a.causal = causal;
+  const int64_t items = ceil_div(n, block) * a.tiles_per_block * heads;
+  if (items >= (int64_t(1) << 31))
+    return fail(HA_ERR_SHAPE, "%lld query tiles exceed the launch limit", (long long)items);
+  a.items_per_head = uint32_t(ceil_div(n, block) * a.tiles_per_block);
+  a.items = uint32_t(items);
   if (merge && merge->L > 0) {
+    // the merge epilogue locates partials by shifts of the base-block index
+    if ((block << merge->L) != n)
+      return fail(HA_ERR_SHAPE, "base block %lld times 2^%d differs from n = %lld",
+                  (long long)block, merge->L, (long long)n);
     const char* w = static_cast<const char*>(ws);
     a.merge_levels = merge->L;
     a.part_o = w + merge->off[HA_WS_PART_O];
     a.part_lse = reinterpret_cast<const float*>(w + merge->off[HA_WS_PART_LSE]);
     a.S = merge->S;
+    a.queue = reinterpret_cast<uint32_t*>(const_cast<char*>(w) + merge->off[HA_WS_SCHED]) +
+              kQueues;
+    if (int rc = reset_queue(a.queue, s)) return rc;
   }
-  const int64_t blocks = ceil_div(n, block);
-  dim3 grid(unsigned(blocks * a.tiles_per_block), unsigned(heads));
+  if (items == 0) return HA_OK;
   ProfRange pr(merge ? "exact_base_merge" : "exact_attention", s);
-  if (dtype == HA_BF16) {
-    if (d == 128) launch_exact_t<bf16_t, 128>(a, grid, s);
-    else launch_exact_t<bf16_t, 64>(a, grid, s);
-  } else {
-    if (d == 128) launch_exact_t<float, 128>(a, grid, s);
-    else launch_exact_t<float, 64>(a, grid, s);
-  }
+  int rc;
+  if (dtype == HA_BF16)
+    rc = d == 128 ? launch_exact_t<bf16_t, 128>(a, s) : launch_exact_t<bf16_t, 64>(a, s);
+  else
+    rc = d == 128 ? launch_exact_t<float, 128>(a, s) : launch_exact_t<float, 64>(a, s);
+  if (rc) return rc;
   HA_LAUNCH_CHECK("exact_attention");
   return HA_OK;
 }
@@ -807,6 +1034,9 @@ int launch_exact(const void* Q, const void* K, const void* V, void* O, float* ls
 int launch_bucket_attention(const Plan& p, const void* Q, const void* K, const void* V, void* O,
                             float* lse, void* ws, hipStream_t s) {
   if (p.att_wgs == 0) return HA_OK;
+  if (p.att_wgs >= (int64_t(1) << 31))
+    return fail(HA_ERR_SHAPE, "%lld bucket work items exceed the launch limit",
+                (long long)p.att_wgs);
   char* w = static_cast<char*>(ws);
   AttnArgs a{};
   a.Q = Q; a.K = K; a.V = V;
@@ -834,15 +1064,18 @@ int launch_bucket_attention(const Plan& p, const void* Q, const void* K, const v
     a.O = O;
     a.lse = lse;
   }
-  dim3 grid(unsigned(p.att_wgs));
+  a.items = uint32_t(p.att_wgs);
+  a.queue = reinterpret_cast<uint32_t*>(w + p.off[HA_WS_SCHED]);
+  if (int rc = reset_queue(a.queue, s)) return rc;
   ProfRange pr(p.product ? "bucket_attention" : "bucket_rowsum", s);
-  if (p.dtype == HA_BF16) {
-    if (p.d == 128) launch_bucket_t<bf16_t, 128>(a, grid, p.product, s);
-    else launch_bucket_t<bf16_t, 64>(a, grid, p.product, s);
-  } else {
-    if (p.d == 128) launch_bucket_t<float, 128>(a, grid, p.product, s);
-    else launch_bucket_t<float, 64>(a, grid, p.product, s);
-  }
+  int rc;
+  if (p.dtype == HA_BF16)
+    rc = p.d == 128 ? launch_bucket_t<bf16_t, 128>(a, p.product, s)
+                    : launch_bucket_t<bf16_t, 64>(a, p.product, s);
+  else
+    rc = p.d == 128 ? launch_bucket_t<float, 128>(a, p.product, s)
+                    : launch_bucket_t<float, 64>(a, p.product, s);
+  if (rc) return rc;
   HA_LAUNCH_CHECK("bucket_attention");
   return HA_OK;
 }

@@ -89,6 +89,7 @@ struct Plan {
 
 constexpr int kVnormBlock = 256;     // rows per V-norm work-group
 constexpr int kAttnQ = 256;          // query rows per attention work-group
+constexpr int kQueues = 8;           // work queues of the persistent attention kernels (one per XCD)
 
 int make_plan(Plan& p, int64_t n, int d, int heads, int causal, int b, int m,
               int base, int r, int dtype, bool product);

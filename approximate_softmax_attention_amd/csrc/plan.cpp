@@ -121,6 +121,7 @@ int make_plan(Plan& p, int64_t n, int d, int heads, int causal, int b, int m,
     add_region(p, HA_WS_PART_O, slots * d * p.esize);
     add_region(p, HA_WS_PART_LSE, slots * 4);
   }
+  add_region(p, HA_WS_SCHED, 2 * kQueues * 4);
   return HA_OK;
 }
 

@@ -176,6 +176,8 @@ int sortlsh_hyperplanes(uint64_t seed, int heads, int r, int d, float* G_host);
  *   HA_WS_V_W                     float [heads][nodes][m] V-norm sample weights
  *   HA_WS_NODE_META               int32 [heads][nodes][4]: uniform count,
  *                                 V-norm count, alpha (float bits), b_eff
+ *   HA_WS_SCHED                   uint32 [2][8] work-queue counters of the
+ *                                 attention kernels (scratch, reset by each call)
  * The hyperplanes themselves are not in the workspace: the library keeps
  * them per device, keyed by (seed, heads, r, d); sortlsh_hyperplanes returns
  * the same values on the host.
@@ -188,6 +190,7 @@ enum ha_ws_region {
   HA_WS_U_IDX, HA_WS_U_BKT, HA_WS_V_IDX, HA_WS_V_BKT, HA_WS_V_W,
   HA_WS_NODE_META,
   HA_WS_PART_O, HA_WS_PART_LSE,
+  HA_WS_SCHED,
   HA_WS_COUNT
 };
 int hyperattn_workspace_layout(int64_t n, int d, int heads, int causal, int b,
