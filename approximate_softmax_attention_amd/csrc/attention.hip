@@ -107,6 +107,7 @@ struct alignas(16) Buf<float, D> {
 template <typename T, int D>
 struct Smem {
   Buf<T, D> buf[2];
+  float slse[kAttnQ];      // epilogue: lse of each staged row
   int64_t item;            // next work item (persistent launches)
 };
 
@@ -115,6 +116,8 @@ struct SmemG {
   Buf<T, D> buf[2];
   alignas(16) int32_t srow[kSlotCap];
   alignas(16) float sw[kSlotCap];
+  float slse[kAttnQ];      // epilogue: lse of each staged row
+  int64_t sdst[kAttnQ];    // epilogue: destination row of each staged row (-1: none)
   int64_t item;            // next work item (persistent launches)
 };
 
@@ -307,8 +310,12 @@ struct LaneOffs<bf16_t, D> {
   using B = Buf<bf16_t, D>;
   uint32_t k[D / 16];
   uint32_t v[2][D / 32];
+  // Derived from a copy of the lane id that the compiler cannot see through,
+  // so that the offsets are formed per work item rather than held in
+  // registers across a persistent kernel's item loop.
   __device__ __forceinline__ void init() {
-    const int lane = lane_id();
+    int lane = lane_id();
+    asm volatile("" : "+v"(lane));
     const int ql = lane & 31, g = lane >> 5, i16 = lane & 15;
 #pragma unroll
     for (int st = 0; st < D / 16; ++st)
@@ -484,9 +491,38 @@ __device__ __forceinline__ float finalize(WaveState<T, D>& ws) {
   return (ws.m + __log2f(l)) * 0.69314718055994531f;
 }
 
-// d index of accumulator (db, i) for lane group g: 32db + 8(i/4) + 4g + i%4
+// ------------------------------------------------------- epilogue staging
+// After the tile loop the tile buffers are free; the epilogue stages the
+// work-group's output rows there (in T, row-major, 16-byte chunks
+// XOR-swizzled by row) and then reads and writes global memory a row at a
+// time: 16 contiguous bytes per lane, four rows per instruction, instead of
+// the MFMA layout's 8 or 16 bytes from each of 32 rows.
 template <typename T, int D>
-__device__ __forceinline__ void store_row(const WaveState<T, D>& ws, T* __restrict__ out) {
+struct Stage {
+  static constexpr int E = 16 / int(sizeof(T));          // elements per chunk
+  static constexpr int CPR = D / E;                      // chunks per row
+  static constexpr int RB = D * int(sizeof(T));          // bytes per row
+  static constexpr int NCH = kAttnQ * CPR / kThreads;    // chunks per thread
+  static_assert(kAttnQ * RB <= int(sizeof(Buf<T, D>)) * 2, "stage fits the tile buffers");
+  static_assert(kAttnQ * CPR % kThreads == 0, "whole chunks per thread");
+  __device__ static int off(int row, int ch) { return row * RB + ((ch ^ (row & (CPR - 1))) << 4); }
+};
+
+// threadIdx.x through a copy the compiler cannot see through: the epilogue's
+// per-thread offsets are then formed where they are used instead of being
+// hoisted out of a persistent kernel's item loop, where they would hold
+// registers across the tile loop.
+__device__ __forceinline__ int opaque_tid() {
+  int t = int(threadIdx.x);
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// This lane's part of its output row (accumulator layout: d = 32db + 8q4 +
+// 4g + j) into staged row `row`.
+template <typename T, int D>
+__device__ __forceinline__ void stage_row(const WaveState<T, D>& ws, char* st, int row) {
+  using S = Stage<T, D>;
   const int g = lane_id() >> 5;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -494,70 +530,46 @@ __device__ __forceinline__ void store_row(const WaveState<T, D>& ws, T* __restri
     for (int q4 = 0; q4 < 4; ++q4) {
       const int d0 = 32 * db + 8 * q4 + 4 * g;
       if constexpr (sizeof(T) == 2) {
-        const uint32_t a = uint32_t(f32_to_bf16(ws.o[db][4 * q4])) |
-                           (uint32_t(f32_to_bf16(ws.o[db][4 * q4 + 1])) << 16);
-        const uint32_t b = uint32_t(f32_to_bf16(ws.o[db][4 * q4 + 2])) |
-                           (uint32_t(f32_to_bf16(ws.o[db][4 * q4 + 3])) << 16);
-        *reinterpret_cast<uint2*>(out + d0) = make_uint2(a, b);
+        const uint32_t lo = uint32_t(f32_to_bf16(ws.o[db][4 * q4])) |
+                            (uint32_t(f32_to_bf16(ws.o[db][4 * q4 + 1])) << 16);
+        const uint32_t hi = uint32_t(f32_to_bf16(ws.o[db][4 * q4 + 2])) |
+                            (uint32_t(f32_to_bf16(ws.o[db][4 * q4 + 3])) << 16);
+        *reinterpret_cast<uint2*>(st + S::off(row, d0 >> 3) + (d0 & 7) * 2) = make_uint2(lo, hi);
       } else {
-        *reinterpret_cast<float4*>(out + d0) =
+        *reinterpret_cast<float4*>(st + S::off(row, d0 >> 2)) =
             make_float4(ws.o[db][4 * q4], ws.o[db][4 * q4 + 1], ws.o[db][4 * q4 + 2],
                         ws.o[db][4 * q4 + 3]);
       }
     }
 }
 
-// A normalised partial result of this lane's query: its half of the output
-// row (the lane's d positions, as store_row writes them) and its lse.
-template <typename T, int D> struct Partial;
-template <int D> struct Partial<bf16_t, D> { uint2 raw[D / 8]; float lse; };
-template <int D> struct Partial<float, D> { float4 raw[D / 8]; float lse; };
-
-template <typename T, int D>
-__device__ __forceinline__ void load_partial(Partial<T, D>& pt, const T* __restrict__ po,
-                                             const float* plse) {
-  const int g = lane_id() >> 5;
+// 16 raw bytes <-> E values of T as floats
+template <typename T>
+__device__ __forceinline__ void unpack16(uint4 raw, float* v) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d0 = 32 * db + 8 * q4 + 4 * g;
-      if constexpr (sizeof(T) == 2)
-        pt.raw[4 * db + q4] = *reinterpret_cast<const uint2*>(po + d0);
-      else
-        pt.raw[4 * db + q4] = *reinterpret_cast<const float4*>(po + d0);
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
-  pt.lse = *plse;
+  } else {
+    v[0] = __uint_as_float(raw.x); v[1] = __uint_as_float(raw.y);
+    v[2] = __uint_as_float(raw.z); v[3] = __uint_as_float(raw.w);
+  }
 }
-
-// Merge a partial into (ws.o, lse) by log-sum-exp weights; returns the new lse.
-template <typename T, int D>
-__device__ __forceinline__ float merge_partial(WaveState<T, D>& ws, float lse,
-                                               const Partial<T, D>& pt) {
-  const float mx = fmaxf(lse, pt.lse);
-  const float wa = __expf(lse - mx);
-  const float wb = __expf(pt.lse - mx);
-  const float inv = 1.f / (wa + wb);
+template <typename T>
+__device__ __forceinline__ uint4 pack16(const float* v) {
+  if constexpr (sizeof(T) == 2) {
+    uint32_t w[4];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      float v[4];
-      if constexpr (sizeof(T) == 2) {
-        const uint2 raw = pt.raw[4 * db + q4];
-        v[0] = __uint_as_float(raw.x << 16);
-        v[1] = __uint_as_float(raw.x & 0xFFFF0000u);
-        v[2] = __uint_as_float(raw.y << 16);
-        v[3] = __uint_as_float(raw.y & 0xFFFF0000u);
-      } else {
-        const float4 raw = pt.raw[4 * db + q4];
-        v[0] = raw.x; v[1] = raw.y; v[2] = raw.z; v[3] = raw.w;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        ws.o[db][4 * q4 + j] = (ws.o[db][4 * q4 + j] * wa + v[j] * wb) * inv;
-    }
-  return mx + __logf(wa + wb);
+    for (int i = 0; i < 4; ++i)
+      w[i] = uint32_t(f32_to_bf16(v[2 * i])) | (uint32_t(f32_to_bf16(v[2 * i + 1])) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                      __float_as_uint(v[3]));
+  }
 }
 
 // Waves per SIMD to aim for: with bf16 and d = 64 two work-groups fit a
@@ -695,45 +707,76 @@ __device__ __forceinline__ void exact_item(const AttnArgs& a, Smem<T, D>& sm, ui
     if (t + 1 < ntiles) pipe.commit(sm.buf[(t + 1) & 1], true);
     __syncthreads();
   }
-  float lse = finalize<T, D>(ws);
-  if (qrow < 0) return;
+  const float lse = finalize<T, D>(ws);
+  // stage the rows, then merge and store them a row at a time
+  using S = Stage<T, D>;
+  char* st = reinterpret_cast<char*>(&sm.buf[0]);
+  stage_row<T, D>(ws, st, wave * kQW + ql);
+  if ((lane_id() >> 5) == 0) sm.slse[wave * kQW + ql] = lse;
+  __syncthreads();
+  const int nrows = int(q_end - q0);
+  const int tid = opaque_tid();
+  float acc[S::NCH][S::E], l[S::NCH];
+#pragma unroll
+  for (int k = 0; k < S::NCH; ++k) {
+    const int c = tid + k * kThreads;
+    const int row = c / S::CPR, ch = c % S::CPR;
+    unpack16<T>(*reinterpret_cast<const uint4*>(st + S::off(row, ch)), acc[k]);
+    l[k] = sm.slse[row];
+  }
   if (a.merge_levels > 0) {
     // The base block blk lies in the second half of its level-lv node (and
     // so has a partial there) iff bit L-1-lv of blk is set; the node's half
-    // size is block << (L-1-lv). All of this is uniform over the work-group.
+    // size is block << (L-1-lv). The partial of row b_lo + r sits at slot
+    // (blk >> (L-lv)) * hl + (blk mod 2^(L-1-lv)) * block + r, so a tile's
+    // partials are contiguous.
     const int L = a.merge_levels;
-    const int64_t r = qrow - b_lo;
-    auto slot_of = [&](int lv) {
+    for (int lv = 0; lv < L; ++lv) {
       const int sh = L - 1 - lv;
+      if (((blk >> sh) & 1u) == 0) continue;
       const int64_t hl = a.block << sh;
-      const int64_t slot = int64_t(blk >> (sh + 1)) * hl +
-                           int64_t(blk & ((1u << sh) - 1u)) * a.block + r;
-      return (int64_t(lv) * a.heads + head) * a.S + slot;
-    };
-    auto next_level = [&](int lv) {
-      for (++lv; lv < L; ++lv)
-        if ((blk >> (L - 1 - lv)) & 1u) return lv;
-      return L;
-    };
-    Partial<T, D> cur, nxt;
-    int lv = next_level(-1);
-    if (lv < L) {
-      int64_t idx = slot_of(lv);
-      load_partial<T, D>(cur, static_cast<const T*>(a.part_o) + idx * D, a.part_lse + idx);
-      while (lv < L) {
-        const int nl = next_level(lv);
-        if (nl < L) {
-          idx = slot_of(nl);
-          load_partial<T, D>(nxt, static_cast<const T*>(a.part_o) + idx * D, a.part_lse + idx);
+      const int64_t slot0 = int64_t(blk >> (sh + 1)) * hl +
+                            int64_t(blk & ((1u << sh) - 1u)) * a.block + (q0 - b_lo);
+      const int64_t idx0 = (int64_t(lv) * a.heads + head) * a.S + slot0;
+      const T* po = static_cast<const T*>(a.part_o) + idx0 * D;
+      const float* pls = a.part_lse + idx0;
+      uint4 raw[S::NCH];
+      float pl[S::NCH];
+#pragma unroll
+      for (int k = 0; k < S::NCH; ++k) {
+        const int c = tid + k * kThreads;
+        const int row = c / S::CPR, ch = c % S::CPR;
+        raw[k] = make_uint4(0, 0, 0, 0);
+        pl[k] = -INFINITY;
+        if (row < nrows) {
+          raw[k] = *reinterpret_cast<const uint4*>(po + int64_t(row) * D + ch * S::E);
+          pl[k] = pls[row];
         }
-        lse = merge_partial<T, D>(ws, lse, cur);
-        cur = nxt;
-        lv = nl;
+      }
+#pragma unroll
+      for (int k = 0; k < S::NCH; ++k) {
+        float v[S::E];
+        unpack16<T>(raw[k], v);
+        const float mx = fmaxf(l[k], pl[k]);
+        const float wa = __expf(l[k] - mx);
+        const float wb = __expf(pl[k] - mx);
+        const float inv = 1.f / (wa + wb);
+#pragma unroll
+        for (int j = 0; j < S::E; ++j) acc[k][j] = (acc[k][j] * wa + v[j] * wb) * inv;
+        l[k] = mx + __logf(wa + wb);
       }
     }
   }
-  store_row<T, D>(ws, static_cast<T*>(a.O) + hoff + qrow * D);
-  if (a.lse && (lane_id() >> 5) == 0) a.lse[int64_t(head) * a.n + qrow] = lse;
+#pragma unroll
+  for (int k = 0; k < S::NCH; ++k) {
+    const int c = tid + k * kThreads;
+    const int row = c / S::CPR, ch = c % S::CPR;
+    if (row >= nrows) continue;
+    const int64_t grow = q0 + row;
+    *reinterpret_cast<uint4*>(static_cast<T*>(a.O) + hoff + grow * D + ch * S::E) =
+        pack16<T>(acc[k]);
+    if (ch == 0 && a.lse) a.lse[int64_t(head) * a.n + grow] = l[k];
+  }
 }
 
 template <typename T, int D, bool kCausal>
@@ -903,22 +946,36 @@ __device__ __forceinline__ void bucket_item(const AttnArgs& a, SmemG<T, D>& sm, 
   if (kProduct)
     for (; t < ntiles; ++t) step(t, PvW{});
   const float lse = finalize<T, D>(ws);
-  if (qrow < 0) return;
-  const bool first = (lane_id() >> 5) == 0;
-  if (MODE == MODE_ROWSUM) {
-    if (first) a.lse[int64_t(head) * a.n + qrow] = lse;
-    return;
+  // stage the rows with their destinations, then store them a row at a time
+  using S = Stage<T, D>;
+  char* st = reinterpret_cast<char*>(&sm.buf[0]);
+  const int srow = wave * kQW + ql;
+  if (MODE != MODE_ROWSUM) stage_row<T, D>(ws, st, srow);
+  if ((lane_id() >> 5) == 0) {
+    int64_t dst = -1;
+    if (qrow >= 0) {
+      if (MODE != MODE_ROWSUM && a.table.causal)
+        // the sub-problem's queries are rows [2 seg h + h, 2 seg h + 2h) of
+        // the head; their slot is seg h + (row - 2 seg h - h)
+        dst = (int64_t(lv) * a.heads + head) * a.S + (qrow - (seg + 1) * h);
+      else
+        dst = int64_t(head) * a.n + qrow;
+    }
+    sm.slse[srow] = lse;
+    sm.sdst[srow] = dst;
   }
-  if (a.table.causal) {
-    // the sub-problem's queries are rows [2 seg h + h, 2 seg h + 2h) of the
-    // head; their slot is seg h + (row - 2 seg h - h)
-    const int64_t slot = qrow - (seg + 1) * h;
-    const int64_t idx = (int64_t(lv) * a.heads + head) * a.S + slot;
-    store_row<T, D>(ws, static_cast<T*>(a.O) + idx * D);
-    if (first) a.lse[idx] = lse;
-  } else {
-    store_row<T, D>(ws, static_cast<T*>(a.O) + hoff + qrow * D);
-    if (first && a.lse) a.lse[int64_t(head) * a.n + qrow] = lse;
+  __syncthreads();
+  const int tid = opaque_tid();
+#pragma unroll
+  for (int k = 0; k < S::NCH; ++k) {
+    const int c = tid + k * kThreads;
+    const int row = c / S::CPR, ch = c % S::CPR;
+    const int64_t dst = sm.sdst[row];
+    if (dst < 0) continue;
+    if (MODE != MODE_ROWSUM)
+      *reinterpret_cast<uint4*>(static_cast<T*>(a.O) + dst * D + ch * S::E) =
+          *reinterpret_cast<const uint4*>(st + S::off(row, ch));
+    if (ch == 0 && a.lse) a.lse[dst] = sm.slse[row];
   }
 }
 
