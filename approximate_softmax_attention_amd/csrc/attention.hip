@@ -62,6 +62,10 @@ constexpr int kWaves = 8;
 constexpr int kQW = 32;   // queries per wave; kAttnQ = kWaves * kQW
 static_assert(kAttnQ == kWaves * kQW, "query tile");
 constexpr float kTau = 8.f;   // lazy-rescale threshold (log2 units)
+// Wave priority while issuing an MFMA chain: the SIMD's arbiter then keeps
+// the matrix unit fed from that wave while the other wave's softmax work
+// fills the VALU.
+constexpr int kMfmaPrio = 1;
 constexpr int kSlotCap = 1024;   // key slots staged in LDS per window (gathered modes)
 
 enum { MODE_EXACT = 0, MODE_BUCKET = 1, MODE_ROWSUM = 2 };
@@ -358,11 +362,13 @@ __device__ __forceinline__ f32x16 scores(const Buf<T, D>& b, const LaneOffs<T, D
   f32x16 acc = zero16();
   if constexpr (sizeof(T) == 2) {
     const char* base = reinterpret_cast<const char*>(b.k) + kb * 32 * D * 2;
+    __builtin_amdgcn_s_setprio(kMfmaPrio);
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
       const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(base + lo.k[st]);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q.v[st], acc, 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
   } else {
     const int lane = lane_id();
     const float* krow = &b.k[(32 * kb + (lane & 31)) * Buf<T, D>::KS];
@@ -383,6 +389,7 @@ template <typename T, int D>
 __device__ __forceinline__ void accumulate_pv(const Buf<T, D>& b, const LaneOffs<T, D>& lo,
                                               WaveState<T, D>& ws, const f32x16& p, int kb) {
   if constexpr (sizeof(T) == 2) {
+    __builtin_amdgcn_s_setprio(kMfmaPrio);
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       bf16x8_t pb;
@@ -400,6 +407,7 @@ __device__ __forceinline__ void accumulate_pv(const Buf<T, D>& b, const LaneOffs
         ws.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, ws.o[db], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   } else {
     const int lane = lane_id();
     const int ql = lane & 31, g = lane >> 5;
