@@ -47,17 +47,24 @@ __device__ __forceinline__ int find_level(const LevelTable& t, int64_t w, int wh
   return lv;
 }
 
+// Work-group counts fit in 32 bits, and 32-bit division is far cheaper than
+// 64-bit.
 __device__ __forceinline__ ChunkRef decode_chunk(const SortArgs& a, int64_t w) {
   ChunkRef c;
   c.lv = find_level(a.table, w, 0);
   const Level& L = a.table.lv[c.lv];
-  int64_t rem = w - L.sort_wg0;
-  c.chunk = rem % L.sort_cps;
-  rem /= L.sort_cps;
-  c.seg = rem % L.nseg;
-  rem /= L.nseg;
-  c.side = int(rem % a.sides);
-  c.head = int(rem / a.sides);
+  uint32_t rem = uint32_t(w - L.sort_wg0);
+  const uint32_t cps = uint32_t(L.sort_cps), nseg = uint32_t(L.nseg);
+  const uint32_t sides = uint32_t(a.sides);
+  uint32_t q = rem / cps;
+  c.chunk = rem - q * cps;
+  rem = q;
+  q = rem / nseg;
+  c.seg = rem - q * nseg;
+  rem = q;
+  q = rem / sides;
+  c.side = int(rem - q * sides);
+  c.head = int(q);
   c.h = L.h;
   return c;
 }
@@ -70,17 +77,28 @@ __device__ __forceinline__ int64_t seg_row(const SortArgs& a, int side, int64_t 
   return 2 * seg * h + (side == 0 ? h : 0) + t;
 }
 
+constexpr int kPer = kSortChunk / kThreads;      // elements per thread and chunk
+
 __global__ __launch_bounds__(kThreads) void sort_hist_kernel(SortArgs a) {
   __shared__ uint32_t hist[kSortBins];
   const int64_t w = blockIdx.x;
   const ChunkRef c = decode_chunk(a, w);
   hist[threadIdx.x] = 0;
-  __syncthreads();
-  const uint8_t* codes = a.codes[c.side] + int64_t(c.head) * a.n;
+  const uint8_t* codes = a.codes[c.side] + int64_t(c.head) * a.n +
+                         seg_row(a, c.side, c.seg, c.h, 0);
   const int64_t t0 = c.chunk * kSortChunk;
   const int64_t t1 = t0 + kSortChunk < c.h ? t0 + kSortChunk : c.h;
-  for (int64_t t = t0 + threadIdx.x; t < t1; t += kThreads)
-    atomicAdd(&hist[codes[seg_row(a, c.side, c.seg, c.h, t)]], 1u);
+  // all of this thread's codes are loaded before any is counted
+  uint32_t v[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int64_t t = t0 + i * kThreads + threadIdx.x;
+    v[i] = t < t1 ? codes[t] : kSortBins;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (v[i] < kSortBins) atomicAdd(&hist[v[i]], 1u);
   __syncthreads();
   a.hist[w * kSortBins + threadIdx.x] = hist[threadIdx.x];
 }
@@ -90,28 +108,36 @@ __global__ __launch_bounds__(kThreads) void sort_offsets_kernel(SortArgs a) {
   const int64_t w = blockIdx.x;
   const int lv = find_level(a.table, w, 1);
   const Level& L = a.table.lv[lv];
-  int64_t rem = w - L.seg_wg0;
-  const int64_t seg = rem % L.nseg;
-  rem /= L.nseg;
-  const int side = int(rem % a.sides);
-  const int head = int(rem / a.sides);
+  uint32_t rem = uint32_t(w - L.seg_wg0);
+  const uint32_t nseg = uint32_t(L.nseg), sides = uint32_t(a.sides);
+  uint32_t q = rem / nseg;
+  const int64_t seg = rem - q * nseg;
+  rem = q;
+  q = rem / sides;
+  const int side = int(rem - q * sides);
+  const int head = int(q);
   const int64_t cw0 = L.sort_wg0 + ((int64_t(head) * a.sides + side) * L.nseg + seg) * L.sort_cps;
   const int bin = threadIdx.x;
-  uint32_t running = 0;
-  for (int64_t c = 0; c < L.sort_cps; ++c) {
-    const uint32_t v = a.hist[(cw0 + c) * kSortBins + bin];
-    a.offs[(cw0 + c) * kSortBins + bin] = running;
-    running += v;
-  }
+  const int cps = int(L.sort_cps);
+  const uint32_t* __restrict__ hist = a.hist + cw0 * kSortBins + bin;
+  uint32_t* __restrict__ offs = a.offs + cw0 * kSortBins + bin;
+  // this bin's total over the segment's chunks
+  uint32_t total = 0;
+  for (int c = 0; c < cps; ++c) total += hist[c * kSortBins];
   // exclusive scan of the per-bin totals across the block
-  uint64_t incl = wave_incl_scan(uint64_t(running));
+  uint64_t incl = wave_incl_scan(uint64_t(total));
   const int wave = threadIdx.x >> 6;
   if (lane_id() == 63) wtot[wave] = uint32_t(incl);
   __syncthreads();
   uint32_t before = 0;
   for (int i = 0; i < wave; ++i) before += wtot[i];
-  const uint32_t base = before + uint32_t(incl) - running;
-  for (int64_t c = 0; c < L.sort_cps; ++c) a.offs[(cw0 + c) * kSortBins + bin] += base;
+  uint32_t running = before + uint32_t(incl) - total;
+  // bin-major, then chunk-minor offsets
+  for (int c = 0; c < cps; ++c) {
+    const uint32_t v = hist[c * kSortBins];
+    offs[c * kSortBins] = running;
+    running += v;
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void sort_scatter_kernel(SortArgs a) {
@@ -133,11 +159,21 @@ __global__ __launch_bounds__(kThreads) void sort_scatter_kernel(SortArgs a) {
   const int64_t t0 = c.chunk * kSortChunk;
   const int64_t t1 = t0 + kSortChunk < c.h ? t0 + kSortChunk : c.h;
   const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
-  for (int64_t base = t0; base < t1; base += kThreads) {
+  // all of this thread's codes are loaded before the batch loop
+  uint32_t cv[kPer];
+#pragma unroll
+  for (int b = 0; b < kPer; ++b) {
+    const int64_t t = t0 + b * kThreads + tid;
+    cv[b] = t < t1 ? codes[seg_row(a, c.side, c.seg, c.h, t)] : 0u;
+  }
+#pragma unroll
+  for (int b = 0; b < kPer; ++b) {
+    const int64_t base = t0 + b * kThreads;
+    if (base >= t1) break;
     const int64_t t = base + tid;
     const bool valid = t < t1;
     const int64_t row = seg_row(a, c.side, c.seg, c.h, t);
-    const uint32_t code = valid ? codes[row] : 0u;
+    const uint32_t code = cv[b];
     uint64_t eq = __ballot(valid);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
