@@ -32,6 +32,39 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def kernel_source_hash():
+    """sha256 over the library's kernel sources (file names and contents)."""
+    import hashlib
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "approximate_softmax_attention_amd", "csrc")
+    for name in sorted(os.listdir(src)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(src, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` (read + written, scaled by the plain
+    copy calibration) from the committed rocprofv3 counter summary, or None
+    when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"hyperattn_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    sha, val = None, None
+    with open(path) as f:
+        for line in f:
+            line = line.strip().strip("`")
+            if line.startswith("source-sha256:"):
+                sha = line.split(":", 1)[1].strip()
+            elif line.startswith(f"bytes-per-launch {kernel}:"):
+                val = int(line.split(":", 1)[1])
+    if sha is None or sha != kernel_source_hash():
+        return None
+    return val
+
+
 def algorithmic_flops(w):
     """MFMA flops the method must do, per kernel (per launch)."""
     H, n, d, b, m = w.heads, w.n, w.d, w.b, w.m
@@ -103,6 +136,48 @@ def cpu_baseline(w):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def sweep(args, torch, api):
+    """HA page, "Single self-attention layer": one layer's forward time against
+    n, causal and non-causal, with exact attention beside it. Inputs are
+    seeded iid N(0, 1) bf16 tensors of the page's shape (d = 64, 12 heads)."""
+    H, d = args.sweep_heads, args.sweep_d
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20231009)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for causal in (False, True):
+        n = 4096
+        while n <= 131072:
+            q, k, v = (torch.randn(H, n, d, device="cuda", dtype=torch.bfloat16, generator=g)
+                       for _ in range(3))
+            kw = dict(causal=causal, b=256, m=256, r=8, recursion_base=4096, seed=7)
+            ws = api.alloc_workspace(api.workspace_bytes(n, d, H, **{x: kw[x] for x in (
+                "causal", "b", "m", "r", "recursion_base")}), "cuda")
+            o = torch.empty_like(q)
+            oe = torch.empty_like(q)
+            reps = max(2, min(20, (1 << 22) // n))
+            t_h = timed(lambda: api.forward(q, k, v, workspace=ws, out=o, **kw), reps)
+            t_e = timed(lambda: api.exact(q, k, v, causal=causal, out=oe), max(2, reps // 4))
+            print(json.dumps({"sweep": "single-layer forward", "heads": H, "head_dim": d,
+                              "seq_len": n, "causal": causal, "dtype": "bf16",
+                              "hyperattention_ms": t_h, "exact_ms": t_e,
+                              "speedup": t_e / t_h}), flush=True)
+            del q, k, v, ws, o, oe
+            torch.cuda.empty_cache()
+            n *= 2
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +186,12 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-exact", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="the single-layer sweep of the HA page's experiment: forward time "
+                         "of HyperAttention and of exact attention for n = 4096 .. 131072, "
+                         "causal and not; one JSON line per point")
+    ap.add_argument("--sweep-heads", type=int, default=12)
+    ap.add_argument("--sweep-d", type=int, default=64)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (torch elementwise kernel) "
                          "so that HBM byte counters can be scaled against known traffic")
@@ -125,6 +206,10 @@ def main():
 
     from approximate_softmax_attention_amd import api, workloads as wl
     from approximate_softmax_attention_amd._lib import HA_BF16, HA_F32
+
+    if args.sweep:
+        sweep(args, torch, api)
+        return
 
     w = wl.WORKLOADS[args.workload or wl.HEADLINE]
     log(f"workload {w.name}: generating inputs")
@@ -172,7 +257,8 @@ def main():
     if dom in flops:
         ach = flops[dom] / (kernels[dom]["avg_ms"] / 1e3)
         roofline = {"bound": "mfma", "achieved": ach / 1e12, "peak": peak / 1e12,
-                    "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
+                    "unit": "TFLOP/s", "frac": ach / peak,
+                    "traffic": profiled_traffic(w.name, dom),
                     "kernel": dom, "flops_per_launch": flops[dom]}
     else:
         roofline = {"bound": "hbm", "achieved": None, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
