@@ -362,11 +362,28 @@ __device__ __forceinline__ f32x16 scores(const Buf<T, D>& b, const LaneOffs<T, D
   f32x16 acc = zero16();
   if constexpr (sizeof(T) == 2) {
     const char* base = reinterpret_cast<const char*>(b.k) + kb * 32 * D * 2;
-    __builtin_amdgcn_s_setprio(kMfmaPrio);
+    // every fragment read is issued before the chain starts (the empty asm
+    // keeps the compiler from sinking them between the MFMAs), so the chain
+    // waits on LDS latency once instead of once per step
+    // (d = 128 only: the d = 64 kernels run four waves per SIMD and have no
+    // registers to spare, so they read each fragment just ahead of its MFMA)
+    if constexpr (D == 128) {
+      bf16x8_t kf[D / 16];
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(base + lo.k[st]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q.v[st], acc, 0, 0, 0);
+      for (int st = 0; st < D / 16; ++st)
+        kf[st] = *reinterpret_cast<const bf16x8_t*>(base + lo.k[st]);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_setprio(kMfmaPrio);
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], q.v[st], acc, 0, 0, 0);
+    } else {
+      __builtin_amdgcn_s_setprio(kMfmaPrio);
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(base + lo.k[st]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q.v[st], acc, 0, 0, 0);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
   } else {
@@ -389,22 +406,52 @@ template <typename T, int D>
 __device__ __forceinline__ void accumulate_pv(const Buf<T, D>& b, const LaneOffs<T, D>& lo,
                                               WaveState<T, D>& ws, const f32x16& p, int kb) {
   if constexpr (sizeof(T) == 2) {
-    __builtin_amdgcn_s_setprio(kMfmaPrio);
+    if constexpr (D == 128) {
+      // all transposing reads of the block first, as for the score chain
+      v4i16_t vx[2][D / 32][2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      bf16x8_t pb;
+      for (int st = 0; st < 2; ++st) {
+        const char* base = reinterpret_cast<const char*>(b.v) + (32 * kb + 16 * st) * D * 2;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[8 * st + j];
-      const char* base = reinterpret_cast<const char*>(b.v) + (32 * kb + 16 * st) * D * 2;
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const v4i16_t x0 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + lo.v[0][db]));
-        const v4i16_t x1 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + lo.v[1][db]));
-        const bf16x8_t a = __builtin_bit_cast(
-            bf16x8_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-        ws.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, ws.o[db], 0, 0, 0);
+          for (int h = 0; h < 2; ++h)
+            vx[st][db][h] =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + lo.v[h][db]));
+      }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_setprio(kMfmaPrio);
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        bf16x8_t pb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[8 * st + j];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const bf16x8_t a = __builtin_bit_cast(
+              bf16x8_t,
+              __builtin_shufflevector(vx[st][db][0], vx[st][db][1], 0, 1, 2, 3, 4, 5, 6, 7));
+          ws.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, ws.o[db], 0, 0, 0);
+        }
+      }
+    } else {
+      __builtin_amdgcn_s_setprio(kMfmaPrio);
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        bf16x8_t pb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[8 * st + j];
+        const char* base = reinterpret_cast<const char*>(b.v) + (32 * kb + 16 * st) * D * 2;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const v4i16_t x0 =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + lo.v[0][db]));
+          const v4i16_t x1 =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + lo.v[1][db]));
+          const bf16x8_t a = __builtin_bit_cast(
+              bf16x8_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+          ws.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, ws.o[db], 0, 0, 0);
+        }
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -834,10 +881,12 @@ __device__ __forceinline__ void bucket_item(const AttnArgs& a, SmemG<T, D>& sm, 
 
   const int64_t node = (int64_t(1) << lv) + seg;
   const int64_t rec = int64_t(head) * a.nodes + (node - 1);
-  const int32_t* meta = a.meta + rec * 4;
-  const int ucount = meta[0];
-  const int vcount = kProduct ? meta[1] : 0;
-  const float alpha = __int_as_float(meta[2]);
+  // List lengths and the uniform weight are fixed per level, so the slot
+  // loads below need not wait for the node record; only an empty V-norm list
+  // (all of the node's V rows zero) is read from it, after they are issued.
+  const int ucount = L.u_cnt;
+  const int vcap = kProduct ? L.v_cap : 0;
+  const float alpha = L.alpha;
 
   const int64_t hoff = int64_t(head) * a.n * D;
   const int64_t hbytes = a.n * D * int64_t(sizeof(T));
@@ -854,13 +903,13 @@ __device__ __forceinline__ void bucket_item(const AttnArgs& a, SmemG<T, D>& sm, 
 
   const int t_b = (b_eff + KT - 1) / KT;
   const int t_u = (ucount + KT - 1) / KT;
-  const int t_v = (vcount + KT - 1) / KT;
-  const int ntiles = t_b + t_u + t_v;
+  const int t_vcap = (vcap + KT - 1) / KT;
+  const int ntiles_cap = t_b + t_u + t_vcap;
   // segment of tile t (0 bucket, 1 uniform, 2 V-norm), its first slot, its size
   auto seg_of = [&](int t, int& j0, int& cnt) {
     if (t < t_b) { j0 = t * KT; cnt = b_eff; return 0; }
     if (t < t_b + t_u) { j0 = (t - t_b) * KT; cnt = ucount; return 1; }
-    j0 = (t - t_b - t_u) * KT; cnt = vcount; return 2;
+    j0 = (t - t_b - t_u) * KT; cnt = vcap; return 2;
   };
   // stage slots of tiles [t0, t0 + kWin) in LDS; all of a thread's index
   // loads are issued before any of them is used
@@ -881,7 +930,7 @@ __device__ __forceinline__ void bucket_item(const AttnArgs& a, SmemG<T, D>& sm, 
       const int t = t0 + e / KT;
       kind[i] = -1;
       jj[i] = 0;
-      if (t < ntiles) {
+      if (t < ntiles_cap) {
         int j0, cnt;
         const int sg = seg_of(t, j0, cnt);
         const int j = j0 + e % KT;
@@ -920,6 +969,7 @@ __device__ __forceinline__ void bucket_item(const AttnArgs& a, SmemG<T, D>& sm, 
   };
 
   fill(0);
+  const int ntiles = kProduct && a.meta[rec * 4 + 1] == 0 ? t_b + t_u : ntiles_cap;
   __syncthreads();
   issue(0);
   pipe.commit(sm.buf[0], needs_v(0));

@@ -59,6 +59,13 @@ struct Level {
   int64_t seg_wg0;    // first per-segment work-group of this level
   int64_t att_wg0;    // first attention work-group of this level
   int64_t att_qch;    // query chunks per bucket
+  // Sample lists of every sub-problem at this level: the uniform list holds
+  // u_cnt = min(m, n_k) entries of weight alpha (n_k / m, or 1 when the list
+  // is exhaustive); the V-norm list holds v_cap entries, or none when the
+  // node's V rows are all zero (recorded per node by the sampler).
+  int u_cnt;
+  int v_cap;
+  float alpha;
 };
 
 struct LevelTable {

@@ -88,6 +88,10 @@ int make_plan(Plan& p, int64_t n, int d, int heads, int causal, int b, int m,
     v.seg_wg0 = p.seg_wgs;
     p.seg_wgs += int64_t(heads) * 2 * v.nseg;
     v.att_qch = ceil_div(v.b_eff, kAttnQ);
+    const bool exhaustive = int64_t(m) >= v.h;
+    v.u_cnt = exhaustive ? static_cast<int>(v.h) : m;
+    v.v_cap = v.u_cnt;
+    v.alpha = exhaustive ? 1.f : static_cast<float>(double(v.h) / double(m));
     v.att_wg0 = p.att_wgs;
     p.att_wgs += int64_t(heads) * v.nseg * v.nbucket * v.att_qch;
   }

@@ -160,6 +160,27 @@ def test_forward_matches_oracle(case):
     assert np.abs(to_np(L) - Lref).max() <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_forward_empty_vnorm_lists(dtype):
+    """V zero on the first half of the keys: every sub-problem whose key range
+    lies there has V-norm total 0, so its V-norm list is empty (the product
+    keeps only the bucket term), while the others sample as usual."""
+    banner(f"forward empty V-norm lists {dtype}")
+    w, Q, K, V, _ = _inputs("chatglm2_causal_n32768_d128_h32_bf16", heads=2, n=2048, d=64,
+                            dtype=dtype, b=64, m=48, recursion_base=256)
+    V = V.copy()
+    V[0, : w.n // 2] = 0.0
+    V[1, : w.n // 4] = 0.0
+    O, L, ws, layout = _run_forward(w, Q, K, V)
+    art = {}
+    Oref, Lref = oha.hyperattention(Q, K, V, causal=True, b=w.b, m=w.m, r=w.r,
+                                    recursion_base=w.recursion_base, seed=w.method_seed,
+                                    artifacts=art)
+    _check_artifacts(w, Q, K, V, ws, layout, art)
+    assert max_rel(to_np(O), Oref) <= TOL[w.dtype]
+    assert np.abs(to_np(L) - Lref).max() <= TOL[w.dtype]
+
+
 def test_planted_workload_full():
     """8 heads, n = 8192, d = 64, bf16, planted heavy keys: full parity."""
     banner("forward planted n=8192")
