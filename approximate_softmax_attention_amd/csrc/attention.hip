@@ -52,6 +52,7 @@ namespace ha {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
@@ -343,16 +344,20 @@ struct LaneOffs<float, D> {
 template <typename T, int D>
 struct WaveState {
   f32x16 o[D / 32];
-  float m;      // running reference maximum (log2 units)
+  float m;      // running reference maximum (log2 units; 0 until the row has one)
   float l;      // this lane's part of the row sum (its 16 keys per block)
+  float thr;    // raw score that moves the reference: (m + kTau) / c; -inf before
+                // the row's first reference, +inf for a lane without a row
 };
 
+// valid: the lane's query row exists (rows past the end never take a reference)
 template <typename T, int D>
-__device__ __forceinline__ void init_state(WaveState<T, D>& ws) {
+__device__ __forceinline__ void init_state(WaveState<T, D>& ws, bool valid) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) ws.o[db] = zero16();
-  ws.m = -INFINITY;
+  ws.m = 0.f;
   ws.l = 0.f;
+  ws.thr = valid ? -INFINITY : INFINITY;
 }
 
 // S^T for key block kb of the tile: s[i] = score of key 32kb + 8(i/4) + 4g + i%4
@@ -401,10 +406,12 @@ __device__ __forceinline__ int key_of(int kb, int i, int g) {
   return 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
 }
 
-// O^T += V^T P^T for key block kb, p[i] the (weighted) probability of key_of(kb, i)
+// O^T += V^T P^T for key block kb, p[i] the (weighted) probability of
+// key_of(kb, i); bf16 tiles take it as the packed pb[i / 8][i % 8].
 template <typename T, int D>
 __device__ __forceinline__ void accumulate_pv(const Buf<T, D>& b, const LaneOffs<T, D>& lo,
-                                              WaveState<T, D>& ws, const f32x16& p, int kb) {
+                                              WaveState<T, D>& ws, const f32x16& p,
+                                              const bf16x8_t* pb, int kb) {
   if constexpr (sizeof(T) == 2) {
     if constexpr (D == 128) {
       // all transposing reads of the block first, as for the score chain
@@ -423,24 +430,18 @@ __device__ __forceinline__ void accumulate_pv(const Buf<T, D>& b, const LaneOffs
       __builtin_amdgcn_s_setprio(kMfmaPrio);
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        bf16x8_t pb;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[8 * st + j];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           const bf16x8_t a = __builtin_bit_cast(
               bf16x8_t,
               __builtin_shufflevector(vx[st][db][0], vx[st][db][1], 0, 1, 2, 3, 4, 5, 6, 7));
-          ws.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, ws.o[db], 0, 0, 0);
+          ws.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], ws.o[db], 0, 0, 0);
         }
       }
     } else {
       __builtin_amdgcn_s_setprio(kMfmaPrio);
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        bf16x8_t pb;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[8 * st + j];
         const char* base = reinterpret_cast<const char*>(b.v) + (32 * kb + 16 * st) * D * 2;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
@@ -450,7 +451,7 @@ __device__ __forceinline__ void accumulate_pv(const Buf<T, D>& b, const LaneOffs
               __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + lo.v[1][db]));
           const bf16x8_t a = __builtin_bit_cast(
               bf16x8_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-          ws.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, ws.o[db], 0, 0, 0);
+          ws.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], ws.o[db], 0, 0, 0);
         }
       }
     }
@@ -481,7 +482,9 @@ __device__ __forceinline__ void compute_tile(const Buf<T, D>& b, const LaneOffs<
                                              const QFrag<T, D>& q, WaveState<T, D>& ws, float c,
                                              bool masked, int nvalid, int lim) {
   constexpr int NB = Buf<T, D>::KT / 32;
+  constexpr bool kPack = sizeof(T) == 2 && KIND != KIND_SUM_W;   // bf16 P feeds the product
   const int g = lane_id() >> 5;
+  const float inv_c = 1.f / c;
 #pragma unroll
   for (int kb = 0; kb < NB; ++kb) {
     if (masked && 32 * kb >= nvalid) break;            // rest of the tile is empty
@@ -499,38 +502,62 @@ __device__ __forceinline__ void compute_tile(const Buf<T, D>& b, const LaneOffs<
         s[i] = ok ? s[i] : -INFINITY;
       }
     }
+    // The reference moves only when some lane's raw maximum passes its
+    // threshold; then both halves of each row take the row maximum (one
+    // permlane swap) and rescale if it exceeds the reference by kTau.
     float mx = fmaxf(s[0], s[1]);
 #pragma unroll
     for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s[i]);
-    mx = half_swap_max(mx) * c;
-    const bool need = mx > ws.m + kTau;
-    if (__ballot(need)) {
-      const float m_new = need ? mx : ws.m;
-      const float f = (m_new == -INFINITY || m_new == ws.m) ? 1.f : fast_exp2(ws.m - m_new);
-      ws.l *= f;
+    if (__ballot(mx > ws.thr)) {
+      mx = half_swap_max(mx) * c;
+      const bool fresh = ws.thr == -INFINITY;
+      if (fresh ? mx > -INFINITY : mx > ws.m + kTau) {
+        const float f = fresh ? 1.f : fast_exp2(ws.m - mx);
+        ws.l *= f;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ws.o[db][i] *= f;
-      ws.m = m_new;
-    }
-    const float mref = ws.m == -INFINITY ? 0.f : ws.m;
-    float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = fast_exp2(fmaf(s[i], c, -mref));
-      if (KIND == KIND_PLAIN) {
-        if (i & 1) ls1 += p; else ls0 += p;
-        s[i] = p;
-      } else if (KIND == KIND_SUM_W) {
-        if (i & 1) ls1 = fmaf(b.w[key_of(kb, i, g)], p, ls1);
-        else ls0 = fmaf(b.w[key_of(kb, i, g)], p, ls0);
-      } else {
-        s[i] = b.w[key_of(kb, i, g)] * p;
+          for (int i = 0; i < 16; ++i) ws.o[db][i] *= f;
+        ws.m = mx;
+        ws.thr = (mx + kTau) * inv_c;
       }
     }
-    if (KIND != KIND_PV_W) ws.l += ls0 + ls1;
-    if (KIND != KIND_SUM_W) accumulate_pv<T, D>(b, lo, ws, s, kb);
+    // (Weighted) probabilities in place, their bf16 pairs, and this lane's
+    // block sum of what the row sum takes: the bf16 values that feed the
+    // product (one dot2 per pair), else the fp32 ones.
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s[i] = fast_exp2(fmaf(s[i], c, -ws.m));
+      if (KIND != KIND_PLAIN) s[i] *= b.w[key_of(kb, i, g)];
+    }
+    bf16x8_t pb[2];
+    float a0 = 0.f, a1 = 0.f;
+    if constexpr (kPack) {
+      bf16x2_t one;
+      one[0] = (__bf16)1.f;
+      one[1] = (__bf16)1.f;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pb[st][j] = (__bf16)s[8 * st + j];
+        // (pairs by constant shuffles: element access on a bit_cast of the
+        // vector came out wrong, every pair read as the first)
+        const bf16x8_t v = pb[st];
+        a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, a0, false);
+        a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, a1, false);
+        a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, a0, false);
+        a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, a1, false);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i & 1) a1 += s[i];
+        else a0 += s[i];
+      }
+    }
+    const float bsum = a0 + a1;
+    if (KIND != KIND_PV_W) ws.l += bsum;
+    if (KIND != KIND_SUM_W) accumulate_pv<T, D>(b, lo, ws, s, pb, kb);
   }
 }
 
@@ -732,7 +759,7 @@ __device__ __forceinline__ void exact_item(const AttnArgs& a, Smem<T, D>& sm, ui
   LaneOffs<T, D> lo;
   lo.init();
   WaveState<T, D> ws;
-  init_state<T, D>(ws);
+  init_state<T, D>(ws, qrow >= 0);
 
   const int64_t k_end = kCausal ? q_end : b_hi;
   const int ntiles = int((k_end - b_lo + KT - 1) / KT);
@@ -899,7 +926,7 @@ __device__ __forceinline__ void bucket_item(const AttnArgs& a, SmemG<T, D>& sm, 
   LaneOffs<T, D> lo;
   lo.init();
   WaveState<T, D> ws;
-  init_state<T, D>(ws);
+  init_state<T, D>(ws, qrow >= 0);
 
   const int t_b = (b_eff + KT - 1) / KT;
   const int t_u = (ucount + KT - 1) / KT;
