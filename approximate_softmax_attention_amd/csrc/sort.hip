@@ -8,9 +8,10 @@
 //   1. per chunk of 2048 elements: a 256-bin histogram (LDS counters);
 //   2. per segment: exclusive offsets, bin-major then chunk-minor;
 //   3. per chunk: stable ranks (wave ballots find the earlier lanes with the
-//      same code, LDS counts carry the order across waves and batches) and
-//      the scatter of perm (sorted position -> row) and rank (slot -> sorted
-//      position, keys only).
+//      same code, per-wave LDS counts carry the order across batches and
+//      waves), then perm (sorted position -> row) written in sorted order
+//      from an LDS copy of the chunk, and rank (slot -> sorted position, keys
+//      only).
 #include "common.h"
 #include "device_util.h"
 
@@ -140,39 +141,52 @@ __global__ __launch_bounds__(kThreads) void sort_offsets_kernel(SortArgs a) {
   }
 }
 
+// Wave wv owns the chunk's elements [wv * kWaveSpan, (wv + 1) * kWaveSpan)
+// (kPer batches of 64), so stable ranks need no barrier inside the wave: a
+// batch's equal codes are found by ballots and the wave's running count per
+// code lives in its own LDS row. Elements are then placed at their sorted
+// position within the chunk in LDS and written out in that order, so lanes
+// next to each other write runs of one bin's consecutive global positions.
+constexpr int kWaves = kThreads / 64;
+constexpr int kWaveSpan = kSortChunk / kWaves;
+
 __global__ __launch_bounds__(kThreads) void sort_scatter_kernel(SortArgs a) {
-  __shared__ uint32_t run[kSortBins];
-  __shared__ uint32_t wcnt[kThreads / 64][kSortBins];
+  __shared__ uint32_t base[kSortBins];             // chunk's first global position per bin
+  __shared__ uint32_t lstart[kSortBins];           // chunk's first local position per bin
+  __shared__ uint32_t wcnt[kWaves][kSortBins];     // per-wave counts, then wave prefixes
+  __shared__ uint32_t wtot[kWaves];
+  __shared__ int32_t srow[kSortChunk];
+  __shared__ uint32_t spos[kSortChunk];
   const int64_t w = blockIdx.x;
   const ChunkRef c = decode_chunk(a, w);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = lane_id();
-  run[tid] = a.offs[w * kSortBins + tid];
+  base[tid] = a.offs[w * kSortBins + tid];
 #pragma unroll
-  for (int i = 0; i < kThreads / 64; ++i) wcnt[i][tid] = 0;
-  __syncthreads();
+  for (int i = 0; i < kWaves; ++i) wcnt[i][tid] = 0;
   const uint8_t* codes = a.codes[c.side] + int64_t(c.head) * a.n;
   const int64_t slot0 = (int64_t(c.lv) * a.heads + c.head) * a.S + c.seg * c.h;
   int32_t* perm = a.perm[c.side] + slot0;
   int32_t* rank = (a.rank && c.side == 1) ? a.rank + slot0 : nullptr;
   const int64_t t0 = c.chunk * kSortChunk;
   const int64_t t1 = t0 + kSortChunk < c.h ? t0 + kSortChunk : c.h;
+  const int64_t tw = t0 + wave * kWaveSpan;          // this wave's first element
   const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
-  // all of this thread's codes are loaded before the batch loop
+  // all of this thread's codes are loaded before any is ranked
   uint32_t cv[kPer];
 #pragma unroll
   for (int b = 0; b < kPer; ++b) {
-    const int64_t t = t0 + b * kThreads + tid;
+    const int64_t t = tw + b * 64 + lane;
     cv[b] = t < t1 ? codes[seg_row(a, c.side, c.seg, c.h, t)] : 0u;
   }
+  __syncthreads();
+  // rank within the wave: earlier batches (the wave's count row) plus the
+  // earlier lanes of this batch with the same code
+  uint32_t inw[kPer];
 #pragma unroll
   for (int b = 0; b < kPer; ++b) {
-    const int64_t base = t0 + b * kThreads;
-    if (base >= t1) break;
-    const int64_t t = base + tid;
-    const bool valid = t < t1;
-    const int64_t row = seg_row(a, c.side, c.seg, c.h, t);
+    const bool valid = tw + b * 64 + lane < t1;
     const uint32_t code = cv[b];
     uint64_t eq = __ballot(valid);
 #pragma unroll
@@ -182,24 +196,47 @@ __global__ __launch_bounds__(kThreads) void sort_scatter_kernel(SortArgs a) {
       eq &= bit ? bk : ~bk;
     }
     const uint32_t local = __popcll(eq & lt_mask);
-    if (valid && local == 0) wcnt[wave][code] = uint32_t(__popcll(eq));
+    const uint32_t before = valid ? wcnt[wave][code] : 0u;
+    inw[b] = before + local;
+    // every lane has read before the leader of each code writes (one wave,
+    // LDS operations in program order)
+    __builtin_amdgcn_wave_barrier();
+    if (valid && local == 0) wcnt[wave][code] = before + uint32_t(__popcll(eq));
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  // per bin: prefixes over the waves, and the chunk's exclusive scan over bins
+  {
+    uint32_t run = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      const uint32_t v = wcnt[i][tid];
+      wcnt[i][tid] = run;
+      run += v;
+    }
+    const uint32_t incl = uint32_t(wave_incl_scan(uint64_t(run)));
+    if (lane == 63) wtot[wave] = incl;
     __syncthreads();
-    if (valid) {
-      uint32_t pos = run[code] + local;
-      for (int i = 0; i < wave; ++i) pos += wcnt[i][code];
-      perm[pos] = int32_t(row);
+    uint32_t before = 0;
+    for (int i = 0; i < wave; ++i) before += wtot[i];
+    lstart[tid] = before + incl - run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < kPer; ++b) {
+    const int64_t t = tw + b * 64 + lane;
+    if (t < t1) {
+      const uint32_t code = cv[b];
+      const uint32_t r = wcnt[wave][code] + inw[b];   // rank among the chunk's equal codes
+      const uint32_t pos = base[code] + r;
+      srow[lstart[code] + r] = int32_t(seg_row(a, c.side, c.seg, c.h, t));
+      spos[lstart[code] + r] = pos;
       if (rank) rank[t] = int32_t(pos);
     }
-    __syncthreads();
-    uint32_t add = 0;
-#pragma unroll
-    for (int i = 0; i < kThreads / 64; ++i) {
-      add += wcnt[i][tid];
-      wcnt[i][tid] = 0;
-    }
-    run[tid] += add;
-    __syncthreads();
   }
+  __syncthreads();
+  const int nv = int(t1 - t0);
+  for (int j = tid; j < nv; j += kThreads) perm[spos[j]] = srow[j];
 }
 
 // Recompute the work-group offsets of the table for the given side count.
