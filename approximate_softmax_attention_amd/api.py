@@ -73,7 +73,11 @@ def alloc_workspace(nbytes, device):
 
 def forward(q, k, v, *, causal, b=256, m=256, r=8, recursion_base=4096, seed=0,
             return_lse=False, workspace=None, out=None, lse_out=None):
-    """HyperAttention forward; returns O (and lse if asked)."""
+    """HyperAttention forward; returns O (and lse if asked).
+
+    r: hyperplanes per head for sortLSH (1..8), or 0 for the local block mask
+    (bucket k = query and key rows [k b, (k+1) b) of each sub-problem).
+    """
     shape, q, k, v = _qkv(q, k, v)
     H, n, d = q.shape
     dt = _dtype_code(q)

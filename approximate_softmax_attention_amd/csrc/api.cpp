@@ -135,8 +135,8 @@ int hyperattn_workspace_layout(int64_t n, int d, int heads, int causal, int b, i
 
 int sortlsh_hyperplanes(uint64_t seed, int heads, int r, int d, float* G_host) {
   g_error.clear();
-  if (!G_host) return fail(HA_ERR_NULL, "G_host is NULL");
-  if (r < 1 || r > 8) return fail(HA_ERR_UNSUPPORTED, "r=%d not in [1, 8]", r);
+  if (r < 0 || r > 8) return fail(HA_ERR_UNSUPPORTED, "r=%d not in [0, 8]", r);
+  if (!G_host && r > 0) return fail(HA_ERR_NULL, "G_host is NULL");
   if (d != 64 && d != 128) return fail(HA_ERR_UNSUPPORTED, "d=%d not 64 or 128", d);
   if (heads < 0 || heads >= (1 << 16)) return fail(HA_ERR_SHAPE, "heads=%d out of range", heads);
   host_hyperplanes(seed, heads, r, d, G_host);
@@ -226,7 +226,7 @@ int sortlsh_hash(const void* X, int64_t n, int d, int heads, int r, uint64_t see
   if (dtype != HA_F32 && dtype != HA_BF16)
     return fail(HA_ERR_UNSUPPORTED, "dtype %d is not HA_F32 or HA_BF16", dtype);
   if (d != 64 && d != 128) return fail(HA_ERR_UNSUPPORTED, "d=%d not 64 or 128", d);
-  if (r < 1 || r > 8) return fail(HA_ERR_UNSUPPORTED, "r=%d not in [1, 8]", r);
+  if (r < 0 || r > 8) return fail(HA_ERR_UNSUPPORTED, "r=%d not in [0, 8]", r);
   if (n < 0 || n >= (int64_t(1) << 31)) return fail(HA_ERR_SHAPE, "n=%lld out of range", (long long)n);
   if (heads < 0 || heads >= (1 << 16)) return fail(HA_ERR_SHAPE, "heads=%d out of range", heads);
   if (n == 0 || heads == 0) return HA_OK;

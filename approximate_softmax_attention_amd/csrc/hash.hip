@@ -434,6 +434,30 @@ __global__ __launch_bounds__(kThreads) void vnorm_prefix_kernel(
   if (row == n - 1) Ph[n] = incl;
 }
 
+// r = 0 (no hyperplanes): every code is GrayRank(0) = 0. codes[z] is a
+// [heads][n] array; blockIdx.y is the head, z the side.
+__global__ __launch_bounds__(kThreads) void zero_codes_kernel(uint8_t* __restrict__ cq,
+                                                              uint8_t* __restrict__ ck,
+                                                              int64_t n) {
+  uint8_t* c = (blockIdx.z == 0 ? cq : ck) + int64_t(blockIdx.y) * n;
+  const int64_t i0 = (int64_t(blockIdx.x) * kThreads + threadIdx.x) * 16;
+  if (i0 + 16 <= n && (reinterpret_cast<uintptr_t>(c + i0) & 15) == 0) {
+    *reinterpret_cast<uint4*>(c + i0) = make_uint4(0, 0, 0, 0);
+  } else {
+    const int64_t i1 = i0 + 16 < n ? i0 + 16 : n;
+    for (int64_t i = i0; i < i1; ++i) c[i] = 0;
+  }
+}
+
+int launch_zero_codes(uint8_t* cq, uint8_t* ck, int64_t n, int heads, int sides,
+                      hipStream_t s) {
+  const dim3 grid(unsigned(ceil_div(n, int64_t(kThreads) * 16)), unsigned(heads),
+                  unsigned(sides));
+  hipLaunchKernelGGL(zero_codes_kernel, grid, dim3(kThreads), 0, s, cq, ck, n);
+  HA_LAUNCH_CHECK("hash");
+  return HA_OK;
+}
+
 template <typename T, int D>
 void launch_hash_t(dim3 grid, hipStream_t s, const void* Q, const void* K, const float* G,
                    const uint16_t* Gb, int r, int64_t n, uint8_t* cq, uint8_t* ck) {
@@ -477,11 +501,16 @@ int launch_hash(const Plan& p, const void* Q, const void* K, const void* V, cons
   char* w = static_cast<char*>(ws);
   {
     ProfRange pr("hash", s);
-    dispatch_hash(p.dtype, p.d, dim3(unsigned(ceil_div(p.n, kHashRows)), unsigned(p.heads), 2u),
-                  s, Q, K, G, Gb, p.r, p.n,
-                  reinterpret_cast<uint8_t*>(w + p.off[HA_WS_CODES_Q]),
-                  reinterpret_cast<uint8_t*>(w + p.off[HA_WS_CODES_K]));
-    HA_LAUNCH_CHECK("hash");
+    auto* cq = reinterpret_cast<uint8_t*>(w + p.off[HA_WS_CODES_Q]);
+    auto* ck = reinterpret_cast<uint8_t*>(w + p.off[HA_WS_CODES_K]);
+    if (p.r == 0) {
+      if (int rc = launch_zero_codes(cq, ck, p.n, p.heads, 2, s)) return rc;
+    } else {
+      dispatch_hash(p.dtype, p.d,
+                    dim3(unsigned(ceil_div(p.n, kHashRows)), unsigned(p.heads), 2u), s, Q, K,
+                    G, Gb, p.r, p.n, cq, ck);
+      HA_LAUNCH_CHECK("hash");
+    }
   }
   if (p.product) {
     ProfRange pr("vnorm_rows", s);
@@ -496,6 +525,7 @@ int launch_hash(const Plan& p, const void* Q, const void* K, const void* V, cons
 int launch_hash_one(const void* X, int64_t n, int d, int heads, int r, int dtype,
                     const float* G, const uint16_t* Gb, uint8_t* codes, hipStream_t s) {
   ProfRange pr("hash", s);
+  if (r == 0) return launch_zero_codes(codes, codes, n, heads, 1, s);
   dispatch_hash(dtype, d, dim3(unsigned(ceil_div(n, kHashRows)), unsigned(heads), 1u), s, X, X,
                 G, Gb, r, n, codes, codes);
   HA_LAUNCH_CHECK("hash");

@@ -116,7 +116,8 @@ int device_hyperplanes(uint64_t seed, int heads, int r, int d, const float** out
       }
   float* ptr = nullptr;
   uint16_t* ptr16 = nullptr;
-  HA_HIP_TRY(hipMalloc(&ptr, count * sizeof(float)));
+  // (at least one element, so that r = 0 still yields a valid pointer)
+  HA_HIP_TRY(hipMalloc(&ptr, (count ? count : 1) * sizeof(float)));
   hipError_t e = hipMalloc(&ptr16, count16 * sizeof(uint16_t));
   if (e == hipSuccess)
     e = hipMemcpy(ptr, host.data(), count * sizeof(float), hipMemcpyHostToDevice);

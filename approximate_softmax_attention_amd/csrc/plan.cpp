@@ -27,8 +27,8 @@ int make_plan(Plan& p, int64_t n, int d, int heads, int causal, int b, int m,
     return fail(HA_ERR_UNSUPPORTED, "dtype %d is not HA_F32 (0) or HA_BF16 (1)", dtype);
   if (d != 64 && d != 128)
     return fail(HA_ERR_UNSUPPORTED, "head dimension d=%d not supported (64 or 128)", d);
-  if (r < 1 || r > 8)
-    return fail(HA_ERR_UNSUPPORTED, "r=%d hyperplanes not supported (1..8)", r);
+  if (r < 0 || r > 8)
+    return fail(HA_ERR_UNSUPPORTED, "r=%d hyperplanes not supported (0..8)", r);
   if (n < 0 || n >= (int64_t(1) << 31))
     return fail(HA_ERR_SHAPE, "n=%lld out of range [0, 2^31)", (long long)n);
   if (heads < 0 || heads >= (1 << 16))

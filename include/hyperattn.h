@@ -74,6 +74,11 @@ enum ha_status {
  *       + sum over m V-row-norm samples j_t (p_j ∝ |V_j|^2) outside i's
  *         bucket of (1/(m p_j)) e^{s_ij} V_j;   O_i = N_i / d~_i.
  *     When m >= n_k both samples are every key of the range, weight 1.
+ *  r = 0 takes a predefined mask instead of sortLSH (HA page, "Algorithm":
+ *  Algorithms 2 and 3 accept any mask of the large entries): every code is 0,
+ *  so the stable sort keeps index order and bucket k of a sub-problem holds
+ *  its query rows and key rows [k b_eff, (k+1) b_eff), a block-diagonal local
+ *  mask. Q and K are then not read for hashing.
  *  Non-causal: one sub-problem with queries and keys [0, n).
  *  Causal: while a diagonal block is larger than recursion_base, split it in
  *  halves; the lower-left block (queries of the second half, keys of the
@@ -84,8 +89,8 @@ enum ha_status {
  * Q, K, V: inputs [heads][n][d]. O: output [heads][n][d], same dtype.
  * lse: optional output [heads][n] fp32 (log d~ merged over the row's parts).
  * b >= 1 bucket size; m >= 1 samples per estimator; recursion_base >= 1
- * (ignored when causal == 0); r in [1, 8] hyperplanes; seed selects
- * hyperplanes and samples.
+ * (ignored when causal == 0); r in [0, 8] hyperplanes (0: the local block
+ * mask above); seed selects hyperplanes and samples.
  * HA_ERR_SHAPE if b_eff does not divide a sub-problem size, if a causal block
  * to be split has odd size, or if one head (n * d elements) exceeds 2 GiB.
  * workspace: >= hyperattn_workspace_bytes(...) with the same arguments.
@@ -109,6 +114,7 @@ size_t hyperattn_workspace_bytes(int64_t n, int d, int heads, int causal,
  * codes[h][i] = GrayRank(sum_k [<x_i, g_hk> > 0] 2^k), where the sign is that
  * of the fp64 sum of x_it * g_hkt taken in order t = 0..d-1 and g_hk are the
  * hyperplanes sortlsh_hyperplanes(seed, heads, r, d) returns.
+ * r in [0, 8]; with r = 0 every code is 0 and perm is the identity.
  * codes: output [heads][n] uint8. perm: optional output [heads][n] int32,
  * perm[h][p] = the row at sorted position p.
  * workspace: >= sortlsh_hash_workspace_bytes(n, heads, perm != NULL).
@@ -147,7 +153,8 @@ int rowsum_estimate(const void* Q, const void* K, int64_t n, int d, int heads,
  * counter-based SplitMix64 draws (purpose 1, head h, node 0, counters 2e and
  * 2e+1 with e = k*d + t): sqrt(-2 ln u1) cos(2 pi u2), u1 in (0,1],
  * u2 in [0,1), rounded to fp32 and then to the nearest bf16 (ties to even).
- * Touches no device. G_host must hold heads*r*d floats.
+ * Touches no device. G_host must hold heads*r*d floats (r = 0: nothing is
+ * written and G_host may be NULL).
  */
 int sortlsh_hyperplanes(uint64_t seed, int heads, int r, int d, float* G_host);
 

@@ -45,6 +45,12 @@ def test_hyperplanes_equal_oracle(seed, heads, r, d):
                           sortlsh.hyperplanes(seed, heads, r, d))
 
 
+def test_zero_hyperplanes_allowed():
+    from approximate_softmax_attention_amd import api
+    assert api.hyperplanes(5, 3, 0, 64).shape == (3, 0, 64)
+    assert L().sortlsh_hyperplanes(5, 3, 0, 64, None) == 0
+
+
 def ws_bytes(n=1024, d=64, heads=1, causal=0, b=128, m=128, base=4096, r=8, dt=1):
     return L().hyperattn_workspace_bytes(n, d, heads, causal, b, m, base, r, dt)
 
@@ -54,6 +60,8 @@ def test_workspace_sizes_and_validation_messages():
     assert ws_bytes(n=0) == 0 and _lib.last_error() == ""
     assert ws_bytes(d=96) == 0 and "d=96" in _lib.last_error()
     assert ws_bytes(r=9) == 0 and "r=9" in _lib.last_error()
+    assert ws_bytes(r=-1) == 0 and "r=-1" in _lib.last_error()
+    assert ws_bytes(r=0) == ws_bytes(r=8) > 0
     assert ws_bytes(b=100) == 0 and "divide" in _lib.last_error()
     assert ws_bytes(n=96, causal=1, b=1, base=2) == 0 and "odd" in _lib.last_error()
     assert ws_bytes(m=0) == 0
@@ -100,8 +108,8 @@ def test_entry_points_validate_before_any_device_call():
     # unsupported
     rc = lib.exact_attention_forward(p, p, p, p, None, 10, 80, 1, 0, 1, None)
     assert rc == -3
-    rc = lib.sortlsh_hash(p, 10, 64, 1, 0, 1, 1, p, None, None, 0, None)
-    assert rc == -3
+    rc = lib.sortlsh_hash(p, 10, 64, 1, 9, 1, 1, p, None, None, 0, None)
+    assert rc == -3 and "r=9" in _lib.last_error()
     rc = lib.hyperattn_forward(p, p, p, p, None, 1024, 64, 1, 0, 128, 128, 4096, 8, 1, 5,
                                p, 1 << 20, None)
     assert rc == -3

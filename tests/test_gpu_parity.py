@@ -77,6 +77,20 @@ def test_sortlsh_hash_bit_exact(dtype, d):
         assert codes[0, 5].item() == 0
 
 
+def test_hash_without_hyperplanes_is_the_identity_order():
+    """r = 0: every code is 0 and the stable sort keeps index order (ragged
+    n, so the code rows of the second head are not 16-byte aligned)."""
+    banner("hash r=0")
+    import torch
+    api = _api()
+    x = torch.randn((3, 1003, 64), device="cuda", dtype=torch.bfloat16)
+    codes, perm = api.sortlsh_hash(x, r=0, seed=5, with_perm=True)
+    _sync()
+    assert int(codes.abs().sum()) == 0
+    ident = torch.arange(1003, device="cuda", dtype=torch.int32).expand(3, -1)
+    assert torch.equal(perm, ident)
+
+
 def test_hash_near_zero_projections_use_exact_sign():
     """Rows almost orthogonal to a hyperplane exercise the fp64 re-check."""
     banner("hash near-zero")
@@ -142,6 +156,12 @@ FORWARD_CASES = {
                          dict(heads=2, n=4096, b=128, m=100, recursion_base=512)),
     "causal_bf16_ragged_base": ("chatglm2_causal_n32768_d128_h32_bf16",
                                 dict(heads=1, n=1536, b=96, m=300, recursion_base=200)),
+    # r = 0: the local block mask in place of sortLSH
+    "local_mask_causal_bf16_d128": ("chatglm2_causal_n32768_d128_h32_bf16",
+                                    dict(heads=2, n=4096, b=128, m=100, r=0,
+                                         recursion_base=512)),
+    "local_mask_noncausal_fp32_d64": ("single_head_noncausal_n1024_d64_fp32",
+                                      dict(heads=2, n=1024, b=64, m=48, r=0)),
 }
 
 

@@ -223,11 +223,12 @@ def test_single_bucket_reduces_to_exact():
             assert np.abs(L[h] - Oe[h][1]).max() < 1e-12
 
 
-def test_exhaustive_samples_reduce_to_exact():
+@pytest.mark.parametrize("r", [8, 0])     # 0: the local block mask instead of sortLSH
+def test_exhaustive_samples_reduce_to_exact(r):
     Q, K, V = _inputs(64, 8, seed=1)
     Oe, Le = exact.exact_attention(Q[0], K[0], V[0])
     for b in (1, 8, 16):
-        O, L = ha.hyperattention(Q, K, V, causal=False, b=b, m=64, r=8, seed=4)
+        O, L = ha.hyperattention(Q, K, V, causal=False, b=b, m=64, r=r, seed=4)
         assert np.abs(O[0] - Oe).max() < 1e-12
         assert np.abs(L[0] - Le).max() < 1e-12
 

@@ -179,3 +179,19 @@ def test_similar_rows_share_buckets():
     G = sortlsh.hyperplanes(8, 1, 8, 64)[0]
     Q = rs.standard_normal((256, 64))
     assert np.array_equal(sortlsh.hash_codes(Q, G), sortlsh.hash_codes(Q * 3.0, G))
+
+
+def test_zero_hyperplanes_give_the_local_block_mask():
+    """r = 0 (a predefined mask in place of sortLSH): every code is 0, the
+    stable sort keeps index order, and bucket k is rows [k b, (k + 1) b) on
+    both sides (closed form)."""
+    rs = np.random.default_rng(5)
+    G = sortlsh.hyperplanes(3, 2, 0, 64)
+    assert G.shape == (2, 0, 64)
+    X = rs.standard_normal((96, 64))
+    codes = sortlsh.hash_codes(X, G[1])
+    assert np.array_equal(codes, np.zeros(96, dtype=codes.dtype))
+    s = sortlsh.sortlsh(codes, sortlsh.hash_codes(X[::-1], G[0]), 32)
+    idx = np.arange(96)
+    assert np.array_equal(s["bucket_q"], idx // 32)
+    assert np.array_equal(s["bucket_k"], idx // 32)
