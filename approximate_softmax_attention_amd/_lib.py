@@ -31,6 +31,10 @@ SIGNATURES = {
     "rowsum_estimate": (_i32, [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _u64, _i32, _vp,
                                _vp, _sz, _vp]),
     "sortlsh_hyperplanes": (_i32, [_u64, _i32, _i32, _i32, _fp]),
+    "hyperattn_forward_rope": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
+                                      _i32, _i32, _i32, _i32, _u64, _c.c_double, _i32, _vp, _sz,
+                                      _vp]),
+    "rope_table": (_i32, [_i64, _i32, _c.c_double, _fp]),
     "hyperattn_workspace_layout": (_i32, [_i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                           _c.POINTER(_i64), _c.POINTER(_i64)]),
     "hyperattn_last_error": (_c.c_char_p, []),

@@ -97,6 +97,41 @@ def forward(q, k, v, *, causal, b=256, m=256, r=8, recursion_base=4096, seed=0,
     return o
 
 
+def forward_rope(q, k, v, *, causal, rope_base=10000.0, b=256, m=256, r=8,
+                 recursion_base=4096, seed=0, return_lse=False, return_rotated=False,
+                 workspace=None):
+    """HyperAttention forward on Q and K before their rotary embedding, which
+    the library applies on the device in the pass that hashes them; returns O
+    (then lse, then the rotated Q and K, as asked)."""
+    shape, q, k, v = _qkv(q, k, v)
+    H, n, d = q.shape
+    dt = _dtype_code(q)
+    o = torch.empty_like(q)
+    qr, kr = torch.empty_like(q), torch.empty_like(k)
+    lse = torch.empty((H, n), dtype=torch.float32, device=q.device) if return_lse else None
+    nb = workspace_bytes(n, d, H, causal=causal, b=b, m=m, r=r,
+                         recursion_base=recursion_base, dtype=dt)
+    ws = workspace if workspace is not None else alloc_workspace(nb, q.device)
+    check(lib().hyperattn_forward_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(qr), _ptr(kr), _ptr(o),
+                                       _ptr(lse), n, d, H, int(causal), b, m, recursion_base, r,
+                                       seed, float(rope_base), dt, _ptr(ws), ws.numel(),
+                                       _stream(q.device)))
+    out = [o.reshape(shape)]
+    if return_lse:
+        out.append(lse.reshape(shape[:-1]))
+    if return_rotated:
+        out += [qr.reshape(shape), kr.reshape(shape)]
+    return out[0] if len(out) == 1 else tuple(out)
+
+
+def rope_table(n, d, rope_base=10000.0):
+    """The cos/sin table of forward_rope, [n, d/2, 2] fp32 (host computation)."""
+    T = np.empty((n, d // 2, 2), dtype=np.float32)
+    check(lib().rope_table(n, d, float(rope_base),
+                           T.ctypes.data_as(ctypes.POINTER(ctypes.c_float))))
+    return T
+
+
 def exact(q, k, v, *, causal=False, return_lse=False, out=None):
     """Exact softmax attention (the library's own kernel)."""
     shape, q, k, v = _qkv(q, k, v)

@@ -1,6 +1,7 @@
 // The C ABI declared in include/hyperattn.h: argument validation, the launch
 // sequence of each entry point, the thread-local error message and the
 // event-based kernel timing.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -159,25 +160,56 @@ int exact_attention_forward(const void* Q, const void* K, const void* V, void* O
   return launch_exact(Q, K, V, O, lse, n, d, heads, causal ? 1 : 0, dtype, n, nullptr, nullptr, s);
 }
 
-int hyperattn_forward(const void* Q, const void* K, const void* V, void* O, float* lse,
-                      int64_t n, int d, int heads, int causal, int b, int m, int recursion_base,
-                      int r, uint64_t seed, int dtype, void* workspace, size_t workspace_bytes,
-                      void* stream) {
-  g_error.clear();
+namespace {
+
+// The forward pass; with rope set, Q and K are first rotated into Qr and Kr
+// (in the pass that hashes them) and the attention reads those.
+struct Rope {
+  void* Qr;
+  void* Kr;
+  double base;
+};
+
+int forward_impl(const void* Q, const void* K, const void* V, void* O, float* lse, int64_t n,
+                 int d, int heads, int causal, int b, int m, int recursion_base, int r,
+                 uint64_t seed, int dtype, void* workspace, size_t workspace_bytes,
+                 void* stream, const Rope* rope) {
   Plan p;
   int rc = make_plan(p, n, d, heads, causal, b, m, recursion_base, r, dtype, true);
   if (rc != HA_OK) return rc;
+  if (rope && !(rope->base > 1.0 && std::isfinite(rope->base)))
+    return fail(HA_ERR_UNSUPPORTED, "rope_base=%g must be a finite number above 1", rope->base);
   if (n == 0 || heads == 0) return HA_OK;
   if (!Q || !K || !V || !O) return fail(HA_ERR_NULL, "Q, K, V and O must not be NULL");
+  if (rope && (!rope->Qr || !rope->Kr)) return fail(HA_ERR_NULL, "Q_rot and K_rot must not be NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p.causal && p.L == 0)   // the whole sequence is one base block
+  const float* tab = nullptr;
+  if (rope && (rc = device_rope_table(n, d, rope->base, &tab)) != HA_OK) return rc;
+  if (p.causal && p.L == 0) {  // the whole sequence is one base block
+    if (rope) {
+      if ((rc = launch_rope(p, Q, K, rope->Qr, rope->Kr, tab, false, nullptr, nullptr, nullptr,
+                            s)) != HA_OK)
+        return rc;
+      Q = rope->Qr;
+      K = rope->Kr;
+    }
     return launch_exact(Q, K, V, O, lse, n, d, heads, 1, dtype, n, nullptr, nullptr, s);
+  }
   rc = check_workspace(p, workspace, workspace_bytes);
   if (rc != HA_OK) return rc;
   const float* G = nullptr;
   const uint16_t* Gb = nullptr;
   if ((rc = device_hyperplanes(seed, heads, r, d, &G, &Gb)) != HA_OK) return rc;
-  if ((rc = launch_hash(p, Q, K, V, G, Gb, workspace, s)) != HA_OK) return rc;
+  if (rope) {
+    if ((rc = launch_rope(p, Q, K, rope->Qr, rope->Kr, tab, true, G, Gb, workspace, s)) != HA_OK)
+      return rc;
+    Q = rope->Qr;
+    K = rope->Kr;
+    rc = launch_hash(p, nullptr, nullptr, V, G, Gb, workspace, s);
+  } else {
+    rc = launch_hash(p, Q, K, V, G, Gb, workspace, s);
+  }
+  if (rc != HA_OK) return rc;
   if ((rc = launch_vnorm_scan(p, workspace, s)) != HA_OK) return rc;
   if ((rc = launch_sort(p, workspace, 2, s)) != HA_OK) return rc;
   if ((rc = launch_samples(p, seed, workspace, s)) != HA_OK) return rc;
@@ -185,6 +217,40 @@ int hyperattn_forward(const void* Q, const void* K, const void* V, void* O, floa
   if (p.causal)
     rc = launch_exact(Q, K, V, O, lse, n, d, heads, 1, dtype, p.base_block, &p, workspace, s);
   return rc;
+}
+
+}  // namespace
+
+int hyperattn_forward(const void* Q, const void* K, const void* V, void* O, float* lse,
+                      int64_t n, int d, int heads, int causal, int b, int m, int recursion_base,
+                      int r, uint64_t seed, int dtype, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  g_error.clear();
+  return forward_impl(Q, K, V, O, lse, n, d, heads, causal, b, m, recursion_base, r, seed,
+                      dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+int hyperattn_forward_rope(const void* Q, const void* K, const void* V, void* Q_rot,
+                           void* K_rot, void* O, float* lse, int64_t n, int d, int heads,
+                           int causal, int b, int m, int recursion_base, int r, uint64_t seed,
+                           double rope_base, int dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  g_error.clear();
+  const Rope rope{Q_rot, K_rot, rope_base};
+  return forward_impl(Q, K, V, O, lse, n, d, heads, causal, b, m, recursion_base, r, seed,
+                      dtype, workspace, workspace_bytes, stream, &rope);
+}
+
+int rope_table(int64_t n, int d, double rope_base, float* table_host) {
+  g_error.clear();
+  if (d != 64 && d != 128) return fail(HA_ERR_UNSUPPORTED, "d=%d not 64 or 128", d);
+  if (n < 0 || n >= (int64_t(1) << 31)) return fail(HA_ERR_SHAPE, "n=%lld out of range", (long long)n);
+  if (!(rope_base > 1.0 && std::isfinite(rope_base)))
+    return fail(HA_ERR_UNSUPPORTED, "rope_base=%g must be a finite number above 1", rope_base);
+  if (n == 0) return HA_OK;
+  if (!table_host) return fail(HA_ERR_NULL, "table_host is NULL");
+  host_rope_table(n, d, rope_base, table_host);
+  return HA_OK;
 }
 
 int rowsum_estimate(const void* Q, const void* K, int64_t n, int d, int heads, int b, int m, int r,

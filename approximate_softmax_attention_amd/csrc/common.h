@@ -111,8 +111,19 @@ void host_hyperplanes(uint64_t seed, int heads, int r, int d, float* G);
 
 // --------------------------------------------------------------- launchers
 // All return HA_OK or HA_ERR_HIP; arguments are validated by the caller.
+// Q (with K) null: no hash; V null: no V norms.
 int launch_hash(const Plan& p, const void* Q, const void* K, const void* V,
                 const float* G, const uint16_t* Gb, void* ws, hipStream_t s);
+// Rotary embedding of Q and K into Qr and Kr (rope.hip); with hash, also the
+// sortLSH codes of the rotated rows. tab: device_rope_table's.
+int launch_rope(const Plan& p, const void* Q, const void* K, void* Qr, void* Kr,
+                const float* tab, bool hash, const float* G, const uint16_t* Gb, void* ws,
+                hipStream_t s);
+// cos and sin of i * base^(-2t/d) for rows i < n and pairs t < d/2, as
+// [n][d/2][2], fp64 from the C library rounded to fp32 (host), and its
+// per-device cache.
+void host_rope_table(int64_t n, int d, double base, float* out);
+int device_rope_table(int64_t n, int d, double base, const float** out);
 int launch_hash_one(const void* X, int64_t n, int d, int heads, int r, int dtype,
                     const float* G, const uint16_t* Gb, uint8_t* codes, hipStream_t s);
 int launch_vnorm_scan(const Plan& p, void* ws, hipStream_t s);

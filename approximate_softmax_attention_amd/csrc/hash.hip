@@ -499,7 +499,7 @@ void dispatch_vnorm(int dtype, int d, dim3 grid, hipStream_t s, const void* V, i
 int launch_hash(const Plan& p, const void* Q, const void* K, const void* V, const float* G,
                 const uint16_t* Gb, void* ws, hipStream_t s) {
   char* w = static_cast<char*>(ws);
-  {
+  if (Q) {
     ProfRange pr("hash", s);
     auto* cq = reinterpret_cast<uint8_t*>(w + p.off[HA_WS_CODES_Q]);
     auto* ck = reinterpret_cast<uint8_t*>(w + p.off[HA_WS_CODES_K]);
@@ -512,7 +512,7 @@ int launch_hash(const Plan& p, const void* Q, const void* K, const void* V, cons
       HA_LAUNCH_CHECK("hash");
     }
   }
-  if (p.product) {
+  if (p.product && V) {
     ProfRange pr("vnorm_rows", s);
     dispatch_vnorm(p.dtype, p.d, dim3(unsigned(p.vblocks), unsigned(p.heads)), s, V, p.n,
                    reinterpret_cast<double*>(w + p.off[HA_WS_VNORM_A]),

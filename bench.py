@@ -178,6 +178,43 @@ def sweep(args, torch, api):
             n *= 2
 
 
+def rope_mode(args, torch, api, wl):
+    """The headline workload with its rotary embedding applied by the library
+    (hyperattn_forward_rope on the rows before RoPE): one JSON line with the
+    forward time and the per-kernel breakdown, the fused rotate-and-hash pass
+    included."""
+    w = wl.scaled(wl.WORKLOADS[args.workload or wl.HEADLINE], rope=False)
+    log(f"workload {w.name} before RoPE: generating inputs")
+    Q, K, V = make_device_inputs(w, torch)
+    nb = api.workspace_bytes(w.n, w.d, w.heads, causal=w.causal, b=w.b, m=w.m, r=w.r,
+                             recursion_base=w.recursion_base,
+                             dtype=api.HA_BF16 if w.dtype == "bf16" else api.HA_F32)
+    ws = api.alloc_workspace(nb, "cuda")
+    kw = dict(causal=w.causal, b=w.b, m=w.m, r=w.r, recursion_base=w.recursion_base,
+              seed=w.method_seed, workspace=ws)
+    for _ in range(args.warmup):
+        api.forward_rope(Q, K, V, **kw)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with api.KernelTimer() as kt:
+        e0.record(stream)
+        for _ in range(args.steps):
+            api.forward_rope(Q, K, V, **kw)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    kernels = {k: {"launches": n, "avg_ms": t / n} for k, (n, t) in kt.stats.items()}
+    rh = kernels.get("rope_hash", {}).get("avg_ms")
+    # rope_hash reads Q and K, writes them rotated, reads the cos/sin table once
+    moved = 2 * 2 * w.heads * w.n * w.d * (2 if w.dtype == "bf16" else 4) + w.n * w.d * 8
+    print(json.dumps({"mode": "forward_rope", "workload": w.name + " (RoPE on the device)",
+                      "steps": args.steps, "ms_per_step": ms, "tokens_per_s": w.n / (ms / 1e3),
+                      "rope_hash_gbs": moved / (rh / 1e3) / 1e9 if rh else None,
+                      "rope_hash_hbm_frac": moved / (rh / 1e3) / PEAK_HBM if rh else None,
+                      "kernels": kernels}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,6 +227,9 @@ def main():
                     help="the single-layer sweep of the HA page's experiment: forward time "
                          "of HyperAttention and of exact attention for n = 4096 .. 131072, "
                          "causal and not; one JSON line per point")
+    ap.add_argument("--rope", action="store_true",
+                    help="time the headline workload with RoPE applied by the library "
+                         "(hyperattn_forward_rope on the rows before RoPE); one JSON line")
     ap.add_argument("--sweep-heads", type=int, default=12)
     ap.add_argument("--sweep-d", type=int, default=64)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -209,6 +249,9 @@ def main():
 
     if args.sweep:
         sweep(args, torch, api)
+        return
+    if args.rope:
+        rope_mode(args, torch, api, wl)
         return
 
     w = wl.WORKLOADS[args.workload or wl.HEADLINE]

@@ -101,6 +101,41 @@ int hyperattn_forward(const void* Q, const void* K, const void* V, void* O,
                       int dtype, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/*
+ * hyperattn_forward_rope — hyperattn_forward on Q and K that still need their
+ * rotary position embedding, applied on the device in the pass that hashes
+ * them (the long-context layers rotate Q and K before attention, and the
+ * hash must see the rotated rows: HA page, "Algorithm", Definition 1 applied
+ * to the rows the attention uses).
+ * Rotation: pairs (t, t + d/2) for t < d/2, theta_t = rope_base^(-2t/d), row
+ * i at position i:
+ *   x'_t = x_t cos(i theta_t) - x_{t+d/2} sin(i theta_t),
+ *   x'_{t+d/2} = x_t sin(i theta_t) + x_{t+d/2} cos(i theta_t),
+ * in fp32 with each product and sum rounded once, cos and sin as rope_table
+ * returns them, then (bf16 rows) rounded to the nearest bf16, ties to even.
+ * Q_rot, K_rot: outputs [heads][n][d] in the input dtype, the rotated rows
+ * (the attention then reads them). All other arguments, outputs and errors
+ * as hyperattn_forward, with the same workspace size; rope_base must be a
+ * finite number above 1 (HA_ERR_UNSUPPORTED). The cos/sin table
+ * (n * d * 4 bytes) is computed on the host on first use and kept on the
+ * device in a small cache keyed by (n, d, rope_base), like the hyperplanes.
+ */
+int hyperattn_forward_rope(const void* Q, const void* K, const void* V,
+                           void* Q_rot, void* K_rot, void* O, float* lse,
+                           int64_t n, int d, int heads, int causal, int b,
+                           int m, int recursion_base, int r, uint64_t seed,
+                           double rope_base, int dtype, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * rope_table — host-only: the cos/sin table hyperattn_forward_rope uses.
+ * table_host[(i * d/2 + t) * 2 + 0] = cos(i * theta_t) and [... + 1] =
+ * sin(i * theta_t), with theta_t = pow(rope_base, -2t/d), the angle, cos and
+ * sin in fp64 from the C library, each entry rounded once to fp32.
+ * table_host holds n * d floats.
+ */
+int rope_table(int64_t n, int d, double rope_base, float* table_host);
+
 /* Bytes of workspace hyperattn_forward needs for these sizes (0 on invalid
  * arguments; hyperattn_last_error() then says why). */
 size_t hyperattn_workspace_bytes(int64_t n, int d, int heads, int causal,

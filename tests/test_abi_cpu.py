@@ -45,6 +45,31 @@ def test_hyperplanes_equal_oracle(seed, heads, r, d):
                           sortlsh.hyperplanes(seed, heads, r, d))
 
 
+@pytest.mark.parametrize("n,d,base", [(7, 64, 10000.0), (300, 128, 10000.0), (33, 64, 500.0)])
+def test_rope_table_equals_oracle(n, d, base):
+    """The host cos/sin table of the rotary embedding is the oracle's, bit for
+    bit (fp64 from the C library, rounded once to fp32)."""
+    from approximate_softmax_attention_amd import api
+    from oracle import rope
+    T = api.rope_table(n, d, base)
+    c, s = rope.angle_table(n, d, base)
+    assert np.array_equal(T[..., 0], c.astype(np.float32))
+    assert np.array_equal(T[..., 1], s.astype(np.float32))
+
+
+def test_forward_rope_validates_before_any_device_call():
+    lib = L()
+    p = _vp(256)
+    rc = lib.hyperattn_forward_rope(p, p, p, p, p, p, None, 1024, 64, 1, 0, 128, 128, 4096, 8,
+                                    1, 1.0, 1, p, 1 << 20, None)
+    assert rc == -3 and "rope_base" in _lib.last_error()
+    rc = lib.hyperattn_forward_rope(p, p, p, None, p, p, None, 1024, 64, 1, 0, 128, 128, 4096,
+                                    8, 1, 10000.0, 1, p, 1 << 20, None)
+    assert rc == -1 and "Q_rot" in _lib.last_error()
+    rc = lib.rope_table(16, 96, 10000.0, None)
+    assert rc == -3
+
+
 def test_zero_hyperplanes_allowed():
     from approximate_softmax_attention_amd import api
     assert api.hyperplanes(5, 3, 0, 64).shape == (3, 0, 64)

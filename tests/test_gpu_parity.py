@@ -201,6 +201,58 @@ def test_forward_empty_vnorm_lists(dtype):
     assert np.abs(to_np(L) - Lref).max() <= TOL[w.dtype]
 
 
+ROPE_CASES = {
+    # name: (workload, changes); inputs are the workload's rows before RoPE
+    "causal_bf16_d128_fused": ("chatglm2_causal_n32768_d128_h32_bf16",
+                               dict(heads=2, n=4096, b=128, m=100, recursion_base=512,
+                                    rope=False)),
+    "noncausal_fp32_d64": ("single_head_noncausal_n1024_d64_fp32",
+                           dict(heads=2, n=1024, b=64, m=48)),
+    "causal_bf16_d64_local_mask": ("chatglm2_causal_n32768_d128_h32_bf16",
+                                   dict(heads=2, n=2048, d=64, b=64, m=48, r=0,
+                                        recursion_base=256, rope=False)),
+    "causal_bf16_no_recursion": ("chatglm2_causal_n32768_d128_h32_bf16",
+                                 dict(heads=2, n=512, b=128, m=64, recursion_base=4096,
+                                      rope=False)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(ROPE_CASES))
+def test_forward_rope_matches_oracle(case):
+    """Rotary embedding on the device (fused with the hash for bf16): the
+    rotated rows are bit-exact, then every artefact and output as in the
+    plain forward on those rows."""
+    from oracle import rope as orope
+    import torch
+    name, changes = ROPE_CASES[case]
+    banner(f"forward rope {case}")
+    w, Q, K, V, _ = _inputs(name, **changes)
+    api = _api()
+    dt = w.dtype
+    q, k, v = (to_dev(x, dt) for x in (Q, K, V))
+    kw = dict(causal=w.causal, b=w.b, m=w.m, r=w.r, recursion_base=w.recursion_base,
+              dtype=api.HA_BF16 if dt == "bf16" else api.HA_F32)
+    layout = api.workspace_layout(w.n, w.d, w.heads, **kw)
+    ws = api.alloc_workspace(api.workspace_bytes(w.n, w.d, w.heads, **kw), "cuda")
+    ws.fill_(0xFF)
+    O, L, Qr, Kr = api.forward_rope(q, k, v, causal=w.causal, b=w.b, m=w.m, r=w.r,
+                                    recursion_base=w.recursion_base, seed=w.method_seed,
+                                    return_lse=True, return_rotated=True, workspace=ws)
+    _sync()
+    tab = orope.angle_table(w.n, w.d, 10000.0)
+    Qo = np.stack([orope.rope(Q[h], dtype=dt, table=tab) for h in range(w.heads)])
+    Ko = np.stack([orope.rope(K[h], dtype=dt, table=tab) for h in range(w.heads)])
+    assert np.array_equal(to_np(Qr), Qo) and np.array_equal(to_np(Kr), Ko)
+    art = {}
+    Oref, Lref = oha.hyperattention(Qo, Ko, V, causal=w.causal, b=w.b, m=w.m, r=w.r,
+                                    recursion_base=w.recursion_base, seed=w.method_seed,
+                                    artifacts=art)
+    if not (w.causal and w.n <= w.recursion_base):
+        _check_artifacts(w, Qo, Ko, V, ws, layout, art)
+    assert max_rel(to_np(O), Oref) <= TOL[w.dtype]
+    assert np.abs(to_np(L) - Lref).max() <= TOL[w.dtype]
+
+
 def test_planted_workload_full():
     """8 heads, n = 8192, d = 64, bf16, planted heavy keys: full parity."""
     banner("forward planted n=8192")
