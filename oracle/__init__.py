@@ -34,4 +34,6 @@ exact          exact attention Att = D^-1 exp(QK^T) V, causal and not
 sortlsh        hyperplanes, Hamming-sorted hash, sortLSH buckets
 sampling       uniform column samples and V-row-norm samples
 hyperattention ApproxD + HyperAttention (non-causal), causal recursion, merge
+backward       gradients of exact attention and of the HyperAttention estimator
+rope           rotary position embedding of Q and K before hashing
 """

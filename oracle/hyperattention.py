@@ -115,7 +115,7 @@ def _head_inputs(Q, K, V):
 
 
 def hyperattention(Q, K, V, *, causal, b, m, r=8, recursion_base=4096, seed=0,
-                   rows=None, artifacts=None, G=None, head_ids=None):
+                   rows=None, artifacts=None, G=None, head_ids=None, sample_from=None):
     """HyperAttention forward for all heads. Q, K, V: [H, n, d].
 
     rows: optional list of query rows to evaluate (all heads); others are NaN.
@@ -123,6 +123,11 @@ def hyperattention(Q, K, V, *, causal, b, m, r=8, recursion_base=4096, seed=0,
     G: optional hyperplanes [H, r, d] (defaults to sortlsh.hyperplanes(seed)).
     head_ids: the head index of each entry of the first axis (default 0..H-1);
     hyperplanes and random draws depend on it.
+    sample_from: optional (Q', K', V') of the same shapes: the hash codes come
+    from Q', K' and the V-norm weights from V' instead of the inputs, so the
+    buckets and sample lists stay fixed while the inputs move (the estimator
+    as a function of Q, K, V for a fixed draw, whose derivative the backward
+    pass computes).
     Returns O [H, n, d] and lse [H, n] (fp64).
     """
     H, n, d = np.shape(Q)
@@ -143,9 +148,11 @@ def hyperattention(Q, K, V, *, causal, b, m, r=8, recursion_base=4096, seed=0,
     for h in range(H):
         hid = hids[h]
         Qh, Kh, Vh = _head_inputs(Q[h], K[h], V[h])
-        codes_q = sortlsh.hash_codes(Qh, G[h])
-        codes_k = sortlsh.hash_codes(Kh, G[h])
-        _, W, P = sampling.vnorm_weights(Vh)
+        Qs, Ks, Vs = (Qh, Kh, Vh) if sample_from is None else _head_inputs(
+            sample_from[0][h], sample_from[1][h], sample_from[2][h])
+        codes_q = sortlsh.hash_codes(Qs, G[h])
+        codes_k = sortlsh.hash_codes(Ks, G[h])
+        _, W, P = sampling.vnorm_weights(Vs)
         head_art = []
         O = np.full((n, Vh.shape[1]), np.nan)
         lse = np.full(n, np.nan)
