@@ -35,6 +35,13 @@ SIGNATURES = {
                                       _i32, _i32, _i32, _i32, _u64, _c.c_double, _i32, _vp, _sz,
                                       _vp]),
     "rope_table": (_i32, [_i64, _i32, _c.c_double, _fp]),
+    "hyperattn_backward": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
+                                  _i32, _i32, _i32, _i32, _i32, _u64, _i32, _vp, _sz, _vp]),
+    "hyperattn_backward_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                 _i32]),
+    "exact_attention_backward": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32,
+                                        _i32, _i32, _i32, _vp, _sz, _vp]),
+    "exact_attention_backward_workspace_bytes": (_sz, [_i64, _i32]),
     "hyperattn_workspace_layout": (_i32, [_i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                           _c.POINTER(_i64), _c.POINTER(_i64)]),
     "hyperattn_last_error": (_c.c_char_p, []),
@@ -94,4 +101,6 @@ def header_functions():
 WS_REGIONS = ["CODES_Q", "CODES_K", "VNORM_A", "VNORM_W", "VNORM_P", "VNORM_BLK",
               "PERM_Q", "PERM_K", "RANK_K", "SORT_HIST", "SORT_OFFS",
               "U_IDX", "U_BKT", "V_IDX", "V_BKT", "V_W", "NODE_META",
-              "PART_O", "PART_LSE", "SCHED"]
+              "PART_O", "PART_LSE", "SCHED",
+              "DELTA", "PART_DQ", "PART_DK", "PART_DV",
+              "SLOT_FIRST", "SLOT_NEXT", "SLOT_DK", "SLOT_DV"]

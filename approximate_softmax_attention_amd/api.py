@@ -146,6 +146,79 @@ def exact(q, k, v, *, causal=False, return_lse=False, out=None):
     return o
 
 
+def _grad_inputs(q, k, v, o, lse, do):
+    shape, q, k, v = _qkv(q, k, v)
+    o, do = _fold(o, "o"), _fold(do, "do")
+    for t, name in ((o, "o"), (do, "do")):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must have the shape, dtype and device of q")
+    H, n, _ = q.shape
+    if not lse.is_contiguous() or lse.dtype != torch.float32 or lse.numel() != H * n:
+        raise ValueError("lse must be the forward pass's contiguous fp32 [heads, n] output")
+    return shape, q, k, v, o, lse, do
+
+
+def backward_workspace_bytes(n, d, heads, *, causal, b, m, r=8, recursion_base=4096,
+                             dtype=HA_BF16):
+    nb = lib().hyperattn_backward_workspace_bytes(n, d, heads, int(causal), b, m,
+                                                  recursion_base, r, dtype)
+    if nb == 0 and _lib.last_error():
+        raise _lib.HyperAttnError(-3, _lib.last_error())
+    return nb
+
+
+def backward(q, k, v, o, lse, do, *, causal, b=256, m=256, r=8, recursion_base=4096, seed=0,
+             workspace=None):
+    """Gradients (dq, dk, dv) of sum(do * o) for o, lse = forward(q, k, v, ...,
+    return_lse=True) with the same arguments (bf16 tensors)."""
+    shape, q, k, v, o, lse, do = _grad_inputs(q, k, v, o, lse, do)
+    H, n, d = q.shape
+    dt = _dtype_code(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nb = backward_workspace_bytes(n, d, H, causal=causal, b=b, m=m, r=r,
+                                  recursion_base=recursion_base, dtype=dt)
+    ws = workspace if workspace is not None else alloc_workspace(nb, q.device)
+    check(lib().hyperattn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), n, d, H, int(causal), b, m,
+                                   recursion_base, r, seed, dt, _ptr(ws), ws.numel(),
+                                   _stream(q.device)))
+    return dq.reshape(shape), dk.reshape(shape), dv.reshape(shape)
+
+
+def exact_backward(q, k, v, o, lse, do, *, causal=False):
+    """Gradients (dq, dk, dv) of exact attention (the library's own kernels)."""
+    shape, q, k, v, o, lse, do = _grad_inputs(q, k, v, o, lse, do)
+    H, n, d = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = alloc_workspace(lib().exact_attention_backward_workspace_bytes(n, H), q.device)
+    check(lib().exact_attention_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                         _ptr(dq), _ptr(dk), _ptr(dv), n, d, H, int(causal),
+                                         _dtype_code(q), _ptr(ws), ws.numel(),
+                                         _stream(q.device)))
+    return dq.reshape(shape), dk.reshape(shape), dv.reshape(shape)
+
+
+class HyperAttentionFunction(torch.autograd.Function):
+    """torch.autograd wrapper: forward and backward both run in the library.
+
+    HyperAttentionFunction.apply(q, k, v, causal, b, m, r, recursion_base, seed).
+    """
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal, b, m, r, recursion_base, seed):
+        o, lse = forward(q, k, v, causal=causal, b=b, m=m, r=r, recursion_base=recursion_base,
+                         seed=seed, return_lse=True)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.args = dict(causal=causal, b=b, m=m, r=r, recursion_base=recursion_base, seed=seed)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), **ctx.args)
+        return dq, dk, dv, None, None, None, None, None, None
+
+
 def rowsum_estimate(q, k, *, b=256, m=256, r=8, seed=0):
     """log d~ per row (Algorithm 2, non-causal)."""
     shape, q, k, _ = _qkv(q, k)

@@ -279,6 +279,85 @@ int rowsum_estimate(const void* Q, const void* K, int64_t n, int d, int heads, i
   return launch_bucket_attention(p, Q, K, nullptr, nullptr, log_d, workspace, s);
 }
 
+size_t hyperattn_backward_workspace_bytes(int64_t n, int d, int heads, int causal, int b, int m,
+                                          int recursion_base, int r, int dtype) {
+  g_error.clear();
+  Plan p;
+  if (make_plan(p, n, d, heads, causal, b, m, recursion_base, r, dtype, true, true) != HA_OK)
+    return 0;
+  return p.total;
+}
+
+int hyperattn_backward(const void* Q, const void* K, const void* V, const void* O,
+                       const float* lse, const void* dO, void* dQ, void* dK, void* dV, int64_t n,
+                       int d, int heads, int causal, int b, int m, int recursion_base, int r,
+                       uint64_t seed, int dtype, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  g_error.clear();
+  Plan p;
+  int rc = make_plan(p, n, d, heads, causal, b, m, recursion_base, r, dtype, true, true);
+  if (rc != HA_OK) return rc;
+  if (n == 0 || heads == 0) return HA_OK;
+  if (!Q || !K || !V || !O || !lse || !dO || !dQ || !dK || !dV)
+    return fail(HA_ERR_NULL, "Q, K, V, O, lse, dO, dQ, dK and dV must not be NULL");
+  rc = check_workspace(p, workspace, workspace_bytes);
+  if (rc != HA_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(workspace);
+  float* delta = reinterpret_cast<float*>(w + p.off[HA_WS_DELTA]);
+  const BwdIO io{Q, K, V, dO, lse, delta, dQ, dK, dV};
+  if ((rc = launch_delta(O, dO, delta, n * heads, d, s)) != HA_OK) return rc;
+  if (p.causal && p.L == 0)   // the whole sequence is one base block
+    return launch_bwd_exact(io, n, d, heads, 1, n, nullptr, nullptr, s);
+  // the forward pass's buckets and sample lists, recomputed from the seed
+  const float* G = nullptr;
+  const uint16_t* Gb = nullptr;
+  if ((rc = device_hyperplanes(seed, heads, r, d, &G, &Gb)) != HA_OK) return rc;
+  if ((rc = launch_hash(p, Q, K, V, G, Gb, workspace, s)) != HA_OK) return rc;
+  if ((rc = launch_vnorm_scan(p, workspace, s)) != HA_OK) return rc;
+  if ((rc = launch_sort(p, workspace, 2, s)) != HA_OK) return rc;
+  if ((rc = launch_samples(p, seed, workspace, s)) != HA_OK) return rc;
+  if ((rc = launch_bwd_links(p, workspace, s)) != HA_OK) return rc;
+  if ((rc = launch_bwd_samples(p, io, workspace, s)) != HA_OK) return rc;
+  if ((rc = launch_bwd_bucket(p, io, workspace, s)) != HA_OK) return rc;
+  if (p.causal) rc = launch_bwd_exact(io, n, d, heads, 1, p.base_block, &p, workspace, s);
+  return rc;
+}
+
+size_t exact_attention_backward_workspace_bytes(int64_t n, int heads) {
+  g_error.clear();
+  if (n < 0 || heads < 0) return 0;
+  return size_t(align256(n * heads * 4));
+}
+
+int exact_attention_backward(const void* Q, const void* K, const void* V, const void* O,
+                             const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                             int64_t n, int d, int heads, int causal, int dtype, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  g_error.clear();
+  if (dtype != HA_BF16) return fail(HA_ERR_UNSUPPORTED, "the backward pass takes bf16 tensors only");
+  if (d != 64 && d != 128) return fail(HA_ERR_UNSUPPORTED, "d=%d not 64 or 128", d);
+  if (n < 0 || n >= (int64_t(1) << 31)) return fail(HA_ERR_SHAPE, "n=%lld out of range", (long long)n);
+  if (heads < 0 || heads >= (1 << 16)) return fail(HA_ERR_SHAPE, "heads=%d out of range", heads);
+  if (n * d * 2 >= (int64_t(1) << 31))
+    return fail(HA_ERR_SHAPE, "one head of n=%lld rows exceeds 2 GiB", (long long)n);
+  if (n == 0 || heads == 0) return HA_OK;
+  if (!Q || !K || !V || !O || !lse || !dO || !dQ || !dK || !dV)
+    return fail(HA_ERR_NULL, "Q, K, V, O, lse, dO, dQ, dK and dV must not be NULL");
+  const size_t need = size_t(align256(n * heads * 4));
+  if (!workspace) return fail(HA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(HA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(HA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* delta = static_cast<float*>(workspace);
+  const BwdIO io{Q, K, V, dO, lse, delta, dQ, dK, dV};
+  int rc = launch_delta(O, dO, delta, n * heads, d, s);
+  if (rc != HA_OK) return rc;
+  return launch_bwd_exact(io, n, d, heads, causal ? 1 : 0, n, nullptr, nullptr, s);
+}
+
 size_t sortlsh_hash_workspace_bytes(int64_t n, int heads, int with_perm) {
   g_error.clear();
   if (n < 0 || heads < 0) return 0;

@@ -66,6 +66,12 @@ struct Level {
   int u_cnt;
   int v_cap;
   float alpha;
+  // Backward pass: the gradient of the node's sample slots (uniform list
+  // then V-norm list, u_cnt + v_cap slots) is computed by items of kAttnQ
+  // slots times kBwdQChunk query positions.
+  int smp_nsc;        // slot chunks per node
+  int64_t smp_nqc;    // query chunks per node
+  int64_t smp_wg0;    // first sample-slot item of this level
 };
 
 struct LevelTable {
@@ -88,6 +94,8 @@ struct Plan {
   int64_t sort_wgs = 0;       // sort chunk work-groups (all levels/heads/sides)
   int64_t seg_wgs = 0;        // per-segment work-groups (all levels/heads/sides)
   int64_t att_wgs = 0;        // bucket attention work-groups
+  bool backward = false;      // workspace of the backward pass
+  int64_t smp_wgs = 0;        // sample-slot gradient items (backward)
   LevelTable table{};
   int64_t off[HA_WS_COUNT] = {};
   int64_t bytes[HA_WS_COUNT] = {};
@@ -97,9 +105,11 @@ struct Plan {
 constexpr int kVnormBlock = 256;     // rows per V-norm work-group
 constexpr int kAttnQ = 256;          // query rows per attention work-group
 constexpr int kQueues = 8;           // work queues of the persistent attention kernels (one per XCD)
+constexpr int kBwdQChunk = 8192;     // query positions per sample-slot gradient item
+constexpr int kBwdMaxM = 2048;       // largest m of the backward pass (slot lists staged in LDS)
 
 int make_plan(Plan& p, int64_t n, int d, int heads, int causal, int b, int m,
-              int base, int r, int dtype, bool product);
+              int base, int r, int dtype, bool product, bool backward = false);
 int check_workspace(const Plan& p, const void* ws, size_t ws_bytes);
 
 // Hyperplanes on the device for (seed, heads, r, d); cached per device.
@@ -139,6 +149,37 @@ int launch_exact(const void* Q, const void* K, const void* V, void* O, float* ls
                  int64_t block, const Plan* merge, const void* ws, hipStream_t s);
 
 size_t sort_single_scratch_bytes(int64_t n, int heads);
+
+// ------------------------------------------------------------ backward pass
+// Inputs and outputs of one backward call (device pointers, bf16 tensors
+// [heads][n][d]; lse and delta fp32 [heads][n]).
+struct BwdIO {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* dO;
+  const float* lse;       // final log-normaliser of each row (forward output)
+  const float* delta;     // dO_i . O_i (launch_delta's output)
+  void* dQ;
+  void* dK;
+  void* dV;
+};
+// delta[row] = sum_t O[row][t] dO[row][t] for rows * d elements (bf16)
+int launch_delta(const void* O, const void* dO, float* delta, int64_t rows, int d,
+                 hipStream_t s);
+// Per node: which sample slots share a key row (first slot per key row of the
+// node, next slot with the same row).
+int launch_bwd_links(const Plan& p, void* ws, hipStream_t s);
+// Gradient of every sample slot's key and value rows, partial per query chunk.
+int launch_bwd_samples(const Plan& p, const BwdIO& io, void* ws, hipStream_t s);
+// dQ of every bucket's queries, and dK, dV of every bucket's keys plus the
+// node's sample slots on those rows: per-level partials (causal) or the
+// outputs (non-causal).
+int launch_bwd_bucket(const Plan& p, const BwdIO& io, void* ws, hipStream_t s);
+// Exact attention's gradients over key/query blocks of `block` rows; with
+// merge, the base case of the causal recursion, adding every level's partials.
+int launch_bwd_exact(const BwdIO& io, int64_t n, int d, int heads, int causal, int64_t block,
+                     const Plan* merge, const void* ws, hipStream_t s);
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -21,7 +21,7 @@ int64_t add_region(Plan& p, int id, int64_t bytes) {
 }  // namespace
 
 int make_plan(Plan& p, int64_t n, int d, int heads, int causal, int b, int m,
-              int base, int r, int dtype, bool product) {
+              int base, int r, int dtype, bool product, bool backward) {
   p = Plan();
   if (dtype != HA_F32 && dtype != HA_BF16)
     return fail(HA_ERR_UNSUPPORTED, "dtype %d is not HA_F32 (0) or HA_BF16 (1)", dtype);
@@ -40,9 +40,13 @@ int make_plan(Plan& p, int64_t n, int d, int heads, int causal, int b, int m,
     return fail(HA_ERR_SHAPE, "sample count m=%d out of range [1, 2^24)", m);
   if (causal && base < 1)
     return fail(HA_ERR_SHAPE, "recursion_base=%d must be >= 1", base);
+  if (backward && dtype != HA_BF16)
+    return fail(HA_ERR_UNSUPPORTED, "the backward pass takes bf16 tensors only");
+  if (backward && m > kBwdMaxM)
+    return fail(HA_ERR_UNSUPPORTED, "the backward pass takes m <= %d (m=%d)", kBwdMaxM, m);
 
   p.n = n; p.d = d; p.heads = heads; p.causal = causal ? 1 : 0; p.b = b; p.m = m;
-  p.base = base; p.r = r; p.dtype = dtype; p.product = product;
+  p.base = base; p.r = r; p.dtype = dtype; p.product = product; p.backward = backward;
   p.esize = dtype == HA_BF16 ? 2 : 4;
   if (n == 0 || heads == 0) return HA_OK;
 
@@ -94,6 +98,10 @@ int make_plan(Plan& p, int64_t n, int d, int heads, int causal, int b, int m,
     v.alpha = exhaustive ? 1.f : static_cast<float>(double(v.h) / double(m));
     v.att_wg0 = p.att_wgs;
     p.att_wgs += int64_t(heads) * v.nseg * v.nbucket * v.att_qch;
+    v.smp_nsc = static_cast<int>(ceil_div(v.u_cnt + v.v_cap, kAttnQ));
+    v.smp_nqc = ceil_div(v.h, kBwdQChunk);
+    v.smp_wg0 = p.smp_wgs;
+    p.smp_wgs += int64_t(heads) * v.nseg * v.smp_nsc * v.smp_nqc;
   }
   p.vblocks = ceil_div(n, kVnormBlock);
 
@@ -121,11 +129,23 @@ int make_plan(Plan& p, int64_t n, int d, int heads, int causal, int b, int m,
     add_region(p, HA_WS_V_W, samples * 4);
   }
   add_region(p, HA_WS_NODE_META, H * p.nodes * 16);
-  if (product && p.causal && p.L > 0) {
+  if (product && p.causal && p.L > 0 && !backward) {
     add_region(p, HA_WS_PART_O, slots * d * p.esize);
     add_region(p, HA_WS_PART_LSE, slots * 4);
   }
   add_region(p, HA_WS_SCHED, 2 * kQueues * 4);
+  if (backward) {
+    add_region(p, HA_WS_DELTA, H * n * 4);
+    if (p.causal && p.L > 0) {
+      add_region(p, HA_WS_PART_DQ, slots * d * 4);
+      add_region(p, HA_WS_PART_DK, slots * d * 4);
+      add_region(p, HA_WS_PART_DV, slots * d * 4);
+    }
+    add_region(p, HA_WS_SLOT_FIRST, slots * 4);
+    add_region(p, HA_WS_SLOT_NEXT, H * p.nodes * 2 * m * 4);
+    add_region(p, HA_WS_SLOT_DK, p.smp_wgs * kAttnQ * d * 4);
+    add_region(p, HA_WS_SLOT_DV, p.smp_wgs * kAttnQ * d * 4);
+  }
   return HA_OK;
 }
 

@@ -7,7 +7,7 @@ Recipe (numpy only, deterministic):
 
 * Every (data seed, tensor, head) triple has its own PCG64 stream that draws
   float64 standard normals of shape [n, d]. Tensor ids: Q = 0, K = 1, V = 2,
-  planting = 3.
+  planting = 3, the output gradient dO of the backward pass = 4.
 * Optional planting of heavy entries (the 8-head, n = 8192 workload): queries
   are visited in index order; each picks 4 distinct keys uniformly at random
   and overwrites them with 3 sqrt(d) q / ||q|| plus N(0, 0.1^2) noise per
@@ -70,7 +70,7 @@ WORKLOADS = {
 
 HEADLINE = "longctx_causal_n131072_d128_h32_bf16"
 
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_PLANT = 0, 1, 2, 3
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_PLANT, TENSOR_DO = 0, 1, 2, 3, 4
 
 
 def normals(data_seed, tensor, head, n, d):
@@ -141,6 +141,19 @@ def make_inputs(w, heads=None):
         q, k, v, p = make_head(w, h)
         Qs.append(q), Ks.append(k), Vs.append(v), P.append(p)
     return np.stack(Qs), np.stack(Ks), np.stack(Vs), P
+
+
+def make_grad(w, heads=None):
+    """Output gradients dO [H, n, d] for the backward pass: standard normals,
+    rounded like the inputs."""
+    hs = range(w.heads) if heads is None else heads
+    out = []
+    for h in hs:
+        x32 = normals(w.data_seed, TENSOR_DO, h, w.n, w.d).astype(np.float32)
+        if w.dtype == "bf16":
+            x32 = bf16_bits_to_f32(f32_to_bf16_bits(x32))
+        out.append(x32)
+    return np.stack(out)
 
 
 def make_inputs_parallel(w, heads=None, workers=None):

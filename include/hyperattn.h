@@ -182,6 +182,66 @@ int rowsum_estimate(const void* Q, const void* K, int64_t n, int d, int heads,
                     void* stream);
 
 /*
+ * hyperattn_backward — gradients of hyperattn_forward's output: dQ, dK, dV
+ * of the loss L = sum(dO * O) for the O that hyperattn_forward returns with
+ * the same arguments. The HA page times the forward and backward passes
+ * together ("Single self-attention layer") but states no formula; this is
+ * the exact derivative of the forward pass's estimator with its buckets,
+ * sample lists and sample weights held fixed (they are piecewise constant in
+ * Q, K and V). Row i's output is O_i = N_i / Z_i, where
+ * N_i = sum_j w_ij e^{s_ij} V_j and Z_i = sum_j u_ij e^{s_ij} run over the
+ * key slots row i evaluates. The slot weights (w, u) are:
+ *   a bucket or base-case key         (1, 1)
+ *   a uniform sample                  (0, n_k/m)
+ *   a V-norm sample                   (its weight, 0)
+ *   a sample inside the query's bucket (0, 0)
+ * With E_ij = e^{s_ij - lse_i} and Delta_i = dO_i . O_i:
+ *   ds_ij = E_ij (w_ij dO_i . V_j - u_ij Delta_i),
+ *   dV_j += w_ij E_ij dO_i,
+ *   dQ_i += ds_ij K_j / sqrt(d),
+ *   dK_j += ds_ij Q_i / sqrt(d).
+ * A key drawn several times counts once per draw.
+ * Q, K, V, dO: inputs [heads][n][d] bf16. O and lse: hyperattn_forward's
+ * outputs for these inputs and arguments (lse is required).
+ * dQ, dK, dV: outputs [heads][n][d] bf16.
+ * The buckets and samples are recomputed from `seed` on the device, so the
+ * arguments must be those of the forward call. Accumulation is in fp32, and
+ * every sum runs in a fixed order with no atomics, so results are
+ * deterministic.
+ * bf16 only (HA_ERR_UNSUPPORTED for HA_F32), m <= 2048; other arguments and
+ * errors as hyperattn_forward.
+ * workspace: >= hyperattn_backward_workspace_bytes(...) with the same
+ * arguments. It is larger than the forward's: it holds per-level fp32
+ * partial gradients and the sample slots' partial gradients.
+ */
+int hyperattn_backward(const void* Q, const void* K, const void* V,
+                       const void* O, const float* lse, const void* dO,
+                       void* dQ, void* dK, void* dV, int64_t n, int d,
+                       int heads, int causal, int b, int m,
+                       int recursion_base, int r, uint64_t seed, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+size_t hyperattn_backward_workspace_bytes(int64_t n, int d, int heads,
+                                          int causal, int b, int m,
+                                          int recursion_base, int r,
+                                          int dtype);
+
+/*
+ * exact_attention_backward — gradients of exact_attention_forward (HA page,
+ * "Method overview"; causal: mask M^C): with P = D^-1 A and Delta_i =
+ * dO_i . O_i, dV = P^T dO, dS = P (dO V^T - Delta 1^T), dQ = dS K / sqrt(d),
+ * dK = dS^T Q / sqrt(d). O and lse are the forward call's outputs (lse
+ * required). bf16 only. workspace: >=
+ * exact_attention_backward_workspace_bytes(n, heads) bytes (Delta).
+ */
+int exact_attention_backward(const void* Q, const void* K, const void* V,
+                             const void* O, const float* lse, const void* dO,
+                             void* dQ, void* dK, void* dV, int64_t n, int d,
+                             int heads, int causal, int dtype,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+size_t exact_attention_backward_workspace_bytes(int64_t n, int heads);
+
+/*
  * sortlsh_hyperplanes — host-only: the r Gaussian hyperplanes per head the
  * hash uses (HA page, "Algorithm", Definition 1; hash family as read here).
  * G_host[h][k][t] (fp32 holding a bf16 value) = Box-Muller normal from two
@@ -220,6 +280,9 @@ int sortlsh_hyperplanes(uint64_t seed, int heads, int r, int d, float* G_host);
  *                                 V-norm count, alpha (float bits), b_eff
  *   HA_WS_SCHED                   uint32 [2][8] work-queue counters of the
  *                                 attention kernels (scratch, reset by each call)
+ *   HA_WS_DELTA ... HA_WS_SLOT_DV backward pass only (hyperattn_backward's
+ *                                 workspace; bytes 0 in the forward layout):
+ *                                 HA_WS_DELTA float [heads][n] = dO_i . O_i
  * The hyperplanes themselves are not in the workspace: the library keeps
  * them per device, keyed by (seed, heads, r, d); sortlsh_hyperplanes returns
  * the same values on the host.
@@ -233,6 +296,8 @@ enum ha_ws_region {
   HA_WS_NODE_META,
   HA_WS_PART_O, HA_WS_PART_LSE,
   HA_WS_SCHED,
+  HA_WS_DELTA, HA_WS_PART_DQ, HA_WS_PART_DK, HA_WS_PART_DV,
+  HA_WS_SLOT_FIRST, HA_WS_SLOT_NEXT, HA_WS_SLOT_DK, HA_WS_SLOT_DV,
   HA_WS_COUNT
 };
 int hyperattn_workspace_layout(int64_t n, int d, int heads, int causal, int b,

@@ -1,0 +1,131 @@
+"""GPU parity of the backward pass: the library's gradients through its C ABI
+against the oracle's (oracle.backward) on the shared seeded inputs.
+
+Tolerance: the gradients are bf16 outputs of bf16 inputs with fp32
+accumulation, compared as max |g - g_ref| / max |g_ref| per head against the
+bf16 bound of gpu_util.TOL. The library differentiates its own forward
+output (bf16 O, fp32 lse), the oracle its fp64 one.
+"""
+
+import numpy as np
+import pytest
+
+from approximate_softmax_attention_amd import workloads as wl
+from oracle import backward as obw
+from tests.gpu_util import TOL, banner, max_rel, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _api():
+    from approximate_softmax_attention_amd import api
+    return api
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _errs(grads, refs):
+    return [max_rel(to_np(g), r) for g, r in zip(grads, refs)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [77, 300])
+def test_exact_backward(d, causal, n):
+    banner(f"exact backward d={d} causal={causal} n={n}")
+    w = wl.scaled(wl.WORKLOADS["single_head_noncausal_n1024_d64_fp32"], heads=2, n=n, d=d,
+                  dtype="bf16")
+    Q, K, V, _ = wl.make_inputs(w)
+    dO = wl.make_grad(w)
+    api = _api()
+    q, k, v, do = (to_dev(x, "bf16") for x in (Q, K, V, dO))
+    o, lse = api.exact(q, k, v, causal=causal, return_lse=True)
+    grads = api.exact_backward(q, k, v, o, lse, do, causal=causal)
+    _sync()
+    refs = [np.stack([obw.exact_attention_backward(Q[h], K[h], V[h], dO[h], causal=causal)[i]
+                      for h in range(2)]) for i in range(3)]
+    errs = _errs(grads, refs)
+    print(f"  dQ {errs[0]:.2e} dK {errs[1]:.2e} dV {errs[2]:.2e}", flush=True)
+    assert max(errs) <= TOL["bf16"], errs
+
+
+BACKWARD_CASES = {
+    # non-causal, samples smaller than n, d = 64
+    "noncausal_d64": ("planted_noncausal_n8192_d64_h8_bf16",
+                      dict(heads=2, n=1024, b=128, m=128, planted=0)),
+    # causal, two levels and a base case, d = 128
+    "causal_d128": ("chatglm2_causal_n32768_d128_h32_bf16",
+                    dict(heads=2, n=2048, b=128, m=128, recursion_base=512, rope=False)),
+    # causal, three levels, the last one with exhaustive samples (m >= n_k)
+    "causal_exhaustive": ("chatglm2_causal_n32768_d128_h32_bf16",
+                          dict(heads=1, n=1024, d=64, b=64, m=200, recursion_base=128,
+                               rope=False)),
+    # the local block mask (r = 0)
+    "local_mask": ("planted_noncausal_n8192_d64_h8_bf16",
+                   dict(heads=2, n=1024, b=128, m=64, r=0, planted=0)),
+    # buckets of 512 rows: two query / key chunks per bucket
+    "wide_bucket": ("longctx_noncausal_n131072_d64_h8_bf16",
+                    dict(heads=1, n=2048, d=128, b=512, m=256)),
+    # 16384 rows: the sample slots' gradient takes two query chunks
+    "two_query_chunks": ("longctx_noncausal_n131072_d64_h8_bf16",
+                         dict(heads=1, n=16384, b=256, m=256)),
+}
+
+
+def _run_case(name, zero_v_half=False):
+    base, changes = BACKWARD_CASES[name]
+    w = wl.scaled(wl.WORKLOADS[base], **changes)
+    Q, K, V, _ = wl.make_inputs(w)
+    if zero_v_half:
+        V[:, : w.n // 2] = 0.0
+    dO = wl.make_grad(w)
+    api = _api()
+    q, k, v, do = (to_dev(x, "bf16") for x in (Q, K, V, dO))
+    kw = dict(causal=w.causal, b=w.b, m=w.m, r=w.r, recursion_base=w.recursion_base,
+              seed=w.method_seed)
+    o, lse = api.forward(q, k, v, return_lse=True, **kw)
+    grads = api.backward(q, k, v, o, lse, do, **kw)
+    _sync()
+    refs = obw.hyperattention_backward(Q, K, V, dO, causal=w.causal, b=w.b, m=w.m, r=w.r,
+                                       recursion_base=w.recursion_base, seed=w.method_seed)
+    return w, (q, k, v, o, lse, do, kw), grads, refs
+
+
+@pytest.mark.parametrize("name", list(BACKWARD_CASES))
+def test_hyperattention_backward(name):
+    banner(f"hyperattention backward {name}")
+    _, _, grads, refs = _run_case(name)
+    errs = _errs(grads, refs)
+    print(f"  dQ {errs[0]:.2e} dK {errs[1]:.2e} dV {errs[2]:.2e}", flush=True)
+    assert max(errs) <= TOL["bf16"], errs
+
+
+def test_backward_empty_vnorm_list():
+    """V rows [0, n/2) all zero: the first level's node draws no V-norm
+    sample, so its keys get no product gradient from samples."""
+    banner("hyperattention backward with an empty V-norm list")
+    _, _, grads, refs = _run_case("causal_exhaustive", zero_v_half=True)
+    errs = _errs(grads, refs)
+    print(f"  dQ {errs[0]:.2e} dK {errs[1]:.2e} dV {errs[2]:.2e}", flush=True)
+    assert max(errs) <= TOL["bf16"], errs
+
+
+def test_backward_deterministic_and_autograd():
+    """Two calls give the same bytes, and the autograd wrapper returns them."""
+    banner("hyperattention backward determinism and autograd")
+    import torch
+    _, (q, k, v, o, lse, do, kw), grads, _ = _run_case("causal_d128")
+    api = _api()
+    again = api.backward(q, k, v, o, lse, do, **kw)
+    qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+    out = api.HyperAttentionFunction.apply(qa, ka, va, kw["causal"], kw["b"], kw["m"], kw["r"],
+                                           kw["recursion_base"], kw["seed"])
+    out.backward(do)
+    _sync()
+    assert torch.equal(out.detach(), o)
+    for g, h, t in zip(grads, again, (qa, ka, va)):
+        assert torch.equal(g, h)
+        assert torch.equal(g, t.grad)
