@@ -132,12 +132,14 @@ def rope_table(n, d, rope_base=10000.0):
     return T
 
 
-def exact(q, k, v, *, causal=False, return_lse=False, out=None):
+def exact(q, k, v, *, causal=False, return_lse=False, out=None, lse_out=None):
     """Exact softmax attention (the library's own kernel)."""
     shape, q, k, v = _qkv(q, k, v)
     H, n, d = q.shape
     o = out if out is not None else torch.empty_like(q)
-    lse = torch.empty((H, n), dtype=torch.float32, device=q.device) if return_lse else None
+    lse = lse_out
+    if return_lse and lse is None:
+        lse = torch.empty((H, n), dtype=torch.float32, device=q.device)
     check(lib().exact_attention_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), n, d, H,
                                         int(causal), _dtype_code(q), _stream(q.device)))
     o = o.reshape(shape)

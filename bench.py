@@ -215,6 +215,108 @@ def rope_mode(args, torch, api, wl):
                       "kernels": kernels}), flush=True)
 
 
+def backward_flops(w):
+    """MFMA flops the backward pass must do (the products the gradient
+    formulas need, counted once), per kernel group: per query row of a level,
+    the bucket's keys need S, dP, dQ, dK, dV (5 products of 2bd), the uniform
+    sample S, dQ, dK (3 of 2md) and the V-norm sample all five; the base case
+    needs the five products over its causal half."""
+    H, n, d, b, m = w.heads, w.n, w.d, w.b, w.m
+    out = {}
+    if w.causal:
+        L, size = 0, n
+        while size > w.recursion_base:
+            size //= 2
+            L += 1
+        lv_flops = 0.0
+        for lv in range(L):
+            h = n >> (lv + 1)
+            be, mm = min(b, h), min(m, h)
+            lv_flops += (n // 2) * 2 * d * (5 * be + 8 * mm)
+        out["levels"] = H * lv_flops
+        out["base"] = H * (n // size) * 5 * 2.0 * d * size * (size + 1) / 2
+    else:
+        be, mm = min(b, n), min(m, n)
+        out["levels"] = H * n * 2 * d * (5 * be + 8 * mm)
+    return out
+
+
+def backward_mode(args, torch, api, wl):
+    """The headline workload's forward and backward pass (the HA page times
+    forward + backward in its single-layer experiment), with exact attention's
+    forward + backward beside it; one JSON line with the per-kernel
+    breakdown."""
+    w = wl.WORKLOADS[args.workload or wl.HEADLINE]
+    log(f"workload {w.name}: generating inputs")
+    Q, K, V = make_device_inputs(w, torch)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4)
+    dO = torch.randn(Q.shape, device="cuda", dtype=Q.dtype, generator=g)
+    kw = dict(causal=w.causal, b=w.b, m=w.m, r=w.r, recursion_base=w.recursion_base,
+              seed=w.method_seed)
+    wsf = api.alloc_workspace(api.workspace_bytes(w.n, w.d, w.heads, causal=w.causal, b=w.b,
+                                                  m=w.m, r=w.r,
+                                                  recursion_base=w.recursion_base), "cuda")
+    wsb = api.alloc_workspace(api.backward_workspace_bytes(w.n, w.d, w.heads, causal=w.causal,
+                                                           b=w.b, m=w.m, r=w.r,
+                                                           recursion_base=w.recursion_base),
+                              "cuda")
+    O = torch.empty_like(Q)
+    lse = torch.empty((w.heads, w.n), dtype=torch.float32, device="cuda")
+
+    def step():
+        api.forward(Q, K, V, workspace=wsf, out=O, lse_out=lse, return_lse=True, **kw)
+        return api.backward(Q, K, V, O, lse, dO, workspace=wsb, **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with api.KernelTimer() as kt:
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    kernels = {k: {"launches": n, "avg_ms": t / n} for k, (n, t) in kt.stats.items()}
+    fl = backward_flops(w)
+    groups = {"levels": ("bwd_sample_kv", "bwd_bucket_q", "bwd_bucket_kv"),
+              "base": ("bwd_base_q", "bwd_base_kv")}
+    mfma = {}
+    for grp, names in groups.items():
+        t = sum(kernels.get(k, {}).get("avg_ms", 0.0) for k in names)
+        if grp in fl and t > 0:
+            mfma[grp] = {"tflops": fl[grp] / (t / 1e3) / 1e12,
+                         "frac": fl[grp] / (t / 1e3) / PEAK_BF16}
+    bwd_ms = sum(v["avg_ms"] for k, v in kernels.items() if k.startswith("bwd_")) + sum(
+        kernels.get(k, {}).get("avg_ms", 0.0) for k in ("hash", "vnorm_rows", "vnorm_weights",
+                                                          "vnorm_prefix", "sort_hist",
+                                                          "sort_offsets", "sort_scatter",
+                                                          "samples")) / 2
+    rec = {"mode": "forward_backward", "workload": w.name, "steps": args.steps,
+           "ms_per_step": ms, "tokens_per_s": w.n / (ms / 1e3), "kernels": kernels,
+           "backward_ms_approx": bwd_ms, "backward_mfma": mfma}
+    if not args.no_exact:
+        Oe = torch.empty_like(Q)
+        le = torch.empty_like(lse)
+
+        def exact_step():
+            api.exact(Q, K, V, causal=w.causal, out=Oe, lse_out=le, return_lse=True)
+            return api.exact_backward(Q, K, V, Oe, le, dO, causal=w.causal)
+
+        exact_step()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        exact_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rec["exact_ms_per_step"] = e0.elapsed_time(e1)
+        rec["speedup_vs_exact"] = rec["exact_ms_per_step"] / ms
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,6 +332,9 @@ def main():
     ap.add_argument("--rope", action="store_true",
                     help="time the headline workload with RoPE applied by the library "
                          "(hyperattn_forward_rope on the rows before RoPE); one JSON line")
+    ap.add_argument("--backward", action="store_true",
+                    help="time forward + backward on the headline workload (and exact "
+                         "attention's forward + backward); one JSON line")
     ap.add_argument("--sweep-heads", type=int, default=12)
     ap.add_argument("--sweep-d", type=int, default=64)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -252,6 +357,9 @@ def main():
         return
     if args.rope:
         rope_mode(args, torch, api, wl)
+        return
+    if args.backward:
+        backward_mode(args, torch, api, wl)
         return
 
     w = wl.WORKLOADS[args.workload or wl.HEADLINE]
