@@ -271,38 +271,58 @@ __device__ __forceinline__ void q_tile(const BwdBuf<D>& b, const LaneOffs<bf16_t
 }
 
 // -------------------------------------------------------- key-major tiles
+// Passes of the key-major loops: dV, dK or both at once. With d = 128 the K,
+// V, dK and dV fragments of 32 key slots do not fit the 256 registers of a
+// wave at two waves per SIMD, so those kernels sweep the queries twice (dV,
+// then dK) and hold only what each sweep needs.
+enum { PASS_V = 1, PASS_K = 2, PASS_KV = 3 };
+template <int D> struct KvPasses {
+  static constexpr bool kSplit = D == 128;
+};
+
 // One LDS tile of queries for the wave's 32 key slots (weights om, nu):
-// dV^T += dO^T (w E), dK^T += Q^T dS. Rows without a query carry
+// dV^T += dO^T (w E) and/or dK^T += Q^T dS. Rows without a query carry
 // t.w = +inf (E = 0). kCausal: query index r valid iff r >= lim;
 // kBucketMask: valid iff the query's bucket differs from the slot's.
-template <int D, bool kCausal, bool kBucketMask>
+// use_dp: some slot of the wave has om != 0 (else dP is not needed).
+template <int D, bool kCausal, bool kBucketMask, int PASS>
 __device__ __forceinline__ void kv_tile(const BwdBuf<D>& b, const LaneOffs<bf16_t, D>& lo,
                                         const QFrag<bf16_t, D>& kf, const QFrag<bf16_t, D>& vf,
                                         f32x16* dk, f32x16* dv, float c, float om, float nu,
-                                        int bkt, int nvalid, int lim, int skip_below) {
+                                        int bkt, bool use_dp, int nvalid, int lim,
+                                        int skip_below) {
   const int g = lane_id() >> 5;
 #pragma unroll
   for (int qb = 0; qb < KT / 32; ++qb) {
     if (32 * qb >= nvalid) break;
     if (kCausal && 32 * qb + 31 < skip_below) continue;   // the wave's keys all follow
     const f32x16 s = tile_dot<D>(b.t.k, lo, kf, qb);
-    const f32x16 dp = tile_dot<D>(b.t.v, lo, vf, qb);
-    float pv[16], pk[16];
+    f32x16 dp = zero16();
+    if ((PASS & PASS_K) && use_dp) dp = tile_dot<D>(b.t.v, lo, vf, qb);
+    float e[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = key_of(qb, i, g);
       bool ok = true;
       if (kCausal) ok = r >= lim;
       if (kBucketMask) ok = ok && b.tag[r] != bkt;
-      const float e = ok ? fast_exp2(fmaf(s[i], c, -b.t.w[r])) : 0.f;
-      pv[i] = om * e;
-      pk[i] = e * (om * dp[i] - nu * b.w2[r]);
+      e[i] = ok ? fast_exp2(fmaf(s[i], c, -b.t.w[r])) : 0.f;
     }
     bf16x8_t pb[2];
-    pack_bf16(pv, pb);
-    tile_tr_acc<D>(b.t.v, lo, dv, pb, qb);
-    pack_bf16(pk, pb);
-    tile_tr_acc<D>(b.t.k, lo, dk, pb, qb);
+    if (PASS & PASS_V) {
+      float pv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pv[i] = om * e[i];
+      pack_bf16(pv, pb);
+      tile_tr_acc<D>(b.t.v, lo, dv, pb, qb);
+    }
+    if (PASS & PASS_K) {
+      float pk[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pk[i] = e[i] * (om * dp[i] - nu * b.w2[key_of(qb, i, g)]);
+      pack_bf16(pk, pb);
+      tile_tr_acc<D>(b.t.k, lo, dk, pb, qb);
+    }
   }
 }
 
@@ -388,6 +408,62 @@ __device__ __forceinline__ void q_exact_item(const BwdArgs& a, BwdSmem<D>& sm, u
   store_row_bf16<D>(dq, a.dQ + (int64_t(head) * a.n + qrow) * D);
 }
 
+// One sweep of the block's queries [q_lo, b_hi) for the wave's keys.
+template <int D, bool kCausal, int PASS>
+__device__ __forceinline__ void kv_exact_sweep(const BwdArgs& a, BwdSmem<D>& sm, int head,
+                                               int64_t q_lo, int64_t b_hi, int64_t kw0,
+                                               int64_t krow, const QFrag<bf16_t, D>& kf,
+                                               const QFrag<bf16_t, D>& vf, f32x16* dk,
+                                               f32x16* dv) {
+  const auto Qr = rsrc_of(a.Q, head, a.n, D);
+  const auto dOr = rsrc_of(a.dO, head, a.n, D);
+  LaneOffs<bf16_t, D> lo;
+  lo.init();
+  const int ntiles = int((b_hi - q_lo + KT - 1) / KT);
+  const float* lse = a.lse + int64_t(head) * a.n;
+  const float* dl = a.delta + int64_t(head) * a.n;
+  Pipe<bf16_t, D> pipe;
+  auto issue = [&](int t) {
+    const int64_t r0 = q_lo + int64_t(t) * KT;
+    const int nv = int(b_hi - r0 < KT ? b_hi - r0 : KT);
+    BwdBuf<D>& b = sm.buf[t & 1];
+    pipe.issue(b.t, Qr, dOr, true, [&](int row) { return row < nv ? int(r0 + row) : -1; },
+               [&](int row) { return row < nv ? lse[r0 + row] * kLog2e : INFINITY; });
+    if ((PASS & PASS_K) && threadIdx.x < KT)
+      b.w2[threadIdx.x] = int(threadIdx.x) < nv ? dl[r0 + threadIdx.x] : 0.f;
+  };
+  issue(0);
+  pipe.commit(sm.buf[0].t, true);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) issue(t + 1);
+    const int64_t r0 = q_lo + int64_t(t) * KT;
+    const int nvalid = int(b_hi - r0 < KT ? b_hi - r0 : KT);
+    // causal: query r0 + r is valid for key krow iff r >= krow - r0
+    const int64_t dk0 = (krow >= 0 ? krow : kw0) - r0;
+    const int lim = dk0 < 0 ? 0 : (dk0 > KT ? KT : int(dk0));
+    const int64_t sb = kw0 - r0;
+    const int skip_below = sb < 0 ? 0 : (sb > KT ? KT : int(sb));
+    kv_tile<D, kCausal, false, PASS>(sm.buf[t & 1], lo, kf, vf, dk, dv, a.scale_log2, 1.f, 1.f,
+                                     0, true, nvalid, lim, skip_below);
+    if (t + 1 < ntiles) pipe.commit(sm.buf[(t + 1) & 1].t, true);
+    __syncthreads();
+  }
+}
+
+// Adds the level partials of key row krow (base block blk) and stores it.
+template <int D>
+__device__ __forceinline__ void finish_exact_key(const BwdArgs& a, f32x16* acc, bool is_k,
+                                                 uint32_t blk, int64_t b_lo, int64_t krow,
+                                                 int head) {
+  if (is_k) scale_acc<D>(acc, a.scale);
+  for (int lv = 0; lv < a.merge_levels; ++lv) {
+    const int64_t idx = level_slot(a, lv, blk, b_lo, krow, false, head);
+    if (idx >= 0) add_row_f32<D>(acc, (is_k ? a.part_dk : a.part_dv) + idx * D);
+  }
+  store_row_bf16<D>(acc, (is_k ? a.dK : a.dV) + (int64_t(head) * a.n + krow) * D);
+}
+
 // dK, dV of key tile t (kAttnQ keys) against the block's queries (causal:
 // the queries at or after the tile's first key).
 template <int D, bool kCausal>
@@ -406,61 +482,30 @@ __device__ __forceinline__ void kv_exact_item(const BwdArgs& a, BwdSmem<D>& sm, 
   const int ql = lane_id() & 31;
   const int64_t kw0 = k0 + wave * kQW;
   const int64_t krow = kw0 + ql < k_end ? kw0 + ql : -1;
-
-  const auto Qr = rsrc_of(a.Q, head, a.n, D);
+  const int64_t q_lo = kCausal ? k0 : b_lo;
   const auto Kr = rsrc_of(a.K, head, a.n, D);
   const auto Vr = rsrc_of(a.V, head, a.n, D);
-  const auto dOr = rsrc_of(a.dO, head, a.n, D);
   QFrag<bf16_t, D> kf, vf;
   load_q<bf16_t, D>(kf, Kr, krow);
-  load_q<bf16_t, D>(vf, Vr, krow);
-  LaneOffs<bf16_t, D> lo;
-  lo.init();
-  f32x16 dk[D / 32], dv[D / 32];
-  zero_acc<D>(dk);
-  zero_acc<D>(dv);
-
-  const int64_t q_lo = kCausal ? k0 : b_lo;
-  const int ntiles = int((b_hi - q_lo + KT - 1) / KT);
-  const float* lse = a.lse + int64_t(head) * a.n;
-  const float* dl = a.delta + int64_t(head) * a.n;
-  Pipe<bf16_t, D> pipe;
-  auto issue = [&](int t) {
-    const int64_t r0 = q_lo + int64_t(t) * KT;
-    const int nv = int(b_hi - r0 < KT ? b_hi - r0 : KT);
-    BwdBuf<D>& b = sm.buf[t & 1];
-    pipe.issue(b.t, Qr, dOr, true, [&](int row) { return row < nv ? int(r0 + row) : -1; },
-               [&](int row) { return row < nv ? lse[r0 + row] * kLog2e : INFINITY; });
-    if (threadIdx.x < KT) b.w2[threadIdx.x] = int(threadIdx.x) < nv ? dl[r0 + threadIdx.x] : 0.f;
-  };
-  issue(0);
-  pipe.commit(sm.buf[0].t, true);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) issue(t + 1);
-    const int64_t r0 = q_lo + int64_t(t) * KT;
-    const int nvalid = int(b_hi - r0 < KT ? b_hi - r0 : KT);
-    // causal: query r0 + r is valid for key krow iff r >= krow - r0
-    const int64_t dk0 = (krow >= 0 ? krow : kw0) - r0;
-    const int lim = dk0 < 0 ? 0 : (dk0 > KT ? KT : int(dk0));
-    const int64_t sb = kw0 - r0;
-    const int skip_below = sb < 0 ? 0 : (sb > KT ? KT : int(sb));
-    kv_tile<D, kCausal, false>(sm.buf[t & 1], lo, kf, vf, dk, dv, a.scale_log2, 1.f, 1.f, 0,
-                               nvalid, lim, skip_below);
-    if (t + 1 < ntiles) pipe.commit(sm.buf[(t + 1) & 1].t, true);
-    __syncthreads();
+  if constexpr (KvPasses<D>::kSplit) {
+    f32x16 acc[D / 32];
+    zero_acc<D>(acc);
+    kv_exact_sweep<D, kCausal, PASS_V>(a, sm, head, q_lo, b_hi, kw0, krow, kf, vf, nullptr, acc);
+    if (krow >= 0) finish_exact_key<D>(a, acc, false, blk, b_lo, krow, head);
+    load_q<bf16_t, D>(vf, Vr, krow);
+    zero_acc<D>(acc);
+    kv_exact_sweep<D, kCausal, PASS_K>(a, sm, head, q_lo, b_hi, kw0, krow, kf, vf, acc, nullptr);
+    if (krow >= 0) finish_exact_key<D>(a, acc, true, blk, b_lo, krow, head);
+  } else {
+    load_q<bf16_t, D>(vf, Vr, krow);
+    f32x16 dk[D / 32], dv[D / 32];
+    zero_acc<D>(dk);
+    zero_acc<D>(dv);
+    kv_exact_sweep<D, kCausal, PASS_KV>(a, sm, head, q_lo, b_hi, kw0, krow, kf, vf, dk, dv);
+    if (krow < 0) return;
+    finish_exact_key<D>(a, dv, false, blk, b_lo, krow, head);
+    finish_exact_key<D>(a, dk, true, blk, b_lo, krow, head);
   }
-  if (krow < 0) return;
-  scale_acc<D>(dk, a.scale);
-  for (int lv = 0; lv < a.merge_levels; ++lv) {
-    const int64_t idx = level_slot(a, lv, blk, b_lo, krow, false, head);
-    if (idx >= 0) {
-      add_row_f32<D>(dk, a.part_dk + idx * D);
-      add_row_f32<D>(dv, a.part_dv + idx * D);
-    }
-  }
-  store_row_bf16<D>(dk, a.dK + (int64_t(head) * a.n + krow) * D);
-  store_row_bf16<D>(dv, a.dV + (int64_t(head) * a.n + krow) * D);
 }
 
 // ------------------------------------------------------ bucket item decode
@@ -645,15 +690,16 @@ __device__ __forceinline__ void fill_queries(const BwdArgs& a, BwdSmem<D>& sm, c
   }
 }
 
-// Key-major loop over `count` queries at sorted positions [p0, p0 + count)
+// Key-major sweep over `count` queries at sorted positions [p0, p0 + count)
 // of `perm` for the wave's key slots. kMask: a query in bucket bkt (its
 // position / b_eff) is skipped.
-template <int D, bool kMask>
+template <int D, bool kMask, int PASS>
 __device__ __forceinline__ void kv_sorted_loop(const BwdArgs& a, BwdSmem<D>& sm,
                                                const int32_t* perm, int64_t p0, int64_t count,
                                                int b_eff, int head, const QFrag<bf16_t, D>& kf,
                                                const QFrag<bf16_t, D>& vf, f32x16* dk,
-                                               f32x16* dv, float om, float nu, int bkt) {
+                                               f32x16* dv, float om, float nu, int bkt,
+                                               bool use_dp) {
   constexpr int kWin = kSlotCap / KT;
   const auto Qr = rsrc_of(a.Q, head, a.n, D);
   const auto dOr = rsrc_of(a.dO, head, a.n, D);
@@ -667,7 +713,7 @@ __device__ __forceinline__ void kv_sorted_loop(const BwdArgs& a, BwdSmem<D>& sm,
     pipe.issue(b.t, Qr, dOr, true, [&](int row) { return int(sm.srow[e0 + row]); },
                [&](int row) { return sm.sw[e0 + row]; });
     if (threadIdx.x < KT) {
-      b.w2[threadIdx.x] = sm.sw2[e0 + threadIdx.x];
+      if (PASS & PASS_K) b.w2[threadIdx.x] = sm.sw2[e0 + threadIdx.x];
       if (kMask) b.tag[threadIdx.x] = int32_t((p0 + int64_t(t) * KT + threadIdx.x) / b_eff);
     }
   };
@@ -686,22 +732,45 @@ __device__ __forceinline__ void kv_sorted_loop(const BwdArgs& a, BwdSmem<D>& sm,
     }
     const int64_t left = count - int64_t(t) * KT;
     const int nvalid = int(left < KT ? left : KT);
-    kv_tile<D, false, kMask>(sm.buf[t & 1], lo, kf, vf, dk, dv, a.scale_log2, om, nu, bkt, nvalid,
-                             0, 0);
+    kv_tile<D, false, kMask, PASS>(sm.buf[t & 1], lo, kf, vf, dk, dv, a.scale_log2, om, nu, bkt,
+                                   use_dp, nvalid, 0, 0);
     if (t + 1 < ntiles) pipe.commit(sm.buf[(t + 1) & 1].t, true);
     __syncthreads();
   }
 }
 
+// Adds the node's sample slots drawn on key row krow (their partials over
+// every query chunk, slots in increasing order) to the row's dK (is_k) or
+// dV, then stores it: a level partial (causal) or the output.
+template <int D>
+__device__ __forceinline__ void finish_bucket_key(const BwdArgs& a, const BucketItem& it,
+                                                  f32x16* acc, bool is_k, int64_t krow) {
+  const Level& L = a.table.lv[it.lv];
+  const int64_t h = L.h;
+  if (is_k) scale_acc<D>(acc, a.scale);
+  const int64_t k_lo = a.table.causal ? 2 * it.seg * h : 0;
+  const int64_t kslot = (int64_t(it.lv) * a.heads + it.head) * a.S + it.seg * h + (krow - k_lo);
+  const int64_t nqc = L.smp_nqc;
+  const int64_t item0 = L.smp_wg0 + (int64_t(it.head) * L.nseg + it.seg) * L.smp_nsc * nqc;
+  const float* part = is_k ? a.slot_dk : a.slot_dv;
+  for (int t = a.slot_first[kslot]; t >= 0; t = a.slot_next[it.rec * 2 * a.m + t]) {
+    const int64_t sc = t / kAttnQ;
+    const int tt = t - int(sc) * kAttnQ;
+    for (int64_t qc = 0; qc < nqc; ++qc)
+      add_row_f32<D>(acc, part + ((item0 + sc * nqc + qc) * kAttnQ + tt) * D);
+  }
+  if (a.table.causal)
+    store_row_f32<D>(acc, (is_k ? a.part_dk : a.part_dv) + kslot * D);
+  else
+    store_row_bf16<D>(acc, (is_k ? a.dK : a.dV) + (int64_t(it.head) * a.n + krow) * D);
+}
+
 // dK, dV of one bucket chunk's keys against the bucket's queries, plus the
-// sample slots of the node drawn on these key rows (their partials over
-// every query chunk, slots in increasing order).
+// node's sample slots drawn on these key rows.
 template <int D>
 __device__ __forceinline__ void kv_bucket_item(const BwdArgs& a, BwdSmem<D>& sm, int64_t w) {
   const BucketItem it = decode_bucket(a, w);
-  const Level& L = a.table.lv[it.lv];
-  const int b_eff = L.b_eff;
-  const int64_t h = L.h;
+  const int b_eff = a.table.lv[it.lv].b_eff;
   const int wave = threadIdx.x >> 6;
   const int ql = lane_id() & 31;
   const int64_t ki = it.chunk * kAttnQ + wave * kQW + ql;
@@ -710,36 +779,27 @@ __device__ __forceinline__ void kv_bucket_item(const BwdArgs& a, BwdSmem<D>& sm,
   const auto Vr = rsrc_of(a.V, it.head, a.n, D);
   QFrag<bf16_t, D> kf, vf;
   load_q<bf16_t, D>(kf, Kr, krow);
-  load_q<bf16_t, D>(vf, Vr, krow);
-  f32x16 dk[D / 32], dv[D / 32];
-  zero_acc<D>(dk);
-  zero_acc<D>(dv);
-  kv_sorted_loop<D, false>(a, sm, a.perm_q, it.slot0, b_eff, b_eff, it.head, kf, vf, dk, dv, 1.f,
-                           1.f, 0);
-  if (krow < 0) return;
-  scale_acc<D>(dk, a.scale);
-  // the node's sample slots on this key row
-  const int64_t k_lo = a.table.causal ? 2 * it.seg * h : 0;
-  const int64_t kslot = (int64_t(it.lv) * a.heads + it.head) * a.S + it.seg * h + (krow - k_lo);
-  int t = a.slot_first[kslot];
-  const int64_t nqc = L.smp_nqc;
-  const int64_t item0 = L.smp_wg0 + (int64_t(it.head) * L.nseg + it.seg) * L.smp_nsc * nqc;
-  while (t >= 0) {
-    const int64_t sc = t / kAttnQ;
-    const int tt = t - int(sc) * kAttnQ;
-    for (int64_t qc = 0; qc < nqc; ++qc) {
-      const int64_t idx = (item0 + sc * nqc + qc) * kAttnQ + tt;
-      add_row_f32<D>(dk, a.slot_dk + idx * D);
-      add_row_f32<D>(dv, a.slot_dv + idx * D);
-    }
-    t = a.slot_next[it.rec * 2 * a.m + t];
-  }
-  if (a.table.causal) {
-    store_row_f32<D>(dk, a.part_dk + kslot * D);
-    store_row_f32<D>(dv, a.part_dv + kslot * D);
+  if constexpr (KvPasses<D>::kSplit) {
+    f32x16 acc[D / 32];
+    zero_acc<D>(acc);
+    kv_sorted_loop<D, false, PASS_V>(a, sm, a.perm_q, it.slot0, b_eff, b_eff, it.head, kf, vf,
+                                     nullptr, acc, 1.f, 1.f, 0, true);
+    if (krow >= 0) finish_bucket_key<D>(a, it, acc, false, krow);
+    load_q<bf16_t, D>(vf, Vr, krow);
+    zero_acc<D>(acc);
+    kv_sorted_loop<D, false, PASS_K>(a, sm, a.perm_q, it.slot0, b_eff, b_eff, it.head, kf, vf,
+                                     acc, nullptr, 1.f, 1.f, 0, true);
+    if (krow >= 0) finish_bucket_key<D>(a, it, acc, true, krow);
   } else {
-    store_row_bf16<D>(dk, a.dK + (int64_t(it.head) * a.n + krow) * D);
-    store_row_bf16<D>(dv, a.dV + (int64_t(it.head) * a.n + krow) * D);
+    load_q<bf16_t, D>(vf, Vr, krow);
+    f32x16 dk[D / 32], dv[D / 32];
+    zero_acc<D>(dk);
+    zero_acc<D>(dv);
+    kv_sorted_loop<D, false, PASS_KV>(a, sm, a.perm_q, it.slot0, b_eff, b_eff, it.head, kf, vf,
+                                      dk, dv, 1.f, 1.f, 0, true);
+    if (krow < 0) return;
+    finish_bucket_key<D>(a, it, dv, false, krow);
+    finish_bucket_key<D>(a, it, dk, true, krow);
   }
 }
 
@@ -785,20 +845,44 @@ __device__ __forceinline__ void kv_sample_item(const BwdArgs& a, BwdSmem<D>& sm,
   const auto Vr = rsrc_of(a.V, head, a.n, D);
   QFrag<bf16_t, D> kf, vf;
   load_q<bf16_t, D>(kf, Kr, krow);
-  load_q<bf16_t, D>(vf, Vr, krow);
-  f32x16 dk[D / 32], dv[D / 32];
-  zero_acc<D>(dk);
-  zero_acc<D>(dv);
   const int64_t p0 = qc * kBwdQChunk;
   const int64_t count = h - p0 < kBwdQChunk ? h - p0 : kBwdQChunk;
   const int64_t seg0 = (int64_t(lv) * a.heads + head) * a.S + seg * h;
-  kv_sorted_loop<D, true>(a, sm, a.perm_q + seg0, p0, count, L.b_eff, head, kf, vf, dk, dv, om,
-                          nu, bkt);
-  if (krow < 0) return;
-  scale_acc<D>(dk, a.scale);
   const int64_t idx = w * kAttnQ + wave * kQW + ql;
-  store_row_f32<D>(dk, a.slot_dk + idx * D);
-  store_row_f32<D>(dv, a.slot_dv + idx * D);
+  const int32_t* perm = a.perm_q + seg0;
+  // uniform slots have om = 0: no dV and no dP for them
+  const bool wave_om = __ballot(om != 0.f) != 0;
+  if constexpr (KvPasses<D>::kSplit) {
+    f32x16 acc[D / 32];
+    // the work-group skips the dV sweep when none of its slots has om != 0
+    if (__syncthreads_or(om != 0.f)) {
+      zero_acc<D>(acc);
+      kv_sorted_loop<D, true, PASS_V>(a, sm, perm, p0, count, L.b_eff, head, kf, vf, nullptr,
+                                      acc, om, nu, bkt, wave_om);
+      if (krow >= 0) store_row_f32<D>(acc, a.slot_dv + idx * D);
+    } else if (krow >= 0) {
+      zero_acc<D>(acc);
+      store_row_f32<D>(acc, a.slot_dv + idx * D);
+    }
+    load_q<bf16_t, D>(vf, Vr, krow);
+    zero_acc<D>(acc);
+    kv_sorted_loop<D, true, PASS_K>(a, sm, perm, p0, count, L.b_eff, head, kf, vf, acc, nullptr,
+                                    om, nu, bkt, wave_om);
+    if (krow < 0) return;
+    scale_acc<D>(acc, a.scale);
+    store_row_f32<D>(acc, a.slot_dk + idx * D);
+  } else {
+    load_q<bf16_t, D>(vf, Vr, krow);
+    f32x16 dk[D / 32], dv[D / 32];
+    zero_acc<D>(dk);
+    zero_acc<D>(dv);
+    kv_sorted_loop<D, true, PASS_KV>(a, sm, perm, p0, count, L.b_eff, head, kf, vf, dk, dv, om,
+                                     nu, bkt, wave_om);
+    if (krow < 0) return;
+    scale_acc<D>(dk, a.scale);
+    store_row_f32<D>(dk, a.slot_dk + idx * D);
+    store_row_f32<D>(dv, a.slot_dv + idx * D);
+  }
 }
 
 // ------------------------------------------------------------------ kernels

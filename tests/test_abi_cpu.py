@@ -70,6 +70,44 @@ def test_forward_rope_validates_before_any_device_call():
     assert rc == -3
 
 
+def test_backward_validates_before_any_device_call():
+    lib = L()
+    p = _vp(256)
+    args = (1024, 64, 1, 0, 128, 128, 4096, 8, 1)
+    need = lib.hyperattn_backward_workspace_bytes(*args[:8], 1)
+    assert need > ws_bytes() > 0
+    # fp32 and large m are not taken by the backward pass
+    assert lib.hyperattn_backward_workspace_bytes(*args[:8], 0) == 0
+    assert "bf16" in _lib.last_error()
+    assert lib.hyperattn_backward_workspace_bytes(1024, 64, 1, 0, 128, 4096, 4096, 8, 1) == 0
+    assert "m <=" in _lib.last_error()
+    rc = lib.hyperattn_backward(p, p, p, p, None, p, p, p, p, 1024, 64, 1, 0, 128, 128, 4096, 8,
+                                1, 1, p, need, None)
+    assert rc == -1 and "lse" in _lib.last_error()
+    rc = lib.hyperattn_backward(p, p, p, p, p, p, p, p, p, 1024, 64, 1, 0, 128, 128, 4096, 8, 1,
+                                1, p, need - 1, None)
+    assert rc == -4
+    rc = lib.hyperattn_backward(p, p, p, p, p, p, p, p, p, 1000, 64, 1, 0, 128, 128, 4096, 8, 1,
+                                1, p, need, None)
+    assert rc == -2
+    assert lib.hyperattn_backward(None, None, None, None, None, None, None, None, None, 0, 64,
+                                  2, 1, 256, 256, 4096, 8, 1, 1, None, 0, None) == 0
+    assert lib.exact_attention_backward_workspace_bytes(300, 2) == 2560
+    rc = lib.exact_attention_backward(p, p, p, p, p, p, p, p, p, 300, 64, 2, 1, 0, p, 2560, None)
+    assert rc == -3
+    rc = lib.exact_attention_backward(p, p, p, p, p, p, p, p, p, 300, 64, 2, 1, 1, p, 2559, None)
+    assert rc == -4
+
+
+def test_backward_layout_regions():
+    from approximate_softmax_attention_amd import api
+    fwd = api.workspace_layout(8192, 128, 4, causal=1, b=256, m=256, recursion_base=1024)
+    assert fwd["DELTA"][1] == 0 and fwd["SLOT_DK"][1] == 0
+    # causal, 3 levels of 4096 slots per head: per-level partial gradients
+    need = L().hyperattn_backward_workspace_bytes(8192, 128, 4, 1, 256, 256, 1024, 8, 1)
+    assert need >= 3 * (3 * 4 * 4096 * 128 * 4)
+
+
 def test_zero_hyperplanes_allowed():
     from approximate_softmax_attention_amd import api
     assert api.hyperplanes(5, 3, 0, 64).shape == (3, 0, 64)
