@@ -143,3 +143,110 @@ def hyperattention_backward(Q, K, V, dO, *, causal, b, m, r=8, recursion_base=40
                 _add_slots(dQ[h], dK[h], dV[h], Qh[qs], Kh[v_idx], Vh[v_idx], qs, v_idx,
                            dOh[qs], lam[qs], delta[qs], w, np.zeros_like(w), scale)
     return dQ, dK, dV
+
+
+def hyperattention_backward_rows(Q, K, V, dO, q_rows, k_rows, *, causal, b, m, r=8,
+                                 recursion_base=4096, seed=0, G=None, head_ids=None):
+    """dQ at the query rows q_rows and dK, dV at the key rows k_rows, for
+    every head, by the formulas of hyperattention_backward restricted to the
+    slots those rows take part in (for problems too large to differentiate
+    in full). The forward output is computed for the query rows that the
+    requested gradients depend on.
+
+    Returns dQ [H, len(q_rows), d], dK and dV [H, len(k_rows), d] (fp64).
+    """
+    H, n, d = np.shape(Q)
+    scale = 1.0 / np.sqrt(d)
+    q_rows = np.asarray(q_rows, dtype=np.int64)
+    k_rows = np.asarray(k_rows, dtype=np.int64)
+    kw = dict(causal=causal, b=b, m=m, r=r, recursion_base=recursion_base, seed=seed, G=G,
+              head_ids=head_ids)
+    art = {}
+    ha.hyperattention(Q, K, V, rows=np.zeros(0, dtype=np.int64), artifacts=art, **kw)
+    dQ = np.zeros((H, len(q_rows), d))
+    dK = np.zeros((H, len(k_rows), d))
+    dV = np.zeros((H, len(k_rows), np.shape(V)[2]))
+    for h in range(H):
+        # query rows whose forward output the requested gradients need
+        need = set(q_rows.tolist())
+        for j in k_rows.tolist():
+            for lo, size in art["blocks"]:
+                if lo <= j < lo + size:
+                    need.update(range(j, lo + size))
+            for sub in art["sub"][h]:
+                k_lo, size, b_eff = sub["k_lo"], sub["size"], sub["b_eff"]
+                if not k_lo <= j < k_lo + size:
+                    continue
+                bk = sub["rank_k"][j - k_lo] // b_eff
+                need.update(sub["perm_q"][bk * b_eff:(bk + 1) * b_eff].tolist())
+                if j in sub["u_idx"] or j in sub["v_idx"]:
+                    need.update(range(sub["q_lo"], sub["q_lo"] + size))
+        rows = np.array(sorted(need), dtype=np.int64)
+        hk = dict(kw)
+        hk["head_ids"] = [h if head_ids is None else head_ids[h]]
+        hk["G"] = None if G is None else G[h:h + 1]
+        O, lse = ha.hyperattention(Q[h:h + 1], K[h:h + 1], V[h:h + 1], rows=rows, **hk)
+        O, lam = O[0], lse[0]
+        Qh, Kh, Vh, dOh = _as64(Q[h]), _as64(K[h]), _as64(V[h]), _as64(dO[h])
+        delta = np.full(n, np.nan)
+        delta[rows] = (dOh[rows] * O[rows]).sum(axis=1)
+
+        def contrib(qs, keys, w, u):
+            """(ds [len(qs), len(keys)], E) for query rows qs and key rows keys."""
+            E = np.exp((Qh[qs] @ Kh[keys].T) * scale - lam[qs][:, None])
+            ds = E * (w * (dOh[qs] @ Vh[keys].T) - u * delta[qs][:, None])
+            return ds, E
+
+        for t, i in enumerate(q_rows.tolist()):
+            for lo, size in art["blocks"]:
+                if lo <= i < lo + size:
+                    keys = np.arange(lo, i + 1)
+                    ds, _ = contrib([i], keys, 1.0, 1.0)
+                    dQ[h, t] += scale * ds[0] @ Kh[keys]
+            for sub in art["sub"][h]:
+                q_lo, size, b_eff = sub["q_lo"], sub["size"], sub["b_eff"]
+                if not q_lo <= i < q_lo + size:
+                    continue
+                pos = int(np.nonzero(sub["perm_q"] == i)[0][0])
+                bk = pos // b_eff
+                ks = sub["perm_k"][bk * b_eff:(bk + 1) * b_eff]
+                ds, _ = contrib([i], ks, 1.0, 1.0)
+                dQ[h, t] += scale * ds[0] @ Kh[ks]
+                u = sub["alpha"] * (sub["u_bucket"] != bk)
+                ds, _ = contrib([i], sub["u_idx"], 0.0, u[None, :])
+                dQ[h, t] += scale * ds[0] @ Kh[sub["u_idx"]]
+                wv = np.asarray(sub["v_w"], dtype=np.float64) * (sub["v_bucket"] != bk)
+                ds, _ = contrib([i], sub["v_idx"], wv[None, :], 0.0)
+                dQ[h, t] += scale * ds[0] @ Kh[sub["v_idx"]]
+
+        for t, j in enumerate(k_rows.tolist()):
+            for lo, size in art["blocks"]:
+                if lo <= j < lo + size:
+                    qs = np.arange(j, lo + size)
+                    ds, E = contrib(qs, [j], 1.0, 1.0)
+                    dK[h, t] += scale * ds[:, 0] @ Qh[qs]
+                    dV[h, t] += E[:, 0] @ dOh[qs]
+            for sub in art["sub"][h]:
+                q_lo, k_lo, size, b_eff = sub["q_lo"], sub["k_lo"], sub["size"], sub["b_eff"]
+                if not k_lo <= j < k_lo + size:
+                    continue
+                bk = sub["rank_k"][j - k_lo] // b_eff
+                qs = sub["perm_q"][bk * b_eff:(bk + 1) * b_eff]
+                ds, E = contrib(qs, [j], 1.0, 1.0)
+                dK[h, t] += scale * ds[:, 0] @ Qh[qs]
+                dV[h, t] += E[:, 0] @ dOh[qs]
+                # sample slots drawn on row j: every query of the node outside
+                # the slot's bucket
+                allq = sub["perm_q"]
+                qbk = np.arange(size) // b_eff
+                for slot in np.nonzero(sub["u_idx"] == j)[0]:
+                    keep = qbk != sub["u_bucket"][slot]
+                    ds, _ = contrib(allq[keep], [j], 0.0, sub["alpha"])
+                    dK[h, t] += scale * ds[:, 0] @ Qh[allq[keep]]
+                for slot in np.nonzero(sub["v_idx"] == j)[0]:
+                    keep = qbk != sub["v_bucket"][slot]
+                    wv = float(sub["v_w"][slot])
+                    ds, E = contrib(allq[keep], [j], wv, 0.0)
+                    dK[h, t] += scale * ds[:, 0] @ Qh[allq[keep]]
+                    dV[h, t] += wv * E[:, 0] @ dOh[allq[keep]]
+    return dQ, dK, dV

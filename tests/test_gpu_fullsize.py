@@ -60,3 +60,60 @@ def test_fullsize_sampled_rows_and_artifacts(name):
         assert err <= TOL[w.dtype]
         assert lerr <= TOL[w.dtype]
     assert np.isfinite(to_np(O)).all()
+
+
+def backward_rows(w, art, seed=11):
+    """Query rows over every level and base-block edge; key rows at random
+    plus keys drawn as samples at the first and the last level."""
+    rs = np.random.default_rng(seed)
+    q_rows = sample_rows(w, count=10, seed=seed)
+    k_rows = set(rs.choice(w.n, 6, replace=False).tolist()) | {0, w.n - 1}
+    subs = art["sub"][0]
+    for sub in (subs[0], subs[-1]):
+        k_rows |= set(sub["u_idx"][:1].tolist()) | set(sub["v_idx"][:1].tolist())
+    return q_rows, np.array(sorted(k_rows))
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_fullsize_backward_sampled_rows(name):
+    """hyperattn_backward at the full size (all heads in one call, as the
+    benchmark's --backward mode runs it): dQ on sampled query rows and dK, dV
+    on sampled key rows, among them keys drawn as samples, against the
+    oracle's row-restricted gradients."""
+    import torch
+
+    from approximate_softmax_attention_amd import api
+    from oracle import backward as obw
+    from tests.gpu_util import to_dev
+
+    w = wl.WORKLOADS[name]
+    banner(f"fullsize backward {name}: inputs")
+    Q, K, V, _ = wl.make_inputs_parallel(w)
+    dO = wl.make_grad(w)
+    kw = dict(causal=w.causal, b=w.b, m=w.m, r=w.r, recursion_base=w.recursion_base,
+              seed=w.method_seed)
+    banner(f"fullsize backward {name}: gpu forward + backward")
+    q, k, v, do = (to_dev(x, w.dtype) for x in (Q, K, V, dO))
+    o, lse = api.forward(q, k, v, return_lse=True, **kw)
+    grads = api.backward(q, k, v, o, lse, do, **kw)
+    torch.cuda.synchronize()
+    heads = [0, w.heads - 1]
+    art = {}
+    oha.hyperattention(Q[:1], K[:1], V[:1], rows=np.zeros(0, dtype=np.int64), artifacts=art,
+                       **kw)
+    q_rows, k_rows = backward_rows(w, art)
+    banner(f"fullsize backward {name}: oracle on heads {heads}, {len(q_rows)} query rows, "
+           f"{len(k_rows)} key rows")
+    rq, rk, rv = obw.hyperattention_backward_rows(Q[heads], K[heads], V[heads], dO[heads],
+                                                  q_rows, k_rows, head_ids=heads, **kw)
+    gq = to_np(grads[0][heads][:, q_rows])
+    gk = to_np(grads[1][heads][:, k_rows])
+    gv = to_np(grads[2][heads][:, k_rows])
+    for kk in range(len(heads)):
+        errs = [np.abs(g[kk] - r[kk]).max() / np.abs(r[kk]).max()
+                for g, r in ((gq, rq), (gk, rk), (gv, rv))]
+        print(f"{name} head {heads[kk]}: dQ {errs[0]:.2e} dK {errs[1]:.2e} dV {errs[2]:.2e}",
+              flush=True)
+        assert max(errs) <= TOL[w.dtype], errs
+    for g in grads:
+        assert torch.isfinite(g).all()

@@ -122,3 +122,23 @@ def test_reduces_to_exact_gradient():
             assert np.abs(a[h] - x).max() < 1e-12
         for a, x in zip(gc, ec):
             assert np.abs(a[h] - x).max() < 1e-12
+
+
+@pytest.mark.parametrize("kw", [c[1] for c in CASES])
+def test_row_gradients_equal_full_gradients(kw):
+    """The row-restricted gradients (used at full problem sizes) equal the
+    full backward pass's rows, including keys drawn as samples."""
+    rs = np.random.default_rng(21)
+    H, n, d = 2, 64, 8
+    Q, K, V, dO = (rs.standard_normal((H, n, d)) for _ in range(4))
+    art = {}
+    ha.hyperattention(Q, K, V, artifacts=art, **kw)
+    sampled = np.unique(np.concatenate([np.concatenate([s["u_idx"], s["v_idx"]])
+                                        for s in art["sub"][0]]))
+    q_rows = np.array([0, 5, 31, 32, 47, 63])
+    k_rows = np.unique(np.concatenate([[0, 17, 40, 63], sampled[:4]]))
+    gq, gk, gv = bw.hyperattention_backward_rows(Q, K, V, dO, q_rows, k_rows, **kw)
+    fq, fk, fv = bw.hyperattention_backward(Q, K, V, dO, **kw)
+    assert np.abs(gq - fq[:, q_rows]).max() < 1e-12 * max(1.0, np.abs(fq).max())
+    assert np.abs(gk - fk[:, k_rows]).max() < 1e-12 * max(1.0, np.abs(fk).max())
+    assert np.abs(gv - fv[:, k_rows]).max() < 1e-12 * max(1.0, np.abs(fv).max())
