@@ -35,6 +35,7 @@
 // the base case kernels add them to the rows of their diagonal blocks, as
 // the forward pass's base case merges partial outputs.
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 #include "device_util.h"
@@ -54,12 +55,11 @@ enum { SK_FULL = 0, SK_SUM = 1, SK_PROD = 2 };
 // One LDS tile: the rows of two tensors (t.k, t.v) and per-row scalars.
 // Query-major: K and V rows, t.w = w, w2 = u of each key slot.
 // Key-major: Q and dO rows, t.w = Lambda_i log2(e) (+inf for no row),
-// w2 = Delta_i, tag = the query's bucket (sample slots).
+// w2 = Delta_i.
 template <int D>
 struct BwdBuf {
   Buf<bf16_t, D> t;
   float w2[KT];
-  int32_t tag[KT];
 };
 
 template <int D>
@@ -117,8 +117,8 @@ struct BwdArgs {
 // rows of block kb of the tile array (A: tile rows from LDS, B: fragment).
 template <int D>
 __device__ __forceinline__ f32x16 tile_dot(const bf16_t* arr, const LaneOffs<bf16_t, D>& lo,
-                                           const QFrag<bf16_t, D>& f, int kb) {
-  f32x16 acc = zero16();
+                                           const QFrag<bf16_t, D>& f, int kb,
+                                           f32x16 acc = zero16()) {
   const char* base = reinterpret_cast<const char*>(arr) + kb * 32 * D * 2;
   __builtin_amdgcn_s_setprio(kMfmaPrio);
 #pragma unroll
@@ -151,6 +151,21 @@ __device__ __forceinline__ void tile_tr_acc(const bf16_t* arr, const LaneOffs<bf
     }
   }
   __builtin_amdgcn_s_setprio(0);
+}
+
+// The per-row values of block kb that this lane's accumulator elements
+// need: v[i] = arr[key_of(kb, i, g)], read as four 16-byte LDS loads.
+template <typename T>
+__device__ __forceinline__ void rows16(const T* arr, int kb, int g, T* v) {
+  static_assert(sizeof(T) == 4, "32-bit values");
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint4 x = *reinterpret_cast<const uint4*>(arr + 32 * kb + 8 * j + 4 * g);
+    v[4 * j] = __builtin_bit_cast(T, x.x);
+    v[4 * j + 1] = __builtin_bit_cast(T, x.y);
+    v[4 * j + 2] = __builtin_bit_cast(T, x.z);
+    v[4 * j + 3] = __builtin_bit_cast(T, x.w);
+  }
 }
 
 __device__ __forceinline__ void pack_bf16(const float* x, bf16x8_t* pb) {
@@ -247,6 +262,9 @@ __device__ __forceinline__ void q_tile(const BwdBuf<D>& b, const LaneOffs<bf16_t
 #pragma unroll
   for (int kb = 0; kb < KT / 32; ++kb) {
     if (masked && 32 * kb >= nvalid) break;
+    float wt[16];
+    if (KIND == SK_SUM) rows16(b.w2, kb, g, wt);
+    if (KIND == SK_PROD) rows16(b.t.w, kb, g, wt);
     const f32x16 s = tile_dot<D>(b.t.k, lo, qf, kb);
     f32x16 dp;
     if (KIND != SK_SUM) dp = tile_dot<D>(b.t.v, lo, df, kb);
@@ -259,10 +277,11 @@ __device__ __forceinline__ void q_tile(const BwdBuf<D>& b, const LaneOffs<bf16_t
         ok = r < nvalid;
         if (kCausal) ok = ok && r <= lim;
       }
-      const float e = ok ? fast_exp2(fmaf(s[i], c, -lam2)) : 0.f;
+      // masked entries take exp2(-inf) = 0 (a select, not a branch)
+      const float e = fast_exp2(ok ? fmaf(s[i], c, -lam2) : -INFINITY);
       if (KIND == SK_FULL) x[i] = e * (dp[i] - dlt);
-      else if (KIND == SK_SUM) x[i] = -(e * b.w2[r]) * dlt;
-      else x[i] = (e * b.t.w[r]) * dp[i];
+      else if (KIND == SK_SUM) x[i] = -(e * wt[i]) * dlt;
+      else x[i] = (e * wt[i]) * dp[i];
     }
     bf16x8_t pb[2];
     pack_bf16(x, pb);
@@ -282,31 +301,44 @@ template <int D> struct KvPasses {
 
 // One LDS tile of queries for the wave's 32 key slots (weights om, nu):
 // dV^T += dO^T (w E) and/or dK^T += Q^T dS. Rows without a query carry
-// t.w = +inf (E = 0). kCausal: query index r valid iff r >= lim;
-// kBucketMask: valid iff the query's bucket differs from the slot's.
+// t.w = +inf (E = 0). kUnit: om = nu = 1 (base case and bucket keys), when
+// dP's accumulator starts at -Delta so that it ends at dP - Delta and no
+// separate Delta values are held. kCausal: query index r valid iff r >= lim;
+// kBucketMask: valid iff r < mlo or r >= mhi (the tile rows inside the
+// slot's own bucket, a contiguous range since queries come in sorted order).
 // use_dp: some slot of the wave has om != 0 (else dP is not needed).
-template <int D, bool kCausal, bool kBucketMask, int PASS>
+template <int D, bool kCausal, bool kBucketMask, int PASS, bool kUnit>
 __device__ __forceinline__ void kv_tile(const BwdBuf<D>& b, const LaneOffs<bf16_t, D>& lo,
                                         const QFrag<bf16_t, D>& kf, const QFrag<bf16_t, D>& vf,
                                         f32x16* dk, f32x16* dv, float c, float om, float nu,
-                                        int bkt, bool use_dp, int nvalid, int lim,
+                                        int mlo, int mhi, bool use_dp, int nvalid, int lim,
                                         int skip_below) {
   const int g = lane_id() >> 5;
 #pragma unroll
   for (int qb = 0; qb < KT / 32; ++qb) {
     if (32 * qb >= nvalid) break;
     if (kCausal && 32 * qb + 31 < skip_below) continue;   // the wave's keys all follow
+    float lw[16], dl[16];
+    rows16(b.t.w, qb, g, lw);
+    if (PASS & PASS_K) rows16(b.w2, qb, g, dl);
     const f32x16 s = tile_dot<D>(b.t.k, lo, kf, qb);
     f32x16 dp = zero16();
-    if ((PASS & PASS_K) && use_dp) dp = tile_dot<D>(b.t.v, lo, vf, qb);
+    if (kUnit && (PASS & PASS_K)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dp[i] = -dl[i];
+      dp = tile_dot<D>(b.t.v, lo, vf, qb, dp);
+    } else if ((PASS & PASS_K) && use_dp) {
+      dp = tile_dot<D>(b.t.v, lo, vf, qb);
+    }
     float e[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = key_of(qb, i, g);
       bool ok = true;
       if (kCausal) ok = r >= lim;
-      if (kBucketMask) ok = ok && b.tag[r] != bkt;
-      e[i] = ok ? fast_exp2(fmaf(s[i], c, -b.t.w[r])) : 0.f;
+      if (kBucketMask) ok = ok && (r < mlo || r >= mhi);
+      // rows without a query carry +inf; masked entries take exp2(-inf) = 0
+      e[i] = fast_exp2(ok ? fmaf(s[i], c, -lw[i]) : -INFINITY);
     }
     bf16x8_t pb[2];
     if (PASS & PASS_V) {
@@ -319,7 +351,8 @@ __device__ __forceinline__ void kv_tile(const BwdBuf<D>& b, const LaneOffs<bf16_
     if (PASS & PASS_K) {
       float pk[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) pk[i] = e[i] * (om * dp[i] - nu * b.w2[key_of(qb, i, g)]);
+      for (int i = 0; i < 16; ++i)
+        pk[i] = kUnit ? e[i] * dp[i] : e[i] * (om * dp[i] - nu * dl[i]);
       pack_bf16(pk, pb);
       tile_tr_acc<D>(b.t.k, lo, dk, pb, qb);
     }
@@ -444,8 +477,8 @@ __device__ __forceinline__ void kv_exact_sweep(const BwdArgs& a, BwdSmem<D>& sm,
     const int lim = dk0 < 0 ? 0 : (dk0 > KT ? KT : int(dk0));
     const int64_t sb = kw0 - r0;
     const int skip_below = sb < 0 ? 0 : (sb > KT ? KT : int(sb));
-    kv_tile<D, kCausal, false, PASS>(sm.buf[t & 1], lo, kf, vf, dk, dv, a.scale_log2, 1.f, 1.f,
-                                     0, true, nvalid, lim, skip_below);
+    kv_tile<D, kCausal, false, PASS, true>(sm.buf[t & 1], lo, kf, vf, dk, dv, a.scale_log2, 1.f,
+                                           1.f, 0, 0, true, nvalid, lim, skip_below);
     if (t + 1 < ntiles) pipe.commit(sm.buf[(t + 1) & 1].t, true);
     __syncthreads();
   }
@@ -635,7 +668,9 @@ __device__ __forceinline__ void q_bucket_item(const BwdArgs& a, BwdSmem<D>& sm, 
   issue(0);
   pipe.commit(sm.buf[0].t, needs_v(0));
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
+  // one loop per segment, each with its own slot weights
+  auto step = [&](int t, auto kind) __attribute__((always_inline)) {
+    constexpr int KIND = decltype(kind)::value;
     if (t + 1 < ntiles) {
       if ((t + 1) % kWin == 0) {
         fill(t + 1);
@@ -644,19 +679,17 @@ __device__ __forceinline__ void q_bucket_item(const BwdArgs& a, BwdSmem<D>& sm, 
       issue(t + 1);
     }
     int j0, cnt;
-    const int sg = seg_of(t, j0, cnt);
+    seg_of(t, j0, cnt);
     const int nvalid = cnt - j0 < KT ? cnt - j0 : KT;
-    const BwdBuf<D>& b = sm.buf[t & 1];
-    if (sg == 0)
-      q_tile<D, SK_FULL, false>(b, lo, qf, df, dq, a.scale_log2, lam2, dlt, nvalid < KT, nvalid, KT);
-    else if (sg == 1)
-      q_tile<D, SK_SUM, false>(b, lo, qf, df, dq, a.scale_log2, lam2, dlt, nvalid < KT, nvalid, KT);
-    else
-      q_tile<D, SK_PROD, false>(b, lo, qf, df, dq, a.scale_log2, lam2, dlt, nvalid < KT, nvalid,
-                                KT);
+    q_tile<D, KIND, false>(sm.buf[t & 1], lo, qf, df, dq, a.scale_log2, lam2, dlt, nvalid < KT,
+                           nvalid, KT);
     if (t + 1 < ntiles) pipe.commit(sm.buf[(t + 1) & 1].t, needs_v(t + 1));
     __syncthreads();
-  }
+  };
+  int t = 0;
+  for (; t < t_b; ++t) step(t, std::integral_constant<int, SK_FULL>{});
+  for (; t < t_b + t_u; ++t) step(t, std::integral_constant<int, SK_SUM>{});
+  for (; t < ntiles; ++t) step(t, std::integral_constant<int, SK_PROD>{});
   if (qrow < 0) return;
   scale_acc<D>(dq, a.scale);
   if (a.table.causal) {
@@ -712,10 +745,7 @@ __device__ __forceinline__ void kv_sorted_loop(const BwdArgs& a, BwdSmem<D>& sm,
     BwdBuf<D>& b = sm.buf[t & 1];
     pipe.issue(b.t, Qr, dOr, true, [&](int row) { return int(sm.srow[e0 + row]); },
                [&](int row) { return sm.sw[e0 + row]; });
-    if (threadIdx.x < KT) {
-      if (PASS & PASS_K) b.w2[threadIdx.x] = sm.sw2[e0 + threadIdx.x];
-      if (kMask) b.tag[threadIdx.x] = int32_t((p0 + int64_t(t) * KT + threadIdx.x) / b_eff);
-    }
+    if ((PASS & PASS_K) && threadIdx.x < KT) b.w2[threadIdx.x] = sm.sw2[e0 + threadIdx.x];
   };
   fill_queries(a, sm, perm, p0, count, head);
   __syncthreads();
@@ -732,8 +762,18 @@ __device__ __forceinline__ void kv_sorted_loop(const BwdArgs& a, BwdSmem<D>& sm,
     }
     const int64_t left = count - int64_t(t) * KT;
     const int nvalid = int(left < KT ? left : KT);
-    kv_tile<D, false, kMask, PASS>(sm.buf[t & 1], lo, kf, vf, dk, dv, a.scale_log2, om, nu, bkt,
-                                   use_dp, nvalid, 0, 0);
+    // tile rows inside the slot's bucket: sorted positions
+    // [bkt b_eff, (bkt + 1) b_eff), clamped to the tile
+    int mlo = 0, mhi = 0;
+    if (kMask && bkt >= 0) {
+      const int64_t first = int64_t(bkt) * b_eff - (p0 + int64_t(t) * KT);
+      const int64_t last = first + b_eff;
+      mlo = int(first < 0 ? 0 : (first > KT ? KT : first));
+      mhi = int(last < 0 ? 0 : (last > KT ? KT : last));
+    }
+    // bucket keys (no mask) have om = nu = 1
+    kv_tile<D, false, kMask, PASS, !kMask>(sm.buf[t & 1], lo, kf, vf, dk, dv, a.scale_log2, om,
+                                           nu, mlo, mhi, use_dp, nvalid, 0, 0);
     if (t + 1 < ntiles) pipe.commit(sm.buf[(t + 1) & 1].t, true);
     __syncthreads();
   }
