@@ -306,9 +306,10 @@ int hyperattn_backward(const void* Q, const void* K, const void* V, const void* 
   char* w = static_cast<char*>(workspace);
   float* delta = reinterpret_cast<float*>(w + p.off[HA_WS_DELTA]);
   const BwdIO io{Q, K, V, dO, lse, delta, dQ, dK, dV};
+  uint32_t* queue = reinterpret_cast<uint32_t*>(w + p.off[HA_WS_SCHED]);
   if ((rc = launch_delta(O, dO, delta, n * heads, d, s)) != HA_OK) return rc;
   if (p.causal && p.L == 0)   // the whole sequence is one base block
-    return launch_bwd_exact(io, n, d, heads, 1, n, nullptr, nullptr, s);
+    return launch_bwd_exact(io, n, d, heads, 1, n, nullptr, nullptr, queue, s);
   // the forward pass's buckets and sample lists, recomputed from the seed
   const float* G = nullptr;
   const uint16_t* Gb = nullptr;
@@ -320,14 +321,14 @@ int hyperattn_backward(const void* Q, const void* K, const void* V, const void* 
   if ((rc = launch_bwd_links(p, workspace, s)) != HA_OK) return rc;
   if ((rc = launch_bwd_samples(p, io, workspace, s)) != HA_OK) return rc;
   if ((rc = launch_bwd_bucket(p, io, workspace, s)) != HA_OK) return rc;
-  if (p.causal) rc = launch_bwd_exact(io, n, d, heads, 1, p.base_block, &p, workspace, s);
+  if (p.causal) rc = launch_bwd_exact(io, n, d, heads, 1, p.base_block, &p, workspace, queue, s);
   return rc;
 }
 
 size_t exact_attention_backward_workspace_bytes(int64_t n, int heads) {
   g_error.clear();
   if (n < 0 || heads < 0) return 0;
-  return size_t(align256(n * heads * 4));
+  return size_t(align256(n * heads * 4) + 256);   // Delta, then the work-queue counters
 }
 
 int exact_attention_backward(const void* Q, const void* K, const void* V, const void* O,
@@ -344,7 +345,7 @@ int exact_attention_backward(const void* Q, const void* K, const void* V, const 
   if (n == 0 || heads == 0) return HA_OK;
   if (!Q || !K || !V || !O || !lse || !dO || !dQ || !dK || !dV)
     return fail(HA_ERR_NULL, "Q, K, V, O, lse, dO, dQ, dK and dV must not be NULL");
-  const size_t need = size_t(align256(n * heads * 4));
+  const size_t need = size_t(align256(n * heads * 4) + 256);
   if (!workspace) return fail(HA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if (reinterpret_cast<uintptr_t>(workspace) % 256)
     return fail(HA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
@@ -352,10 +353,12 @@ int exact_attention_backward(const void* Q, const void* K, const void* V, const 
     return fail(HA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* delta = static_cast<float*>(workspace);
+  uint32_t* queue = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
+                                                align256(n * heads * 4));
   const BwdIO io{Q, K, V, dO, lse, delta, dQ, dK, dV};
   int rc = launch_delta(O, dO, delta, n * heads, d, s);
   if (rc != HA_OK) return rc;
-  return launch_bwd_exact(io, n, d, heads, causal ? 1 : 0, n, nullptr, nullptr, s);
+  return launch_bwd_exact(io, n, d, heads, causal ? 1 : 0, n, nullptr, nullptr, queue, s);
 }
 
 size_t sortlsh_hash_workspace_bytes(int64_t n, int heads, int with_perm) {

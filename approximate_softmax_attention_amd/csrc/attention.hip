@@ -379,40 +379,6 @@ __device__ __forceinline__ void stage_row(const WaveState<T, D>& ws, char* st, i
     }
 }
 
-// Runs item_fn over this work-group's items: one (from the linear block
-// index, remapped so that neighbouring items share an XCD) when the launch
-// has no queue, else
-// items taken from the queues until all are done. item_fn must contain a
-// barrier before it returns.
-template <typename ItemFn>
-__device__ __forceinline__ void run_items(const AttnArgs& a, int64_t& s_item,
-                                          const ItemFn& item_fn) {
-  int qi = hw_xcc();
-  int64_t item;
-  if (!a.queue) {
-    item = xcd_remap(int64_t(blockIdx.y) * gridDim.x + blockIdx.x,
-                     int64_t(gridDim.x) * gridDim.y);
-  } else {
-    if (threadIdx.x == 0)
-      s_item = queue_resolve(a.queue, a.items, qi, atomicAdd(&a.queue[qi], 1u));
-    __syncthreads();
-    item = s_item;
-  }
-  while (item >= 0) {
-    uint32_t pre = 0;
-    if (a.queue && threadIdx.x == 0) pre = atomicAdd(&a.queue[qi], 1u);
-    item_fn(item);
-    if (!a.queue) break;
-    if (threadIdx.x == 0) s_item = queue_resolve(a.queue, a.items, qi, pre);
-    __syncthreads();
-    item = s_item;
-  }
-}
-
-__global__ void queue_reset_kernel(uint32_t* ctr) {
-  if (threadIdx.x < kQueues) ctr[threadIdx.x] = 0u;
-}
-
 // ------------------------------------------------------------- EXACT kernel
 // Work item lin = head * items_per_head + blk * tiles_per_block + t: query
 // tile t of key block blk. Causal tiles are taken from the longest (last) to
@@ -791,14 +757,6 @@ int launch_bucket_t(const AttnArgs& a, bool product, hipStream_t s) {
   dim3 grid;
   if (int rc = launch_grid(k, a, a.items, grid)) return rc;
   hipLaunchKernelGGL(k, grid, dim3(kThreads), 0, s, a);
-  return HA_OK;
-}
-
-// Zeroes a queue's counters (a kernel rather than a memset, so that the
-// sequence may be captured in a graph).
-int reset_queue(uint32_t* ctr, hipStream_t s) {
-  hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, s, ctr);
-  HA_LAUNCH_CHECK("queue_reset");
   return HA_OK;
 }
 

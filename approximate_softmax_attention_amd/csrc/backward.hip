@@ -68,6 +68,7 @@ struct BwdSmem {
   alignas(16) int32_t srow[kSlotCap];
   alignas(16) float sw[kSlotCap];
   alignas(16) float sw2[kSlotCap];
+  int64_t item;            // next work item (persistent launches)
 };
 
 struct BwdArgs {
@@ -109,7 +110,9 @@ struct BwdArgs {
   const int32_t* slot_next;    // [heads][nodes][2m]
   float* slot_dk;              // [sample items][kAttnQ][d]
   float* slot_dv;
-  int64_t items;
+  // work queue of a persistent launch
+  uint32_t* queue;             // [kQueues] counters, zero at launch
+  uint32_t items;              // total work items
 };
 
 // ------------------------------------------------------------ MFMA helpers
@@ -926,23 +929,45 @@ __device__ __forceinline__ void kv_sample_item(const BwdArgs& a, BwdSmem<D>& sm,
 }
 
 // ------------------------------------------------------------------ kernels
-template <int D, int MODE, bool kCausal>
+// kPersistent: the work-group takes items from the queues until all are
+// done; else it runs the one item of its (XCD-remapped) block index. The
+// two are separate instantiations because the item loop changes register
+// allocation (values hoisted out of it stay live across items).
+template <int D, int MODE, bool kCausal, bool kPersistent>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_q_kernel(BwdArgs a) {
   __shared__ BwdSmem<D> sm;
-  const int64_t item = xcd_remap(int64_t(blockIdx.x), int64_t(gridDim.x));
-  if (MODE == BW_EXACT) q_exact_item<D, kCausal>(a, sm, uint32_t(item));
-  else q_bucket_item<D>(a, sm, item);
+  auto item_fn = [&](int64_t item) __attribute__((always_inline)) {
+    if (MODE == BW_EXACT) q_exact_item<D, kCausal>(a, sm, uint32_t(item));
+    else q_bucket_item<D>(a, sm, item);
+  };
+  if constexpr (kPersistent) {
+    run_items(a, sm.item, [&](int64_t item) __attribute__((always_inline)) {
+      item_fn(item);
+      __syncthreads();
+    });
+  } else {
+    item_fn(xcd_remap(int64_t(blockIdx.x), int64_t(gridDim.x)));
+  }
 }
 
-template <int D, int MODE, bool kCausal>
+template <int D, int MODE, bool kCausal, bool kPersistent>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_kv_kernel(BwdArgs a) {
   __shared__ BwdSmem<D> sm;
-  const int64_t item = xcd_remap(int64_t(blockIdx.x), int64_t(gridDim.x));
-  if (MODE == BW_EXACT) kv_exact_item<D, kCausal>(a, sm, uint32_t(item));
-  else if (MODE == BW_BUCKET) kv_bucket_item<D>(a, sm, item);
-  else kv_sample_item<D>(a, sm, item);
+  auto item_fn = [&](int64_t item) __attribute__((always_inline)) {
+    if (MODE == BW_EXACT) kv_exact_item<D, kCausal>(a, sm, uint32_t(item));
+    else if (MODE == BW_BUCKET) kv_bucket_item<D>(a, sm, item);
+    else kv_sample_item<D>(a, sm, item);
+  };
+  if constexpr (kPersistent) {
+    run_items(a, sm.item, [&](int64_t item) __attribute__((always_inline)) {
+      item_fn(item);
+      __syncthreads();
+    });
+  } else {
+    item_fn(xcd_remap(int64_t(blockIdx.x), int64_t(gridDim.x)));
+  }
 }
 
 // delta[row] = O[row] . dO[row]: CPR lanes per row, 16 bytes each.
@@ -1040,6 +1065,7 @@ void plan_args(BwdArgs& a, const Plan& p, void* ws) {
   a.slot_next = reinterpret_cast<const int32_t*>(w + p.off[HA_WS_SLOT_NEXT]);
   a.slot_dk = reinterpret_cast<float*>(w + p.off[HA_WS_SLOT_DK]);
   a.slot_dv = reinterpret_cast<float*>(w + p.off[HA_WS_SLOT_DV]);
+  a.queue = reinterpret_cast<uint32_t*>(w + p.off[HA_WS_SCHED]);
   if (p.causal && p.L > 0) {
     a.part_dq = reinterpret_cast<float*>(w + p.off[HA_WS_PART_DQ]);
     a.part_dk = reinterpret_cast<float*>(w + p.off[HA_WS_PART_DK]);
@@ -1047,14 +1073,31 @@ void plan_args(BwdArgs& a, const Plan& p, void* ws) {
   }
 }
 
+// A launch of kernel k over `items` work items. persistent: one work-group
+// per resident slot (at most one per item) taking items from the queues,
+// whose counters are zeroed first; else one work-group per item in the
+// dispatcher's order. Measured on the long-context causal workload, the
+// queues help the sample-slot and base-case dQ launches (whose items differ
+// in length) and slow the others, so each launch chooses.
 template <typename Kern>
-int launch_items(Kern k, const BwdArgs& a, int64_t items, const char* name, hipStream_t s) {
+int launch_items(Kern k, BwdArgs a, int64_t items, bool persistent, const char* name,
+                 hipStream_t s) {
   if (items == 0) return HA_OK;
   if (items >= (int64_t(1) << 31))
     return fail(HA_ERR_SHAPE, "%lld work items of %s exceed the launch limit", (long long)items,
                 name);
+  a.items = uint32_t(items);
+  unsigned grid = a.items;
+  if (persistent) {
+    const int r = resident_groups(k);
+    if (r <= 0) return fail(HA_ERR_HIP, "could not query the device's occupancy");
+    if (int rc = reset_queue(a.queue, s)) return rc;
+    grid = unsigned(r) < a.items ? unsigned(r) : a.items;
+  } else {
+    a.queue = nullptr;
+  }
   ProfRange pr(name, s);
-  hipLaunchKernelGGL(k, dim3(unsigned(items)), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), 0, s, a);
   HA_LAUNCH_CHECK(name);
   return HA_OK;
 }
@@ -1091,26 +1134,26 @@ int launch_bwd_links(const Plan& p, void* ws, hipStream_t s) {
 int launch_bwd_samples(const Plan& p, const BwdIO& io, void* ws, hipStream_t s) {
   BwdArgs a = base_args(io, p.n, p.d, p.heads);
   plan_args(a, p, ws);
-  a.items = p.smp_wgs;
-  auto k = p.d == 128 ? bwd_kv_kernel<128, BW_SAMPLE, false> : bwd_kv_kernel<64, BW_SAMPLE, false>;
-  return launch_items(k, a, p.smp_wgs, "bwd_sample_kv", s);
+  auto k = p.d == 128 ? bwd_kv_kernel<128, BW_SAMPLE, false, true> : bwd_kv_kernel<64, BW_SAMPLE, false, true>;
+  return launch_items(k, a, p.smp_wgs, true, "bwd_sample_kv", s);
 }
 
 int launch_bwd_bucket(const Plan& p, const BwdIO& io, void* ws, hipStream_t s) {
   BwdArgs a = base_args(io, p.n, p.d, p.heads);
   plan_args(a, p, ws);
-  a.items = p.att_wgs;
-  auto kq = p.d == 128 ? bwd_q_kernel<128, BW_BUCKET, false> : bwd_q_kernel<64, BW_BUCKET, false>;
-  if (int rc = launch_items(kq, a, p.att_wgs, "bwd_bucket_q", s)) return rc;
+  auto kq = p.d == 128 ? bwd_q_kernel<128, BW_BUCKET, false, false> : bwd_q_kernel<64, BW_BUCKET, false, false>;
+  if (int rc = launch_items(kq, a, p.att_wgs, false, "bwd_bucket_q", s)) return rc;
   auto kkv =
-      p.d == 128 ? bwd_kv_kernel<128, BW_BUCKET, false> : bwd_kv_kernel<64, BW_BUCKET, false>;
-  return launch_items(kkv, a, p.att_wgs, "bwd_bucket_kv", s);
+      p.d == 128 ? bwd_kv_kernel<128, BW_BUCKET, false, false>
+                 : bwd_kv_kernel<64, BW_BUCKET, false, false>;
+  return launch_items(kkv, a, p.att_wgs, false, "bwd_bucket_kv", s);
 }
 
 int launch_bwd_exact(const BwdIO& io, int64_t n, int d, int heads, int causal, int64_t block,
-                     const Plan* merge, const void* ws, hipStream_t s) {
+                     const Plan* merge, const void* ws, uint32_t* queue, hipStream_t s) {
   BwdArgs a = base_args(io, n, d, heads);
   a.block = block;
+  a.queue = queue;
   const int64_t tpb = ceil_div(block, kAttnQ);
   const int64_t per_head = ceil_div(n, block) * tpb;
   const int64_t items = per_head * heads;
@@ -1133,19 +1176,19 @@ int launch_bwd_exact(const BwdIO& io, int64_t n, int d, int heads, int causal, i
   const char* nkv = merge ? "bwd_base_kv" : "bwd_exact_kv";
   int rc;
   if (d == 128) {
-    rc = launch_items(causal ? bwd_q_kernel<128, BW_EXACT, true> : bwd_q_kernel<128, BW_EXACT, false>,
-                      a, items, nq, s);
+    rc = launch_items(causal ? bwd_q_kernel<128, BW_EXACT, true, true> : bwd_q_kernel<128, BW_EXACT, false, true>,
+                      a, items, true, nq, s);
     if (!rc)
-      rc = launch_items(causal ? bwd_kv_kernel<128, BW_EXACT, true>
-                               : bwd_kv_kernel<128, BW_EXACT, false>,
-                        a, items, nkv, s);
+      rc = launch_items(causal ? bwd_kv_kernel<128, BW_EXACT, true, false>
+                               : bwd_kv_kernel<128, BW_EXACT, false, false>,
+                        a, items, false, nkv, s);
   } else {
-    rc = launch_items(causal ? bwd_q_kernel<64, BW_EXACT, true> : bwd_q_kernel<64, BW_EXACT, false>,
-                      a, items, nq, s);
+    rc = launch_items(causal ? bwd_q_kernel<64, BW_EXACT, true, true> : bwd_q_kernel<64, BW_EXACT, false, true>,
+                      a, items, true, nq, s);
     if (!rc)
-      rc = launch_items(causal ? bwd_kv_kernel<64, BW_EXACT, true>
-                               : bwd_kv_kernel<64, BW_EXACT, false>,
-                        a, items, nkv, s);
+      rc = launch_items(causal ? bwd_kv_kernel<64, BW_EXACT, true, false>
+                               : bwd_kv_kernel<64, BW_EXACT, false, false>,
+                        a, items, false, nkv, s);
   }
   return rc;
 }

@@ -178,8 +178,9 @@ int launch_bwd_samples(const Plan& p, const BwdIO& io, void* ws, hipStream_t s);
 int launch_bwd_bucket(const Plan& p, const BwdIO& io, void* ws, hipStream_t s);
 // Exact attention's gradients over key/query blocks of `block` rows; with
 // merge, the base case of the causal recursion, adding every level's partials.
+// queue: kQueues work-queue counters (device memory; zeroed here).
 int launch_bwd_exact(const BwdIO& io, int64_t n, int d, int heads, int causal, int64_t block,
-                     const Plan* merge, const void* ws, hipStream_t s);
+                     const Plan* merge, const void* ws, uint32_t* queue, hipStream_t s);
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -361,6 +361,50 @@ int resident_groups(Kern k) {
 }
 
 
+// Runs item_fn over this work-group's items: one (from the linear block
+// index, remapped so that neighbouring items share an XCD) when the launch
+// has no queue, else
+// items taken from the queues until all are done. item_fn must contain a
+// barrier before it returns.
+// Args: a launch's arguments with `queue` (counters, or null) and `items`.
+template <typename Args, typename ItemFn>
+__device__ __forceinline__ void run_items(const Args& a, int64_t& s_item,
+                                          const ItemFn& item_fn) {
+  int qi = hw_xcc();
+  int64_t item;
+  if (!a.queue) {
+    item = xcd_remap(int64_t(blockIdx.y) * gridDim.x + blockIdx.x,
+                     int64_t(gridDim.x) * gridDim.y);
+  } else {
+    if (threadIdx.x == 0)
+      s_item = queue_resolve(a.queue, a.items, qi, atomicAdd(&a.queue[qi], 1u));
+    __syncthreads();
+    item = s_item;
+  }
+  while (item >= 0) {
+    uint32_t pre = 0;
+    if (a.queue && threadIdx.x == 0) pre = atomicAdd(&a.queue[qi], 1u);
+    item_fn(item);
+    if (!a.queue) break;
+    if (threadIdx.x == 0) s_item = queue_resolve(a.queue, a.items, qi, pre);
+    __syncthreads();
+    item = s_item;
+  }
+}
+
+__global__ void queue_reset_kernel(uint32_t* ctr) {
+  if (threadIdx.x < kQueues) ctr[threadIdx.x] = 0u;
+}
+
+
+// Zeroes a queue's counters (a kernel rather than a memset, so that the
+// sequence may be captured in a graph).
+int reset_queue(uint32_t* ctr, hipStream_t s) {
+  hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, s, ctr);
+  HA_LAUNCH_CHECK("queue_reset");
+  return HA_OK;
+}
+
 }  // namespace
 
 }  // namespace ha

@@ -231,7 +231,8 @@ size_t hyperattn_backward_workspace_bytes(int64_t n, int d, int heads,
  * dO_i . O_i, dV = P^T dO, dS = P (dO V^T - Delta 1^T), dQ = dS K / sqrt(d),
  * dK = dS^T Q / sqrt(d). O and lse are the forward call's outputs (lse
  * required). bf16 only. workspace: >=
- * exact_attention_backward_workspace_bytes(n, heads) bytes (Delta).
+ * exact_attention_backward_workspace_bytes(n, heads) bytes (Delta and the
+ * work-queue counters of the persistent launches).
  */
 int exact_attention_backward(const void* Q, const void* K, const void* V,
                              const void* O, const float* lse, const void* dO,

@@ -92,10 +92,10 @@ def test_backward_validates_before_any_device_call():
     assert rc == -2
     assert lib.hyperattn_backward(None, None, None, None, None, None, None, None, None, 0, 64,
                                   2, 1, 256, 256, 4096, 8, 1, 1, None, 0, None) == 0
-    assert lib.exact_attention_backward_workspace_bytes(300, 2) == 2560
-    rc = lib.exact_attention_backward(p, p, p, p, p, p, p, p, p, 300, 64, 2, 1, 0, p, 2560, None)
+    assert lib.exact_attention_backward_workspace_bytes(300, 2) == 2560 + 256
+    rc = lib.exact_attention_backward(p, p, p, p, p, p, p, p, p, 300, 64, 2, 1, 0, p, 2816, None)
     assert rc == -3
-    rc = lib.exact_attention_backward(p, p, p, p, p, p, p, p, p, 300, 64, 2, 1, 1, p, 2559, None)
+    rc = lib.exact_attention_backward(p, p, p, p, p, p, p, p, p, 300, 64, 2, 1, 1, p, 2815, None)
     assert rc == -4
 
 
