@@ -728,14 +728,16 @@ __device__ __forceinline__ void fill_queries(const BwdArgs& a, BwdSmem<D>& sm, c
 
 // Key-major sweep over `count` queries at sorted positions [p0, p0 + count)
 // of `perm` for the wave's key slots. kMask: a query in bucket bkt (its
-// position / b_eff) is skipped.
+// position / b_eff) is skipped. staged: the rows, Lambda and Delta of the
+// first window are already in LDS (a previous sweep over the same queries
+// that fit one window).
 template <int D, bool kMask, int PASS>
 __device__ __forceinline__ void kv_sorted_loop(const BwdArgs& a, BwdSmem<D>& sm,
                                                const int32_t* perm, int64_t p0, int64_t count,
                                                int b_eff, int head, const QFrag<bf16_t, D>& kf,
                                                const QFrag<bf16_t, D>& vf, f32x16* dk,
                                                f32x16* dv, float om, float nu, int bkt,
-                                               bool use_dp) {
+                                               bool use_dp, bool staged = false) {
   constexpr int kWin = kSlotCap / KT;
   const auto Qr = rsrc_of(a.Q, head, a.n, D);
   const auto dOr = rsrc_of(a.dO, head, a.n, D);
@@ -750,8 +752,10 @@ __device__ __forceinline__ void kv_sorted_loop(const BwdArgs& a, BwdSmem<D>& sm,
                [&](int row) { return sm.sw[e0 + row]; });
     if ((PASS & PASS_K) && threadIdx.x < KT) b.w2[threadIdx.x] = sm.sw2[e0 + threadIdx.x];
   };
-  fill_queries(a, sm, perm, p0, count, head);
-  __syncthreads();
+  if (!staged) {
+    fill_queries(a, sm, perm, p0, count, head);
+    __syncthreads();
+  }
   issue(0);
   pipe.commit(sm.buf[0].t, true);
   __syncthreads();
@@ -830,8 +834,9 @@ __device__ __forceinline__ void kv_bucket_item(const BwdArgs& a, BwdSmem<D>& sm,
     if (krow >= 0) finish_bucket_key<D>(a, it, acc, false, krow);
     load_q<bf16_t, D>(vf, Vr, krow);
     zero_acc<D>(acc);
+    // a bucket of at most kSlotCap queries is still staged from the dV sweep
     kv_sorted_loop<D, false, PASS_K>(a, sm, a.perm_q, it.slot0, b_eff, b_eff, it.head, kf, vf,
-                                     acc, nullptr, 1.f, 1.f, 0, true);
+                                     acc, nullptr, 1.f, 1.f, 0, true, b_eff <= kSlotCap);
     if (krow >= 0) finish_bucket_key<D>(a, it, acc, true, krow);
   } else {
     load_q<bf16_t, D>(vf, Vr, krow);

@@ -72,6 +72,12 @@ BACKWARD_CASES = {
     # 16384 rows: the sample slots' gradient takes two query chunks
     "two_query_chunks": ("longctx_noncausal_n131072_d64_h8_bf16",
                          dict(heads=1, n=16384, b=256, m=256)),
+    # causal with n <= recursion_base: the whole problem is one base block
+    "causal_base_only": ("chatglm2_causal_n32768_d128_h32_bf16",
+                         dict(heads=2, n=384, b=128, m=128, recursion_base=512, rope=False)),
+    # one bucket holds every key: every sample lies inside the query's bucket
+    "bucket_covers_n": ("planted_noncausal_n8192_d64_h8_bf16",
+                        dict(heads=1, n=512, b=512, m=64, planted=0)),
 }
 
 
