@@ -138,9 +138,10 @@ def cpu_baseline(w):
 
 
 def sweep(args, torch, api):
-    """HA page, "Single self-attention layer": one layer's forward time against
-    n, causal and non-causal, with exact attention beside it. Inputs are
-    seeded iid N(0, 1) bf16 tensors of the page's shape (d = 64, 12 heads)."""
+    """HA page, "Single self-attention layer": one layer's forward time and
+    forward + backward time against n, causal and non-causal, with exact
+    attention beside it. Inputs are seeded iid N(0, 1) bf16 tensors of the
+    page's shape (d = 64, 12 heads); dO likewise."""
     H, d = args.sweep_heads, args.sweep_d
     g = torch.Generator(device="cuda")
     g.manual_seed(20231009)
@@ -170,10 +171,29 @@ def sweep(args, torch, api):
             reps = max(2, min(20, (1 << 22) // n))
             t_h = timed(lambda: api.forward(q, k, v, workspace=ws, out=o, **kw), reps)
             t_e = timed(lambda: api.exact(q, k, v, causal=causal, out=oe), max(2, reps // 4))
-            print(json.dumps({"sweep": "single-layer forward", "heads": H, "head_dim": d,
-                              "seq_len": n, "causal": causal, "dtype": "bf16",
-                              "hyperattention_ms": t_h, "exact_ms": t_e,
-                              "speedup": t_e / t_h}), flush=True)
+            rec = {"sweep": "single layer", "heads": H, "head_dim": d,
+                   "seq_len": n, "causal": causal, "dtype": "bf16",
+                   "hyperattention_ms": t_h, "exact_ms": t_e, "speedup": t_e / t_h}
+            if not args.no_backward:
+                do = torch.randn(q.shape, device="cuda", dtype=torch.bfloat16, generator=g)
+                lse = torch.empty((H, n), dtype=torch.float32, device="cuda")
+                le = torch.empty_like(lse)
+                wsb = api.alloc_workspace(api.backward_workspace_bytes(n, d, H, **{
+                    x: kw[x] for x in ("causal", "b", "m", "r", "recursion_base")}), "cuda")
+
+                def h_fb():
+                    api.forward(q, k, v, workspace=ws, out=o, lse_out=lse, return_lse=True, **kw)
+                    api.backward(q, k, v, o, lse, do, workspace=wsb, **kw)
+
+                def e_fb():
+                    api.exact(q, k, v, causal=causal, out=oe, lse_out=le, return_lse=True)
+                    api.exact_backward(q, k, v, oe, le, do, causal=causal)
+
+                rec["hyperattention_fwd_bwd_ms"] = timed(h_fb, max(2, reps // 2))
+                rec["exact_fwd_bwd_ms"] = timed(e_fb, max(2, reps // 8))
+                rec["fwd_bwd_speedup"] = rec["exact_fwd_bwd_ms"] / rec["hyperattention_fwd_bwd_ms"]
+                del do, lse, le, wsb
+            print(json.dumps(rec), flush=True)
             del q, k, v, ws, o, oe
             torch.cuda.empty_cache()
             n *= 2
@@ -336,6 +356,8 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time forward + backward on the headline workload (and exact "
                          "attention's forward + backward); one JSON line")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="with --sweep: forward times only")
     ap.add_argument("--sweep-heads", type=int, default=12)
     ap.add_argument("--sweep-d", type=int, default=64)
     ap.add_argument("--copy-calibration", action="store_true",
