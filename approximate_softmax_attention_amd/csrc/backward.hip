@@ -118,16 +118,30 @@ struct BwdArgs {
 // ------------------------------------------------------------ MFMA helpers
 // acc[i] = <tile row key_of(kb, i, g), the lane's fragment row> over the 32
 // rows of block kb of the tile array (A: tile rows from LDS, B: fragment).
-template <int D>
+// kAhead: every fragment read of the block is issued before the MFMA chain
+// (the empty asm keeps the compiler from sinking them between the MFMAs), so
+// the chain waits on LDS latency once; it holds D/4 more registers.
+template <int D, bool kAhead = false>
 __device__ __forceinline__ f32x16 tile_dot(const bf16_t* arr, const LaneOffs<bf16_t, D>& lo,
                                            const QFrag<bf16_t, D>& f, int kb,
                                            f32x16 acc = zero16()) {
   const char* base = reinterpret_cast<const char*>(arr) + kb * 32 * D * 2;
-  __builtin_amdgcn_s_setprio(kMfmaPrio);
+  if constexpr (kAhead) {
+    bf16x8_t x[D / 16];
 #pragma unroll
-  for (int st = 0; st < D / 16; ++st) {
-    const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(base + lo.k[st]);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, f.v[st], acc, 0, 0, 0);
+    for (int st = 0; st < D / 16; ++st) x[st] = *reinterpret_cast<const bf16x8_t*>(base + lo.k[st]);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_setprio(kMfmaPrio);
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[st], f.v[st], acc, 0, 0, 0);
+  } else {
+    __builtin_amdgcn_s_setprio(kMfmaPrio);
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(base + lo.k[st]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, f.v[st], acc, 0, 0, 0);
+    }
   }
   __builtin_amdgcn_s_setprio(0);
   return acc;
@@ -137,9 +151,34 @@ __device__ __forceinline__ f32x16 tile_dot(const bf16_t* arr, const LaneOffs<bf1
 // 32db + 8(i/4) + 4g + i%4 of the tile) gains the sum over the block's rows
 // of tile[row][column] * p(row), with p packed as pb[i / 8][i % 8] for
 // row key_of(kb, i, g).
-template <int D>
+template <int D, bool kAhead = false>
 __device__ __forceinline__ void tile_tr_acc(const bf16_t* arr, const LaneOffs<bf16_t, D>& lo,
                                             f32x16* acc, const bf16x8_t* pb, int kb) {
+  if constexpr (kAhead) {
+    v4i16_t x[2][D / 32][2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const char* base = reinterpret_cast<const char*>(arr) + (32 * kb + 16 * st) * D * 2;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          x[st][db][h] =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + lo.v[h][db]));
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_setprio(kMfmaPrio);
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x8_t a = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(x[st][db][0], x[st][db][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], acc[db], 0, 0, 0);
+      }
+    __builtin_amdgcn_s_setprio(0);
+    return;
+  }
   __builtin_amdgcn_s_setprio(kMfmaPrio);
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
@@ -253,6 +292,12 @@ __device__ __forceinline__ int64_t level_slot(const BwdArgs& a, int lv, uint32_t
   return (int64_t(lv) * a.heads + head) * a.S + slot;
 }
 
+// Fragment reads issued ahead of their MFMA chains (see tile_dot) in the
+// query-major kernels and in the key-major dV sweep, which have the
+// registers for it.
+constexpr bool kQAhead = true;
+constexpr bool kVAhead = true;
+
 // ------------------------------------------------------ query-major tiles
 // One LDS tile of key slots for the wave's 32 queries: dQ^T += K^T dS^T.
 // masked: a slot is valid iff its index is < nvalid and (causal) <= lim.
@@ -268,9 +313,9 @@ __device__ __forceinline__ void q_tile(const BwdBuf<D>& b, const LaneOffs<bf16_t
     float wt[16];
     if (KIND == SK_SUM) rows16(b.w2, kb, g, wt);
     if (KIND == SK_PROD) rows16(b.t.w, kb, g, wt);
-    const f32x16 s = tile_dot<D>(b.t.k, lo, qf, kb);
+    const f32x16 s = tile_dot<D, kQAhead>(b.t.k, lo, qf, kb);
     f32x16 dp;
-    if (KIND != SK_SUM) dp = tile_dot<D>(b.t.v, lo, df, kb);
+    if (KIND != SK_SUM) dp = tile_dot<D, kQAhead>(b.t.v, lo, df, kb);
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -288,7 +333,7 @@ __device__ __forceinline__ void q_tile(const BwdBuf<D>& b, const LaneOffs<bf16_t
     }
     bf16x8_t pb[2];
     pack_bf16(x, pb);
-    tile_tr_acc<D>(b.t.k, lo, dq, pb, kb);
+    tile_tr_acc<D, kQAhead>(b.t.k, lo, dq, pb, kb);
   }
 }
 
@@ -324,7 +369,7 @@ __device__ __forceinline__ void kv_tile(const BwdBuf<D>& b, const LaneOffs<bf16_
     float lw[16], dl[16];
     rows16(b.t.w, qb, g, lw);
     if (PASS & PASS_K) rows16(b.w2, qb, g, dl);
-    const f32x16 s = tile_dot<D>(b.t.k, lo, kf, qb);
+    const f32x16 s = tile_dot<D, kVAhead && PASS == PASS_V>(b.t.k, lo, kf, qb);
     f32x16 dp = zero16();
     if (kUnit && (PASS & PASS_K)) {
 #pragma unroll
@@ -349,7 +394,7 @@ __device__ __forceinline__ void kv_tile(const BwdBuf<D>& b, const LaneOffs<bf16_
 #pragma unroll
       for (int i = 0; i < 16; ++i) pv[i] = om * e[i];
       pack_bf16(pv, pb);
-      tile_tr_acc<D>(b.t.v, lo, dv, pb, qb);
+      tile_tr_acc<D, kVAhead && PASS == PASS_V>(b.t.v, lo, dv, pb, qb);
     }
     if (PASS & PASS_K) {
       float pk[16];
