@@ -407,6 +407,196 @@ __device__ __forceinline__ void kv_tile(const BwdBuf<D>& b, const LaneOffs<bf16_
   }
 }
 
+// ------------------------------------------- key-major tiles, 16 keys a wave
+// v_mfma_f32_16x16x32_bf16: A is 16 rows x 32 (lane l holds row l % 16,
+// elements 8(l/16) .. +7), B is 32 x 16 (lane l holds column l % 16, rows
+// 8(l/16) .. +7), the result 16 x 16 (lane l holds column l % 16, rows
+// 4(l/16) .. +3). A wave owns 16 key slots: K and V of its slots are the B
+// operands of S = Q K^T and dP = dO V^T over 16-query sub-blocks, and
+// dK^T, dV^T (16 columns of d per product, keys as the result's columns)
+// take 32-query blocks through transposing reads of the Q and dO tiles.
+// K, V, dK and dV of 16 keys take 96 registers at d = 128, so one sweep
+// computes both gradients (the 32-key layout would need 192 and two sweeps).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct Frag16 {
+  bf16x8_t v[D / 32];   // v[st]: row elements 32st + 8(l/16) .. +7
+};
+
+template <int D>
+struct Acc16 {
+  f32x4 a[D / 16];      // a[mb][i]: column 16mb + 4(l/16) + i of the lane's key row
+};
+
+template <int D>
+__device__ __forceinline__ void load_frag16(Frag16<D>& f, __amdgpu_buffer_rsrc_t r, int64_t row) {
+  const int g = lane_id() >> 4;
+  const uint32_t base = row >= 0 ? uint32_t(row) * (D * 2u) : kOob;
+#pragma unroll
+  for (int st = 0; st < D / 32; ++st)
+    f.v[st] = __builtin_bit_cast(bf16x8_t, buf_load16(r, base + (32 * st + 8 * g) * 2));
+}
+
+// Per-lane LDS byte offsets within one bf16 tile (Buf<bf16_t, D> layout):
+//   rd[st]: A operand of S / dP, row l % 16 of a 16-row sub-block, chunk
+//           4st + l/16 (a sub-block 16 rows further adds 16 rows: the
+//           swizzle repeats every 16 rows);
+//   tr[mb]: transposing read of rows 4(l/16) + (l%16)/4 (then 16 rows
+//           further), columns 16mb + 4(l % 4): lane l receives column
+//           16mb + l % 16 of four consecutive rows.
+template <int D>
+struct Offs16 {
+  using B = Buf<bf16_t, D>;
+  static_assert(D == 128, "the swizzle repeats every 16 rows for d = 128");
+  uint32_t rd[D / 32];
+  uint32_t tr[D / 16];
+  __device__ __forceinline__ void init() {
+    int lane = lane_id();
+    asm volatile("" : "+v"(lane));
+    const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int st = 0; st < D / 32; ++st)
+      rd[st] = uint32_t(r16 * B::CPR + ((4 * st + g) ^ B::swz(r16))) * 16u;
+    const int row = 4 * g + (r16 >> 2);
+#pragma unroll
+    for (int mb = 0; mb < D / 16; ++mb) {
+      const int d = 16 * mb + 4 * (r16 & 3);
+      tr[mb] = uint32_t(row * B::CPR + ((d >> 3) ^ B::swz(row))) * 16u + uint32_t(d & 7) * 2u;
+    }
+  }
+};
+
+// S (or dP) for the 16-row sub-block at row r0 of the tile array.
+template <int D>
+__device__ __forceinline__ f32x4 dot16(const bf16_t* arr, const Offs16<D>& o,
+                                       const Frag16<D>& f, int r0, f32x4 acc) {
+  const char* base = reinterpret_cast<const char*>(arr) + r0 * D * 2;
+  bf16x8_t x[D / 32];
+#pragma unroll
+  for (int st = 0; st < D / 32; ++st) x[st] = *reinterpret_cast<const bf16x8_t*>(base + o.rd[st]);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_setprio(kMfmaPrio);
+#pragma unroll
+  for (int st = 0; st < D / 32; ++st)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[st], f.v[st], acc, 0, 0, 0);
+  __builtin_amdgcn_s_setprio(0);
+  return acc;
+}
+
+// acc.a[mb] += (rows [r0, r0 + 32) of the tile array)^T p, p packed with
+// element j of the lane's B operand for row r0 + 4(l/16) + j (j < 4) and
+// r0 + 16 + 4(l/16) + j - 4 (j >= 4).
+template <int D>
+__device__ __forceinline__ void tr_acc16(const bf16_t* arr, const Offs16<D>& o, Acc16<D>& acc,
+                                         bf16x8_t p, int r0) {
+  const char* base = reinterpret_cast<const char*>(arr) + r0 * D * 2;
+  __builtin_amdgcn_s_setprio(kMfmaPrio);
+#pragma unroll
+  for (int mb = 0; mb < D / 16; ++mb) {
+    const v4i16_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + o.tr[mb]));
+    const v4i16_t x1 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + o.tr[mb] + 16 * D * 2));
+    const bf16x8_t a =
+        __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+    acc.a[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p, acc.a[mb], 0, 0, 0);
+  }
+  __builtin_amdgcn_s_setprio(0);
+}
+
+// One LDS tile of queries for the wave's 16 key slots: dV^T += dO^T (w E),
+// dK^T += Q^T dS in one pass (arguments as kv_tile's).
+template <int D, bool kCausal, bool kBucketMask, bool kUnit>
+__device__ __forceinline__ void kv_tile16(const BwdBuf<D>& b, const Offs16<D>& o,
+                                          const Frag16<D>& kf, const Frag16<D>& vf,
+                                          Acc16<D>& dk, Acc16<D>& dv, float c, float om,
+                                          float nu, int mlo, int mhi, bool use_dp, int nvalid,
+                                          int lim, int skip_below) {
+  const int g = lane_id() >> 4;
+#pragma unroll
+  for (int qb = 0; qb < KT / 32; ++qb) {
+    if (32 * qb >= nvalid) break;
+    if (kCausal && 32 * qb + 31 < skip_below) continue;   // the wave's keys all follow
+    float pv[8], pk[8];
+#pragma unroll
+    for (int sq = 0; sq < 2; ++sq) {
+      const int r0 = 32 * qb + 16 * sq;
+      const float4 lw = *reinterpret_cast<const float4*>(b.t.w + r0 + 4 * g);
+      const float4 dl = *reinterpret_cast<const float4*>(b.w2 + r0 + 4 * g);
+      const float lwa[4] = {lw.x, lw.y, lw.z, lw.w};
+      const float dla[4] = {dl.x, dl.y, dl.z, dl.w};
+      const f32x4 s = dot16<D>(b.t.k, o, kf, r0, f32x4{0.f, 0.f, 0.f, 0.f});
+      f32x4 dp = {0.f, 0.f, 0.f, 0.f};
+      if (kUnit) dp = dot16<D>(b.t.v, o, vf, r0, f32x4{-dla[0], -dla[1], -dla[2], -dla[3]});
+      else if (use_dp) dp = dot16<D>(b.t.v, o, vf, r0, dp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 4 * g + i;
+        bool ok = true;
+        if (kCausal) ok = r >= lim;
+        if (kBucketMask) ok = ok && (r < mlo || r >= mhi);
+        const float e = fast_exp2(ok ? fmaf(s[i], c, -lwa[i]) : -INFINITY);
+        pv[4 * sq + i] = om * e;
+        pk[4 * sq + i] = kUnit ? e * dp[i] : e * (om * dp[i] - nu * dla[i]);
+      }
+    }
+    bf16x8_t p;
+    if (kUnit || use_dp) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p[j] = (__bf16)pv[j];
+      tr_acc16<D>(b.t.v, o, dv, p, 32 * qb);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = (__bf16)pk[j];
+    tr_acc16<D>(b.t.k, o, dk, p, 32 * qb);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void zero16(Acc16<D>& a) {
+#pragma unroll
+  for (int mb = 0; mb < D / 16; ++mb) a.a[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+template <int D>
+__device__ __forceinline__ void scale16(Acc16<D>& a, float f) {
+#pragma unroll
+  for (int mb = 0; mb < D / 16; ++mb) a.a[mb] *= f;
+}
+
+template <int D>
+__device__ __forceinline__ void add_row16(Acc16<D>& a, const float* row) {
+  const int g = lane_id() >> 4;
+#pragma unroll
+  for (int mb = 0; mb < D / 16; ++mb) {
+    const float4 v = *reinterpret_cast<const float4*>(row + 16 * mb + 4 * g);
+    a.a[mb][0] += v.x;
+    a.a[mb][1] += v.y;
+    a.a[mb][2] += v.z;
+    a.a[mb][3] += v.w;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_row16_f32(const Acc16<D>& a, float* row) {
+  const int g = lane_id() >> 4;
+#pragma unroll
+  for (int mb = 0; mb < D / 16; ++mb)
+    *reinterpret_cast<float4*>(row + 16 * mb + 4 * g) =
+        make_float4(a.a[mb][0], a.a[mb][1], a.a[mb][2], a.a[mb][3]);
+}
+
+template <int D>
+__device__ __forceinline__ void store_row16_bf16(const Acc16<D>& a, bf16_t* row) {
+  const int g = lane_id() >> 4;
+#pragma unroll
+  for (int mb = 0; mb < D / 16; ++mb) {
+    const uint32_t lo = uint32_t(f32_to_bf16(a.a[mb][0])) | (uint32_t(f32_to_bf16(a.a[mb][1])) << 16);
+    const uint32_t hi = uint32_t(f32_to_bf16(a.a[mb][2])) | (uint32_t(f32_to_bf16(a.a[mb][3])) << 16);
+    *reinterpret_cast<uint2*>(row + 16 * mb + 4 * g) = make_uint2(lo, hi);
+  }
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const bf16_t* base, int head, int64_t n,
                                                           int d) {
   return head_rsrc(base + int64_t(head) * n * d, n * d * 2);
@@ -978,6 +1168,249 @@ __device__ __forceinline__ void kv_sample_item(const BwdArgs& a, BwdSmem<D>& sm,
   }
 }
 
+// ------------------------------------- key-major items, 16 keys a wave (d = 128)
+// A work-group owns kAttnQ / 2 = 128 key slots (8 waves x 16). Bucket and
+// sample items are the halves of the 256-slot items above: item w covers
+// slots [128 (w mod 2), 128 (w mod 2) + 128) of item w / 2.
+constexpr int kKW16 = 16;
+constexpr int kKeys16 = kWaves * kKW16;
+// At d = 128 the base case's and the sample slots' key-major kernels take
+// the 16-key layout (one sweep of long query ranges). A bucket item sees
+// only its bucket's queries: there the 32-key items, whose per-item
+// overheads are amortised over twice the keys, measured faster despite
+// their two sweeps.
+template <int D, int MODE> constexpr bool kKv16 = D == 128 && MODE != BW_BUCKET;
+
+template <int D, bool kCausal>
+__device__ __forceinline__ void kv16_exact_sweep(const BwdArgs& a, BwdSmem<D>& sm, int head,
+                                                 int64_t q_lo, int64_t b_hi, int64_t kw0,
+                                                 int64_t krow, const Frag16<D>& kf,
+                                                 const Frag16<D>& vf, Acc16<D>& dk,
+                                                 Acc16<D>& dv) {
+  const auto Qr = rsrc_of(a.Q, head, a.n, D);
+  const auto dOr = rsrc_of(a.dO, head, a.n, D);
+  Offs16<D> o;
+  o.init();
+  const int ntiles = int((b_hi - q_lo + KT - 1) / KT);
+  const float* lse = a.lse + int64_t(head) * a.n;
+  const float* dl = a.delta + int64_t(head) * a.n;
+  Pipe<bf16_t, D> pipe;
+  auto issue = [&](int t) {
+    const int64_t r0 = q_lo + int64_t(t) * KT;
+    const int nv = int(b_hi - r0 < KT ? b_hi - r0 : KT);
+    BwdBuf<D>& b = sm.buf[t & 1];
+    pipe.issue(b.t, Qr, dOr, true, [&](int row) { return row < nv ? int(r0 + row) : -1; },
+               [&](int row) { return row < nv ? lse[r0 + row] * kLog2e : INFINITY; });
+    if (threadIdx.x < KT) b.w2[threadIdx.x] = int(threadIdx.x) < nv ? dl[r0 + threadIdx.x] : 0.f;
+  };
+  issue(0);
+  pipe.commit(sm.buf[0].t, true);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) issue(t + 1);
+    const int64_t r0 = q_lo + int64_t(t) * KT;
+    const int nvalid = int(b_hi - r0 < KT ? b_hi - r0 : KT);
+    const int64_t dk0 = (krow >= 0 ? krow : kw0) - r0;
+    const int lim = dk0 < 0 ? 0 : (dk0 > KT ? KT : int(dk0));
+    const int64_t sb = kw0 - r0;
+    const int skip_below = sb < 0 ? 0 : (sb > KT ? KT : int(sb));
+    kv_tile16<D, kCausal, false, true>(sm.buf[t & 1], o, kf, vf, dk, dv, a.scale_log2, 1.f, 1.f,
+                                       0, 0, true, nvalid, lim, skip_below);
+    if (t + 1 < ntiles) pipe.commit(sm.buf[(t + 1) & 1].t, true);
+    __syncthreads();
+  }
+}
+
+// dK, dV of key tile t (128 keys) of the block against its queries.
+template <int D, bool kCausal>
+__device__ __forceinline__ void kv16_exact_item(const BwdArgs& a, BwdSmem<D>& sm, uint32_t lin) {
+  const uint32_t gx = a.items_per_head;
+  const int head = int(lin / gx);
+  const uint32_t bx = lin - uint32_t(head) * gx;
+  const uint32_t tpb = a.tiles_per_block;
+  const uint32_t blk = bx / tpb;
+  const int64_t tile = bx - blk * tpb;
+  const int64_t b_lo = blk * a.block;
+  const int64_t b_hi = b_lo + a.block < a.n ? b_lo + a.block : a.n;
+  const int64_t k0 = b_lo + tile * kKeys16;
+  const int64_t k_end = k0 + kKeys16 < b_hi ? k0 + kKeys16 : b_hi;
+  const int wave = threadIdx.x >> 6;
+  const int64_t kw0 = k0 + wave * kKW16;
+  const int64_t kr = kw0 + (lane_id() & 15);
+  const int64_t krow = kr < k_end ? kr : -1;
+  const int64_t q_lo = kCausal ? k0 : b_lo;
+  Frag16<D> kf, vf;
+  load_frag16<D>(kf, rsrc_of(a.K, head, a.n, D), krow);
+  load_frag16<D>(vf, rsrc_of(a.V, head, a.n, D), krow);
+  Acc16<D> dk, dv;
+  zero16<D>(dk);
+  zero16<D>(dv);
+  kv16_exact_sweep<D, kCausal>(a, sm, head, q_lo, b_hi, kw0, krow, kf, vf, dk, dv);
+  if (krow < 0) return;
+  scale16<D>(dk, a.scale);
+  for (int lv = 0; lv < a.merge_levels; ++lv) {
+    const int64_t idx = level_slot(a, lv, blk, b_lo, krow, false, head);
+    if (idx >= 0) {
+      add_row16<D>(dk, a.part_dk + idx * D);
+      add_row16<D>(dv, a.part_dv + idx * D);
+    }
+  }
+  store_row16_bf16<D>(dk, a.dK + (int64_t(head) * a.n + krow) * D);
+  store_row16_bf16<D>(dv, a.dV + (int64_t(head) * a.n + krow) * D);
+}
+
+// Sweep over `count` queries at sorted positions [p0, p0 + count) of `perm`
+// (kv_sorted_loop's arguments).
+template <int D, bool kMask>
+__device__ __forceinline__ void kv16_sorted_loop(const BwdArgs& a, BwdSmem<D>& sm,
+                                                 const int32_t* perm, int64_t p0, int64_t count,
+                                                 int b_eff, int head, const Frag16<D>& kf,
+                                                 const Frag16<D>& vf, Acc16<D>& dk,
+                                                 Acc16<D>& dv, float om, float nu, int bkt,
+                                                 bool use_dp) {
+  constexpr int kWin = kSlotCap / KT;
+  const auto Qr = rsrc_of(a.Q, head, a.n, D);
+  const auto dOr = rsrc_of(a.dO, head, a.n, D);
+  Offs16<D> o;
+  o.init();
+  const int ntiles = int((count + KT - 1) / KT);
+  Pipe<bf16_t, D> pipe;
+  auto issue = [&](int t) {
+    const int e0 = (t % kWin) * KT;
+    BwdBuf<D>& b = sm.buf[t & 1];
+    pipe.issue(b.t, Qr, dOr, true, [&](int row) { return int(sm.srow[e0 + row]); },
+               [&](int row) { return sm.sw[e0 + row]; });
+    if (threadIdx.x < KT) b.w2[threadIdx.x] = sm.sw2[e0 + threadIdx.x];
+  };
+  fill_queries(a, sm, perm, p0, count, head);
+  __syncthreads();
+  issue(0);
+  pipe.commit(sm.buf[0].t, true);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) {
+      if ((t + 1) % kWin == 0) {
+        fill_queries(a, sm, perm, p0 + int64_t(t + 1) * KT, count - int64_t(t + 1) * KT, head);
+        __syncthreads();
+      }
+      issue(t + 1);
+    }
+    const int64_t left = count - int64_t(t) * KT;
+    const int nvalid = int(left < KT ? left : KT);
+    int mlo = 0, mhi = 0;
+    if (kMask && bkt >= 0) {
+      const int64_t first = int64_t(bkt) * b_eff - (p0 + int64_t(t) * KT);
+      const int64_t last = first + b_eff;
+      mlo = int(first < 0 ? 0 : (first > KT ? KT : first));
+      mhi = int(last < 0 ? 0 : (last > KT ? KT : last));
+    }
+    kv_tile16<D, false, kMask, !kMask>(sm.buf[t & 1], o, kf, vf, dk, dv, a.scale_log2, om, nu,
+                                       mlo, mhi, use_dp, nvalid, 0, 0);
+    if (t + 1 < ntiles) pipe.commit(sm.buf[(t + 1) & 1].t, true);
+    __syncthreads();
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void finish_bucket_key16(const BwdArgs& a, const BucketItem& it,
+                                                    Acc16<D>& acc, bool is_k, int64_t krow) {
+  const Level& L = a.table.lv[it.lv];
+  const int64_t h = L.h;
+  if (is_k) scale16<D>(acc, a.scale);
+  const int64_t k_lo = a.table.causal ? 2 * it.seg * h : 0;
+  const int64_t kslot = (int64_t(it.lv) * a.heads + it.head) * a.S + it.seg * h + (krow - k_lo);
+  const int64_t nqc = L.smp_nqc;
+  const int64_t item0 = L.smp_wg0 + (int64_t(it.head) * L.nseg + it.seg) * L.smp_nsc * nqc;
+  const float* part = is_k ? a.slot_dk : a.slot_dv;
+  for (int t = a.slot_first[kslot]; t >= 0; t = a.slot_next[it.rec * 2 * a.m + t]) {
+    const int64_t sc = t / kAttnQ;
+    const int tt = t - int(sc) * kAttnQ;
+    for (int64_t qc = 0; qc < nqc; ++qc)
+      add_row16<D>(acc, part + ((item0 + sc * nqc + qc) * kAttnQ + tt) * D);
+  }
+  if (a.table.causal)
+    store_row16_f32<D>(acc, (is_k ? a.part_dk : a.part_dv) + kslot * D);
+  else
+    store_row16_bf16<D>(acc, (is_k ? a.dK : a.dV) + (int64_t(it.head) * a.n + krow) * D);
+}
+
+template <int D>
+__device__ __forceinline__ void kv16_bucket_item(const BwdArgs& a, BwdSmem<D>& sm, int64_t w) {
+  const BucketItem it = decode_bucket(a, w >> 1);
+  const int b_eff = a.table.lv[it.lv].b_eff;
+  const int wave = threadIdx.x >> 6;
+  const int64_t ki = it.chunk * kAttnQ + (w & 1) * kKeys16 + wave * kKW16 + (lane_id() & 15);
+  const int64_t krow = ki < b_eff ? int64_t(a.perm_k[it.slot0 + ki]) : -1;
+  Frag16<D> kf, vf;
+  load_frag16<D>(kf, rsrc_of(a.K, it.head, a.n, D), krow);
+  load_frag16<D>(vf, rsrc_of(a.V, it.head, a.n, D), krow);
+  Acc16<D> dk, dv;
+  zero16<D>(dk);
+  zero16<D>(dv);
+  kv16_sorted_loop<D, false>(a, sm, a.perm_q, it.slot0, b_eff, b_eff, it.head, kf, vf, dk, dv,
+                             1.f, 1.f, 0, true);
+  if (krow < 0) return;
+  finish_bucket_key16<D>(a, it, dv, false, krow);
+  finish_bucket_key16<D>(a, it, dk, true, krow);
+}
+
+template <int D>
+__device__ __forceinline__ void kv16_sample_item(const BwdArgs& a, BwdSmem<D>& sm, int64_t w) {
+  const int64_t w2 = w >> 1;
+  int lv = 0;
+  for (int l = 1; l < a.table.count; ++l)
+    if (w2 >= a.table.lv[l].smp_wg0) lv = l;
+  const Level& L = a.table.lv[lv];
+  uint32_t rem = uint32_t(w2 - L.smp_wg0);
+  const uint32_t nqc = uint32_t(L.smp_nqc), nsc = uint32_t(L.smp_nsc), nsg = uint32_t(L.nseg);
+  uint32_t quo = rem / nqc;
+  const int64_t qc = rem - quo * nqc;
+  rem = quo;
+  quo = rem / nsc;
+  const int64_t sc = rem - quo * nsc;
+  rem = quo;
+  quo = rem / nsg;
+  const int64_t seg = rem - quo * nsg;
+  const int head = int(quo);
+  const int64_t h = L.h;
+  const int64_t rec = int64_t(head) * a.nodes + ((int64_t(1) << lv) + seg - 1);
+  const int ucount = a.meta[rec * 4];
+  const int vcount = a.meta[rec * 4 + 1];
+  const int wave = threadIdx.x >> 6;
+  const int64_t slot = (w & 1) * kKeys16 + wave * kKW16 + (lane_id() & 15);
+  const int64_t t = sc * kAttnQ + slot;
+  int64_t krow = -1;
+  float om = 0.f, nu = 0.f;
+  int bkt = -1;
+  if (t < ucount) {
+    krow = a.u_idx[rec * a.m + t];
+    bkt = a.u_bkt[rec * a.m + t];
+    nu = L.alpha;
+  } else if (t - ucount < vcount) {
+    krow = a.v_idx[rec * a.m + (t - ucount)];
+    bkt = a.v_bkt[rec * a.m + (t - ucount)];
+    om = a.v_w[rec * a.m + (t - ucount)];
+  }
+  Frag16<D> kf, vf;
+  load_frag16<D>(kf, rsrc_of(a.K, head, a.n, D), krow);
+  load_frag16<D>(vf, rsrc_of(a.V, head, a.n, D), krow);
+  Acc16<D> dk, dv;
+  zero16<D>(dk);
+  zero16<D>(dv);
+  const int64_t p0 = qc * kBwdQChunk;
+  const int64_t count = h - p0 < kBwdQChunk ? h - p0 : kBwdQChunk;
+  const int64_t seg0 = (int64_t(lv) * a.heads + head) * a.S + seg * h;
+  // uniform slots have om = 0: no dV and no dP for a wave of them
+  const bool wave_om = __ballot(om != 0.f) != 0;
+  kv16_sorted_loop<D, true>(a, sm, a.perm_q + seg0, p0, count, L.b_eff, head, kf, vf, dk, dv, om,
+                            nu, bkt, wave_om);
+  if (krow < 0) return;
+  scale16<D>(dk, a.scale);
+  const int64_t idx = w2 * kAttnQ + slot;
+  store_row16_f32<D>(dk, a.slot_dk + idx * D);
+  store_row16_f32<D>(dv, a.slot_dv + idx * D);
+}
+
 // ------------------------------------------------------------------ kernels
 // kPersistent: the work-group takes items from the queues until all are
 // done; else it runs the one item of its (XCD-remapped) block index. The
@@ -1006,9 +1439,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_kv_kernel(BwdArgs a) {
   __shared__ BwdSmem<D> sm;
   auto item_fn = [&](int64_t item) __attribute__((always_inline)) {
-    if (MODE == BW_EXACT) kv_exact_item<D, kCausal>(a, sm, uint32_t(item));
-    else if (MODE == BW_BUCKET) kv_bucket_item<D>(a, sm, item);
-    else kv_sample_item<D>(a, sm, item);
+    if constexpr (kKv16<D, MODE>) {
+      if (MODE == BW_EXACT) kv16_exact_item<D, kCausal>(a, sm, uint32_t(item));
+      else if (MODE == BW_BUCKET) kv16_bucket_item<D>(a, sm, item);
+      else kv16_sample_item<D>(a, sm, item);
+    } else {
+      if (MODE == BW_EXACT) kv_exact_item<D, kCausal>(a, sm, uint32_t(item));
+      else if (MODE == BW_BUCKET) kv_bucket_item<D>(a, sm, item);
+      else kv_sample_item<D>(a, sm, item);
+    }
   };
   if constexpr (kPersistent) {
     run_items(a, sm.item, [&](int64_t item) __attribute__((always_inline)) {
@@ -1185,7 +1624,7 @@ int launch_bwd_samples(const Plan& p, const BwdIO& io, void* ws, hipStream_t s) 
   BwdArgs a = base_args(io, p.n, p.d, p.heads);
   plan_args(a, p, ws);
   auto k = p.d == 128 ? bwd_kv_kernel<128, BW_SAMPLE, false, true> : bwd_kv_kernel<64, BW_SAMPLE, false, true>;
-  return launch_items(k, a, p.smp_wgs, true, "bwd_sample_kv", s);
+  return launch_items(k, a, p.d == 128 ? 2 * p.smp_wgs : p.smp_wgs, true, "bwd_sample_kv", s);
 }
 
 int launch_bwd_bucket(const Plan& p, const BwdIO& io, void* ws, hipStream_t s) {
@@ -1228,10 +1667,19 @@ int launch_bwd_exact(const BwdIO& io, int64_t n, int d, int heads, int causal, i
   if (d == 128) {
     rc = launch_items(causal ? bwd_q_kernel<128, BW_EXACT, true, true> : bwd_q_kernel<128, BW_EXACT, false, true>,
                       a, items, true, nq, s);
+    // the key-major items are tiles of 128 keys (16 per wave)
+    BwdArgs akv = a;
+    const int64_t tpb_kv = ceil_div(block, kKeys16);
+    const int64_t per_head_kv = ceil_div(n, block) * tpb_kv;
+    akv.tiles_per_block = uint32_t(tpb_kv);
+    akv.items_per_head = uint32_t(per_head_kv);
+    if (!rc && per_head_kv * heads >= (int64_t(1) << 31))
+      rc = fail(HA_ERR_SHAPE, "%lld key tiles exceed the launch limit",
+                (long long)(per_head_kv * heads));
     if (!rc)
       rc = launch_items(causal ? bwd_kv_kernel<128, BW_EXACT, true, false>
                                : bwd_kv_kernel<128, BW_EXACT, false, false>,
-                        a, items, false, nkv, s);
+                        akv, per_head_kv * heads, false, nkv, s);
   } else {
     rc = launch_items(causal ? bwd_q_kernel<64, BW_EXACT, true, true> : bwd_q_kernel<64, BW_EXACT, false, true>,
                       a, items, true, nq, s);
