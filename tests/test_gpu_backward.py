@@ -78,6 +78,11 @@ BACKWARD_CASES = {
     # one bucket holds every key: every sample lies inside the query's bucket
     "bucket_covers_n": ("planted_noncausal_n8192_d64_h8_bf16",
                         dict(heads=1, n=512, b=512, m=64, planted=0)),
+    # d = 128 with slot lists that are not whole 128-slot groups (m = 200) and
+    # a last level with exhaustive samples
+    "causal_exhaustive_d128": ("chatglm2_causal_n32768_d128_h32_bf16",
+                               dict(heads=1, n=1024, b=64, m=200, recursion_base=128,
+                                    rope=False)),
 }
 
 
@@ -109,11 +114,12 @@ def test_hyperattention_backward(name):
     assert max(errs) <= TOL["bf16"], errs
 
 
-def test_backward_empty_vnorm_list():
+@pytest.mark.parametrize("name", ["causal_exhaustive", "causal_exhaustive_d128"])
+def test_backward_empty_vnorm_list(name):
     """V rows [0, n/2) all zero: the first level's node draws no V-norm
     sample, so its keys get no product gradient from samples."""
-    banner("hyperattention backward with an empty V-norm list")
-    _, _, grads, refs = _run_case("causal_exhaustive", zero_v_half=True)
+    banner(f"hyperattention backward with an empty V-norm list ({name})")
+    _, _, grads, refs = _run_case(name, zero_v_half=True)
     errs = _errs(grads, refs)
     print(f"  dQ {errs[0]:.2e} dK {errs[1]:.2e} dV {errs[2]:.2e}", flush=True)
     assert max(errs) <= TOL["bf16"], errs
