@@ -32,25 +32,26 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+def kernel_source_hash(backward=False):
     """sha256 over the sources of the forward pass's kernels (file names and
-    contents; the backward pass's kernel file is not part of it)."""
+    contents), or with backward=True over every kernel source."""
     import hashlib
     h = hashlib.sha256()
     src = os.path.join(ROOT, "approximate_softmax_attention_amd", "csrc")
     for name in sorted(os.listdir(src)):
-        if name.endswith((".hip", ".h", ".cpp")) and name != "backward.hip":
+        if name.endswith((".hip", ".h", ".cpp")) and (backward or name != "backward.hip"):
             h.update(name.encode())
             with open(os.path.join(src, name), "rb") as f:
                 h.update(f.read())
     return h.hexdigest()
 
 
-def profiled_traffic(workload, kernel):
+def profiled_traffic(workload, kernel, backward=False):
     """HBM bytes per launch of `kernel` (read + written, scaled by the plain
     copy calibration) from the committed rocprofv3 counter summary, or None
     when there is none or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"hyperattn_{workload}_hbm_traffic.md")
+    name = "backward_hbm_traffic" if backward else "hbm_traffic"
+    path = os.path.join(ROOT, "profiles", f"hyperattn_{workload}_{name}.md")
     if not os.path.exists(path):
         return None
     sha, val = None, None
@@ -61,7 +62,7 @@ def profiled_traffic(workload, kernel):
                 sha = line.split(":", 1)[1].strip()
             elif line.startswith(f"bytes-per-launch {kernel}:"):
                 val = int(line.split(":", 1)[1])
-    if sha is None or sha != kernel_source_hash():
+    if sha is None or sha != kernel_source_hash(backward):
         return None
     return val
 
@@ -262,6 +263,45 @@ def backward_flops(w):
     return out
 
 
+def copy_calibration(torch):
+    """A plain 1 GiB copy (reads 1 GiB, writes 1 GiB) for scaling HBM byte
+    counters against known traffic."""
+    log("plain copy of 1 GiB (reads 1 GiB, writes 1 GiB)")
+    src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.mul(src, 1, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def backward_kernel_flops(w):
+    """MFMA flops each backward kernel needs (per launch), counting the
+    products that kernel's own results require: the key-major kernels need
+    S, dP, dV and dK, the query-major ones S, dP and dQ (so S and dP count in
+    both); uniform sample slots need no dP, dV (query-major: no dP)."""
+    H, n, d, b, m = w.heads, w.n, w.d, w.b, w.m
+    out = {"bwd_bucket_q": 0.0, "bwd_bucket_kv": 0.0, "bwd_sample_kv": 0.0}
+    size = n
+    levels = []
+    if w.causal:
+        while size > w.recursion_base:
+            size //= 2
+            levels.append(size)
+    else:
+        levels = [n]
+    for h in levels:
+        be, mm = min(b, h), min(m, h)
+        rows = n // 2 if w.causal else n
+        out["bwd_bucket_q"] += H * rows * 2 * d * (3 * be + 2 * mm + 3 * mm)
+        out["bwd_bucket_kv"] += H * rows * 2 * d * 4 * be
+        out["bwd_sample_kv"] += H * rows * 2 * d * (2 * mm + 4 * mm)
+    if w.causal:
+        pairs = H * (n // size) * size * (size + 1) / 2
+        out["bwd_base_q"] = 3 * 2.0 * d * pairs
+        out["bwd_base_kv"] = 4 * 2.0 * d * pairs
+    return out
+
+
 def backward_mode(args, torch, api, wl):
     """The headline workload's forward and backward pass (the HA page times
     forward + backward in its single-layer experiment), with exact attention's
@@ -316,9 +356,19 @@ def backward_mode(args, torch, api, wl):
                                                           "vnorm_prefix", "sort_hist",
                                                           "sort_offsets", "sort_scatter",
                                                           "samples")) / 2
+    kfl = backward_kernel_flops(w)
+    dom = max((k for k in kfl if k in kernels), key=lambda k: kernels[k]["avg_ms"])
+    achieved = kfl[dom] / (kernels[dom]["avg_ms"] / 1e3)
+    traffic = profiled_traffic(w.name, dom, backward=True)
+    for k in kfl:
+        if k in kernels:
+            kernels[k]["tflops"] = kfl[k] / (kernels[k]["avg_ms"] / 1e3) / 1e12
     rec = {"mode": "forward_backward", "workload": w.name, "steps": args.steps,
            "ms_per_step": ms, "tokens_per_s": w.n / (ms / 1e3), "kernels": kernels,
-           "backward_ms_approx": bwd_ms, "backward_mfma": mfma}
+           "backward_ms_approx": bwd_ms, "backward_mfma": mfma,
+           "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
+                        "unit": "TFLOP/s", "frac": achieved / PEAK_BF16, "traffic": traffic,
+                        "kernel": dom, "flops_per_launch": kfl[dom]}}
     if not args.no_exact:
         Oe = torch.empty_like(Q)
         le = torch.empty_like(lse)
@@ -335,7 +385,34 @@ def backward_mode(args, torch, api, wl):
         torch.cuda.synchronize()
         rec["exact_ms_per_step"] = e0.elapsed_time(e1)
         rec["speedup_vs_exact"] = rec["exact_ms_per_step"] / ms
+    if args.copy_calibration:
+        copy_calibration(torch)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle's forward + backward on one head")
+        rec["cpu_baseline"] = cpu_baseline_backward(w)
     print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_backward(w):
+    """The oracle's forward + backward (oracle.backward recomputes the
+    forward) on one head of the workload, scaled to all heads."""
+    from threadpoolctl import threadpool_info
+
+    from approximate_softmax_attention_amd import workloads as wl
+    from oracle import backward as obw
+    q, k, v, _ = wl.make_head(w, 0)
+    do = wl.make_grad(w, heads=[0])[0]
+    t0 = time.perf_counter()
+    obw.hyperattention_backward(q[None], k[None], v[None], do[None], causal=w.causal, b=w.b,
+                                m=w.m, r=w.r, recursion_base=w.recursion_base,
+                                seed=w.method_seed)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": w.n / (dt * w.heads), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"1 of {w.heads} heads of the same workload (full n={w.n} forward + "
+                      f"backward, fp64 numpy), {dt:.1f} s, scaled x{w.heads}",
+            "host_cpus": len(os.sched_getaffinity(0))}
 
 
 def main():
@@ -474,12 +551,7 @@ def main():
         del Oe
 
     if args.copy_calibration:
-        log("plain copy of 1 GiB (reads 1 GiB, writes 1 GiB)")
-        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
-        dst = torch.empty_like(src)
-        torch.mul(src, 1, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(torch)
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one head")
