@@ -1174,12 +1174,10 @@ __device__ __forceinline__ void kv_sample_item(const BwdArgs& a, BwdSmem<D>& sm,
 // slots [128 (w mod 2), 128 (w mod 2) + 128) of item w / 2.
 constexpr int kKW16 = 16;
 constexpr int kKeys16 = kWaves * kKW16;
-// At d = 128 the base case's and the sample slots' key-major kernels take
-// the 16-key layout (one sweep of long query ranges). A bucket item sees
-// only its bucket's queries: there the 32-key items, whose per-item
-// overheads are amortised over twice the keys, measured faster despite
-// their two sweeps.
-template <int D, int MODE> constexpr bool kKv16 = D == 128 && MODE != BW_BUCKET;
+// At d = 128 the key-major kernels take the 16-key layout (one sweep for
+// dK and dV). A bucket item keeps 256 key slots per work-group as two
+// halves that share the bucket's query tiles.
+template <int D, int MODE> constexpr bool kKv16 = D == 128;
 
 template <int D, bool kCausal>
 __device__ __forceinline__ void kv16_exact_sweep(const BwdArgs& a, BwdSmem<D>& sm, int head,
@@ -1334,24 +1332,77 @@ __device__ __forceinline__ void finish_bucket_key16(const BwdArgs& a, const Buck
     store_row16_bf16<D>(acc, (is_k ? a.dK : a.dV) + (int64_t(it.head) * a.n + krow) * D);
 }
 
+// dK, dV of one bucket item's 256 key slots (two halves of 128, one after the
+// other) against the bucket's queries. When the bucket has at most 2 KT
+// queries both query tiles are loaded once and serve both halves; larger
+// buckets stream the queries once per half.
 template <int D>
 __device__ __forceinline__ void kv16_bucket_item(const BwdArgs& a, BwdSmem<D>& sm, int64_t w) {
-  const BucketItem it = decode_bucket(a, w >> 1);
+  const BucketItem it = decode_bucket(a, w);
   const int b_eff = a.table.lv[it.lv].b_eff;
   const int wave = threadIdx.x >> 6;
-  const int64_t ki = it.chunk * kAttnQ + (w & 1) * kKeys16 + wave * kKW16 + (lane_id() & 15);
-  const int64_t krow = ki < b_eff ? int64_t(a.perm_k[it.slot0 + ki]) : -1;
-  Frag16<D> kf, vf;
-  load_frag16<D>(kf, rsrc_of(a.K, it.head, a.n, D), krow);
-  load_frag16<D>(vf, rsrc_of(a.V, it.head, a.n, D), krow);
-  Acc16<D> dk, dv;
-  zero16<D>(dk);
-  zero16<D>(dv);
-  kv16_sorted_loop<D, false>(a, sm, a.perm_q, it.slot0, b_eff, b_eff, it.head, kf, vf, dk, dv,
-                             1.f, 1.f, 0, true);
-  if (krow < 0) return;
-  finish_bucket_key16<D>(a, it, dv, false, krow);
-  finish_bucket_key16<D>(a, it, dk, true, krow);
+  const auto Kr = rsrc_of(a.K, it.head, a.n, D);
+  const auto Vr = rsrc_of(a.V, it.head, a.n, D);
+  const int64_t kbase = it.chunk * kAttnQ + wave * kKW16 + (lane_id() & 15);
+  if (b_eff > 2 * KT) {
+    for (int half = 0; half < 2; ++half) {
+      const int64_t ki = kbase + half * kKeys16;
+      const int64_t krow = ki < b_eff ? int64_t(a.perm_k[it.slot0 + ki]) : -1;
+      Frag16<D> kf, vf;
+      load_frag16<D>(kf, Kr, krow);
+      load_frag16<D>(vf, Vr, krow);
+      Acc16<D> dk, dv;
+      zero16<D>(dk);
+      zero16<D>(dv);
+      kv16_sorted_loop<D, false>(a, sm, a.perm_q, it.slot0, b_eff, b_eff, it.head, kf, vf, dk,
+                                 dv, 1.f, 1.f, 0, true);
+      if (krow >= 0) {
+        finish_bucket_key16<D>(a, it, dv, false, krow);
+        finish_bucket_key16<D>(a, it, dk, true, krow);
+      }
+    }
+    return;
+  }
+  // both query tiles resident
+  const auto Qr = rsrc_of(a.Q, it.head, a.n, D);
+  const auto dOr = rsrc_of(a.dO, it.head, a.n, D);
+  const int ntiles = (b_eff + KT - 1) / KT;
+  fill_queries(a, sm, a.perm_q, it.slot0, b_eff, it.head);
+  __syncthreads();
+  Pipe<bf16_t, D> pipe;
+  for (int t = 0; t < ntiles; ++t) {
+    BwdBuf<D>& b = sm.buf[t];
+    const int e0 = t * KT;
+    pipe.issue(b.t, Qr, dOr, true, [&](int row) { return int(sm.srow[e0 + row]); },
+               [&](int row) { return sm.sw[e0 + row]; });
+    if (threadIdx.x < KT) b.w2[threadIdx.x] = sm.sw2[e0 + threadIdx.x];
+  }
+  Offs16<D> o;
+  o.init();
+  for (int half = 0; half < 2; ++half) {
+    const int64_t ki = kbase + half * kKeys16;
+    const int64_t krow = ki < b_eff ? int64_t(a.perm_k[it.slot0 + ki]) : -1;
+    Frag16<D> kf, vf;
+    load_frag16<D>(kf, Kr, krow);
+    load_frag16<D>(vf, Vr, krow);
+    if (half == 0) {
+      pipe.commit(sm.buf[0].t, true);
+      __syncthreads();
+    }
+    Acc16<D> dk, dv;
+    zero16<D>(dk);
+    zero16<D>(dv);
+    for (int t = 0; t < ntiles; ++t) {
+      const int left = b_eff - t * KT;
+      kv_tile16<D, false, false, true>(sm.buf[t], o, kf, vf, dk, dv, a.scale_log2, 1.f, 1.f, 0,
+                                       0, true, left < KT ? left : KT, 0, 0);
+    }
+    if (krow >= 0) {
+      finish_bucket_key16<D>(a, it, dv, false, krow);
+      finish_bucket_key16<D>(a, it, dk, true, krow);
+    }
+  }
+  __syncthreads();   // the tiles are read until here
 }
 
 template <int D>
