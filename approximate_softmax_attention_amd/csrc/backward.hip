@@ -293,10 +293,8 @@ __device__ __forceinline__ int64_t level_slot(const BwdArgs& a, int lv, uint32_t
 }
 
 // Fragment reads issued ahead of their MFMA chains (see tile_dot) in the
-// query-major kernels and in the key-major dV sweep, which have the
-// registers for it.
+// query-major kernels, which have the registers for it.
 constexpr bool kQAhead = true;
-constexpr bool kVAhead = true;
 
 // ------------------------------------------------------ query-major tiles
 // One LDS tile of key slots for the wave's 32 queries: dQ^T += K^T dS^T.
@@ -338,24 +336,19 @@ __device__ __forceinline__ void q_tile(const BwdBuf<D>& b, const LaneOffs<bf16_t
 }
 
 // -------------------------------------------------------- key-major tiles
-// Passes of the key-major loops: dV, dK or both at once. With d = 128 the K,
-// V, dK and dV fragments of 32 key slots do not fit the 256 registers of a
-// wave at two waves per SIMD, so those kernels sweep the queries twice (dV,
-// then dK) and hold only what each sweep needs.
-enum { PASS_V = 1, PASS_K = 2, PASS_KV = 3 };
-template <int D> struct KvPasses {
-  static constexpr bool kSplit = D == 128;
-};
+// 32 key slots a wave (d = 64): K, V, dK and dV of 32 keys take 96 registers
+// there, so one sweep computes both gradients. (At d = 128 they would take
+// 192 and the kernels use the 16-key layout below.)
 
 // One LDS tile of queries for the wave's 32 key slots (weights om, nu):
-// dV^T += dO^T (w E) and/or dK^T += Q^T dS. Rows without a query carry
+// dV^T += dO^T (w E) and dK^T += Q^T dS. Rows without a query carry
 // t.w = +inf (E = 0). kUnit: om = nu = 1 (base case and bucket keys), when
 // dP's accumulator starts at -Delta so that it ends at dP - Delta and no
 // separate Delta values are held. kCausal: query index r valid iff r >= lim;
 // kBucketMask: valid iff r < mlo or r >= mhi (the tile rows inside the
 // slot's own bucket, a contiguous range since queries come in sorted order).
 // use_dp: some slot of the wave has om != 0 (else dP is not needed).
-template <int D, bool kCausal, bool kBucketMask, int PASS, bool kUnit>
+template <int D, bool kCausal, bool kBucketMask, bool kUnit>
 __device__ __forceinline__ void kv_tile(const BwdBuf<D>& b, const LaneOffs<bf16_t, D>& lo,
                                         const QFrag<bf16_t, D>& kf, const QFrag<bf16_t, D>& vf,
                                         f32x16* dk, f32x16* dv, float c, float om, float nu,
@@ -368,14 +361,14 @@ __device__ __forceinline__ void kv_tile(const BwdBuf<D>& b, const LaneOffs<bf16_
     if (kCausal && 32 * qb + 31 < skip_below) continue;   // the wave's keys all follow
     float lw[16], dl[16];
     rows16(b.t.w, qb, g, lw);
-    if (PASS & PASS_K) rows16(b.w2, qb, g, dl);
-    const f32x16 s = tile_dot<D, kVAhead && PASS == PASS_V>(b.t.k, lo, kf, qb);
+    rows16(b.w2, qb, g, dl);
+    const f32x16 s = tile_dot<D>(b.t.k, lo, kf, qb);
     f32x16 dp = zero16();
-    if (kUnit && (PASS & PASS_K)) {
+    if (kUnit) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) dp[i] = -dl[i];
       dp = tile_dot<D>(b.t.v, lo, vf, qb, dp);
-    } else if ((PASS & PASS_K) && use_dp) {
+    } else if (use_dp) {
       dp = tile_dot<D>(b.t.v, lo, vf, qb);
     }
     float e[16];
@@ -389,21 +382,19 @@ __device__ __forceinline__ void kv_tile(const BwdBuf<D>& b, const LaneOffs<bf16_
       e[i] = fast_exp2(ok ? fmaf(s[i], c, -lw[i]) : -INFINITY);
     }
     bf16x8_t pb[2];
-    if (PASS & PASS_V) {
+    if (kUnit || use_dp) {
       float pv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) pv[i] = om * e[i];
       pack_bf16(pv, pb);
-      tile_tr_acc<D, kVAhead && PASS == PASS_V>(b.t.v, lo, dv, pb, qb);
+      tile_tr_acc<D>(b.t.v, lo, dv, pb, qb);
     }
-    if (PASS & PASS_K) {
-      float pk[16];
+    float pk[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        pk[i] = kUnit ? e[i] * dp[i] : e[i] * (om * dp[i] - nu * dl[i]);
-      pack_bf16(pk, pb);
-      tile_tr_acc<D>(b.t.k, lo, dk, pb, qb);
-    }
+    for (int i = 0; i < 16; ++i)
+      pk[i] = kUnit ? e[i] * dp[i] : e[i] * (om * dp[i] - nu * dl[i]);
+    pack_bf16(pk, pb);
+    tile_tr_acc<D>(b.t.k, lo, dk, pb, qb);
   }
 }
 
@@ -680,7 +671,7 @@ __device__ __forceinline__ void q_exact_item(const BwdArgs& a, BwdSmem<D>& sm, u
 }
 
 // One sweep of the block's queries [q_lo, b_hi) for the wave's keys.
-template <int D, bool kCausal, int PASS>
+template <int D, bool kCausal>
 __device__ __forceinline__ void kv_exact_sweep(const BwdArgs& a, BwdSmem<D>& sm, int head,
                                                int64_t q_lo, int64_t b_hi, int64_t kw0,
                                                int64_t krow, const QFrag<bf16_t, D>& kf,
@@ -700,8 +691,7 @@ __device__ __forceinline__ void kv_exact_sweep(const BwdArgs& a, BwdSmem<D>& sm,
     BwdBuf<D>& b = sm.buf[t & 1];
     pipe.issue(b.t, Qr, dOr, true, [&](int row) { return row < nv ? int(r0 + row) : -1; },
                [&](int row) { return row < nv ? lse[r0 + row] * kLog2e : INFINITY; });
-    if ((PASS & PASS_K) && threadIdx.x < KT)
-      b.w2[threadIdx.x] = int(threadIdx.x) < nv ? dl[r0 + threadIdx.x] : 0.f;
+    if (threadIdx.x < KT) b.w2[threadIdx.x] = int(threadIdx.x) < nv ? dl[r0 + threadIdx.x] : 0.f;
   };
   issue(0);
   pipe.commit(sm.buf[0].t, true);
@@ -715,8 +705,8 @@ __device__ __forceinline__ void kv_exact_sweep(const BwdArgs& a, BwdSmem<D>& sm,
     const int lim = dk0 < 0 ? 0 : (dk0 > KT ? KT : int(dk0));
     const int64_t sb = kw0 - r0;
     const int skip_below = sb < 0 ? 0 : (sb > KT ? KT : int(sb));
-    kv_tile<D, kCausal, false, PASS, true>(sm.buf[t & 1], lo, kf, vf, dk, dv, a.scale_log2, 1.f,
-                                           1.f, 0, 0, true, nvalid, lim, skip_below);
+    kv_tile<D, kCausal, false, true>(sm.buf[t & 1], lo, kf, vf, dk, dv, a.scale_log2, 1.f, 1.f,
+                                     0, 0, true, nvalid, lim, skip_below);
     if (t + 1 < ntiles) pipe.commit(sm.buf[(t + 1) & 1].t, true);
     __syncthreads();
   }
@@ -758,25 +748,14 @@ __device__ __forceinline__ void kv_exact_item(const BwdArgs& a, BwdSmem<D>& sm, 
   const auto Vr = rsrc_of(a.V, head, a.n, D);
   QFrag<bf16_t, D> kf, vf;
   load_q<bf16_t, D>(kf, Kr, krow);
-  if constexpr (KvPasses<D>::kSplit) {
-    f32x16 acc[D / 32];
-    zero_acc<D>(acc);
-    kv_exact_sweep<D, kCausal, PASS_V>(a, sm, head, q_lo, b_hi, kw0, krow, kf, vf, nullptr, acc);
-    if (krow >= 0) finish_exact_key<D>(a, acc, false, blk, b_lo, krow, head);
-    load_q<bf16_t, D>(vf, Vr, krow);
-    zero_acc<D>(acc);
-    kv_exact_sweep<D, kCausal, PASS_K>(a, sm, head, q_lo, b_hi, kw0, krow, kf, vf, acc, nullptr);
-    if (krow >= 0) finish_exact_key<D>(a, acc, true, blk, b_lo, krow, head);
-  } else {
-    load_q<bf16_t, D>(vf, Vr, krow);
-    f32x16 dk[D / 32], dv[D / 32];
-    zero_acc<D>(dk);
-    zero_acc<D>(dv);
-    kv_exact_sweep<D, kCausal, PASS_KV>(a, sm, head, q_lo, b_hi, kw0, krow, kf, vf, dk, dv);
-    if (krow < 0) return;
-    finish_exact_key<D>(a, dv, false, blk, b_lo, krow, head);
-    finish_exact_key<D>(a, dk, true, blk, b_lo, krow, head);
-  }
+  load_q<bf16_t, D>(vf, Vr, krow);
+  f32x16 dk[D / 32], dv[D / 32];
+  zero_acc<D>(dk);
+  zero_acc<D>(dv);
+  kv_exact_sweep<D, kCausal>(a, sm, head, q_lo, b_hi, kw0, krow, kf, vf, dk, dv);
+  if (krow < 0) return;
+  finish_exact_key<D>(a, dv, false, blk, b_lo, krow, head);
+  finish_exact_key<D>(a, dk, true, blk, b_lo, krow, head);
 }
 
 // ------------------------------------------------------ bucket item decode
@@ -963,16 +942,14 @@ __device__ __forceinline__ void fill_queries(const BwdArgs& a, BwdSmem<D>& sm, c
 
 // Key-major sweep over `count` queries at sorted positions [p0, p0 + count)
 // of `perm` for the wave's key slots. kMask: a query in bucket bkt (its
-// position / b_eff) is skipped. staged: the rows, Lambda and Delta of the
-// first window are already in LDS (a previous sweep over the same queries
-// that fit one window).
-template <int D, bool kMask, int PASS>
+// position / b_eff) is skipped.
+template <int D, bool kMask>
 __device__ __forceinline__ void kv_sorted_loop(const BwdArgs& a, BwdSmem<D>& sm,
                                                const int32_t* perm, int64_t p0, int64_t count,
                                                int b_eff, int head, const QFrag<bf16_t, D>& kf,
                                                const QFrag<bf16_t, D>& vf, f32x16* dk,
                                                f32x16* dv, float om, float nu, int bkt,
-                                               bool use_dp, bool staged = false) {
+                                               bool use_dp) {
   constexpr int kWin = kSlotCap / KT;
   const auto Qr = rsrc_of(a.Q, head, a.n, D);
   const auto dOr = rsrc_of(a.dO, head, a.n, D);
@@ -985,12 +962,10 @@ __device__ __forceinline__ void kv_sorted_loop(const BwdArgs& a, BwdSmem<D>& sm,
     BwdBuf<D>& b = sm.buf[t & 1];
     pipe.issue(b.t, Qr, dOr, true, [&](int row) { return int(sm.srow[e0 + row]); },
                [&](int row) { return sm.sw[e0 + row]; });
-    if ((PASS & PASS_K) && threadIdx.x < KT) b.w2[threadIdx.x] = sm.sw2[e0 + threadIdx.x];
+    if (threadIdx.x < KT) b.w2[threadIdx.x] = sm.sw2[e0 + threadIdx.x];
   };
-  if (!staged) {
-    fill_queries(a, sm, perm, p0, count, head);
-    __syncthreads();
-  }
+  fill_queries(a, sm, perm, p0, count, head);
+  __syncthreads();
   issue(0);
   pipe.commit(sm.buf[0].t, true);
   __syncthreads();
@@ -1014,8 +989,8 @@ __device__ __forceinline__ void kv_sorted_loop(const BwdArgs& a, BwdSmem<D>& sm,
       mhi = int(last < 0 ? 0 : (last > KT ? KT : last));
     }
     // bucket keys (no mask) have om = nu = 1
-    kv_tile<D, false, kMask, PASS, !kMask>(sm.buf[t & 1], lo, kf, vf, dk, dv, a.scale_log2, om,
-                                           nu, mlo, mhi, use_dp, nvalid, 0, 0);
+    kv_tile<D, false, kMask, !kMask>(sm.buf[t & 1], lo, kf, vf, dk, dv, a.scale_log2, om, nu,
+                                     mlo, mhi, use_dp, nvalid, 0, 0);
     if (t + 1 < ntiles) pipe.commit(sm.buf[(t + 1) & 1].t, true);
     __syncthreads();
   }
@@ -1061,29 +1036,15 @@ __device__ __forceinline__ void kv_bucket_item(const BwdArgs& a, BwdSmem<D>& sm,
   const auto Vr = rsrc_of(a.V, it.head, a.n, D);
   QFrag<bf16_t, D> kf, vf;
   load_q<bf16_t, D>(kf, Kr, krow);
-  if constexpr (KvPasses<D>::kSplit) {
-    f32x16 acc[D / 32];
-    zero_acc<D>(acc);
-    kv_sorted_loop<D, false, PASS_V>(a, sm, a.perm_q, it.slot0, b_eff, b_eff, it.head, kf, vf,
-                                     nullptr, acc, 1.f, 1.f, 0, true);
-    if (krow >= 0) finish_bucket_key<D>(a, it, acc, false, krow);
-    load_q<bf16_t, D>(vf, Vr, krow);
-    zero_acc<D>(acc);
-    // a bucket of at most kSlotCap queries is still staged from the dV sweep
-    kv_sorted_loop<D, false, PASS_K>(a, sm, a.perm_q, it.slot0, b_eff, b_eff, it.head, kf, vf,
-                                     acc, nullptr, 1.f, 1.f, 0, true, b_eff <= kSlotCap);
-    if (krow >= 0) finish_bucket_key<D>(a, it, acc, true, krow);
-  } else {
-    load_q<bf16_t, D>(vf, Vr, krow);
-    f32x16 dk[D / 32], dv[D / 32];
-    zero_acc<D>(dk);
-    zero_acc<D>(dv);
-    kv_sorted_loop<D, false, PASS_KV>(a, sm, a.perm_q, it.slot0, b_eff, b_eff, it.head, kf, vf,
-                                      dk, dv, 1.f, 1.f, 0, true);
-    if (krow < 0) return;
-    finish_bucket_key<D>(a, it, dv, false, krow);
-    finish_bucket_key<D>(a, it, dk, true, krow);
-  }
+  load_q<bf16_t, D>(vf, Vr, krow);
+  f32x16 dk[D / 32], dv[D / 32];
+  zero_acc<D>(dk);
+  zero_acc<D>(dv);
+  kv_sorted_loop<D, false>(a, sm, a.perm_q, it.slot0, b_eff, b_eff, it.head, kf, vf, dk, dv,
+                           1.f, 1.f, 0, true);
+  if (krow < 0) return;
+  finish_bucket_key<D>(a, it, dv, false, krow);
+  finish_bucket_key<D>(a, it, dk, true, krow);
 }
 
 // Partial dK, dV of kAttnQ sample slots of one node (uniform list then
@@ -1135,37 +1096,16 @@ __device__ __forceinline__ void kv_sample_item(const BwdArgs& a, BwdSmem<D>& sm,
   const int32_t* perm = a.perm_q + seg0;
   // uniform slots have om = 0: no dV and no dP for them
   const bool wave_om = __ballot(om != 0.f) != 0;
-  if constexpr (KvPasses<D>::kSplit) {
-    f32x16 acc[D / 32];
-    // the work-group skips the dV sweep when none of its slots has om != 0
-    if (__syncthreads_or(om != 0.f)) {
-      zero_acc<D>(acc);
-      kv_sorted_loop<D, true, PASS_V>(a, sm, perm, p0, count, L.b_eff, head, kf, vf, nullptr,
-                                      acc, om, nu, bkt, wave_om);
-      if (krow >= 0) store_row_f32<D>(acc, a.slot_dv + idx * D);
-    } else if (krow >= 0) {
-      zero_acc<D>(acc);
-      store_row_f32<D>(acc, a.slot_dv + idx * D);
-    }
-    load_q<bf16_t, D>(vf, Vr, krow);
-    zero_acc<D>(acc);
-    kv_sorted_loop<D, true, PASS_K>(a, sm, perm, p0, count, L.b_eff, head, kf, vf, acc, nullptr,
-                                    om, nu, bkt, wave_om);
-    if (krow < 0) return;
-    scale_acc<D>(acc, a.scale);
-    store_row_f32<D>(acc, a.slot_dk + idx * D);
-  } else {
-    load_q<bf16_t, D>(vf, Vr, krow);
-    f32x16 dk[D / 32], dv[D / 32];
-    zero_acc<D>(dk);
-    zero_acc<D>(dv);
-    kv_sorted_loop<D, true, PASS_KV>(a, sm, perm, p0, count, L.b_eff, head, kf, vf, dk, dv, om,
-                                     nu, bkt, wave_om);
-    if (krow < 0) return;
-    scale_acc<D>(dk, a.scale);
-    store_row_f32<D>(dk, a.slot_dk + idx * D);
-    store_row_f32<D>(dv, a.slot_dv + idx * D);
-  }
+  load_q<bf16_t, D>(vf, Vr, krow);
+  f32x16 dk[D / 32], dv[D / 32];
+  zero_acc<D>(dk);
+  zero_acc<D>(dv);
+  kv_sorted_loop<D, true>(a, sm, perm, p0, count, L.b_eff, head, kf, vf, dk, dv, om, nu, bkt,
+                          wave_om);
+  if (krow < 0) return;
+  scale_acc<D>(dk, a.scale);
+  store_row_f32<D>(dk, a.slot_dk + idx * D);
+  store_row_f32<D>(dv, a.slot_dv + idx * D);
 }
 
 // ------------------------------------- key-major items, 16 keys a wave (d = 128)
