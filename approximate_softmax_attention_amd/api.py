@@ -6,7 +6,14 @@ torch's current HIP stream. Every step of the computation runs in the
 library's HIP kernels; there is no other code path.
 
 Tensors are [heads, n, d] (or [batch, heads, n, d], folded into heads),
-contiguous, on a ROCm device, dtype torch.bfloat16 or torch.float32.
+contiguous, on a ROCm device, dtype torch.bfloat16 or torch.float32 (the
+backward pass takes bfloat16).
+
+Entry points: forward, forward_rope, backward, exact, exact_backward,
+rowsum_estimate, sortlsh_hash, hyperplanes, rope_table, workspace_bytes,
+backward_workspace_bytes, workspace_layout; HyperAttentionFunction wraps
+forward and backward for torch.autograd; KernelTimer collects the library's
+per-kernel hipEvent timings.
 """
 
 import ctypes
