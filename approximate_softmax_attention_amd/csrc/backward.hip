@@ -482,17 +482,29 @@ template <int D>
 __device__ __forceinline__ void tr_acc16(const bf16_t* arr, const Offs16<D>& o, Acc16<D>& acc,
                                          bf16x8_t p, int r0) {
   const char* base = reinterpret_cast<const char*>(arr) + r0 * D * 2;
-  __builtin_amdgcn_s_setprio(kMfmaPrio);
+  // the transposing reads of kGroup column blocks are issued ahead of their
+  // MFMAs (4 kGroup registers in flight; all eight at d = 128 measured
+  // best, with four the kernels were about 1% slower)
+  constexpr int kGroup = 8;
 #pragma unroll
-  for (int mb = 0; mb < D / 16; ++mb) {
-    const v4i16_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + o.tr[mb]));
-    const v4i16_t x1 =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + o.tr[mb] + 16 * D * 2));
-    const bf16x8_t a =
-        __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-    acc.a[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p, acc.a[mb], 0, 0, 0);
+  for (int m0 = 0; m0 < D / 16; m0 += kGroup) {
+    v4i16_t x[kGroup][2];
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      x[j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + o.tr[m0 + j]));
+      x[j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16_t*)(base + o.tr[m0 + j] + 16 * D * 2));
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_setprio(kMfmaPrio);
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const bf16x8_t a = __builtin_bit_cast(
+          bf16x8_t, __builtin_shufflevector(x[j][0], x[j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+      acc.a[m0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p, acc.a[m0 + j], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
   }
-  __builtin_amdgcn_s_setprio(0);
 }
 
 // One LDS tile of queries for the wave's 16 key slots: dV^T += dO^T (w E),
