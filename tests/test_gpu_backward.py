@@ -141,3 +141,21 @@ def test_backward_deterministic_and_autograd():
     for g, h, t in zip(grads, again, (qa, ka, va)):
         assert torch.equal(g, h)
         assert torch.equal(g, t.grad)
+
+
+def test_backward_batch_dimension_folds_into_heads():
+    """[batch, heads, n, d] tensors give the gradients of the same call on
+    [batch * heads, n, d]."""
+    banner("hyperattention backward with a batch dimension")
+    import torch
+    (q, k, v, o, lse, do, kw) = _run_case("noncausal_d64")[1]
+    api = _api()
+    H, n, d = q.shape
+    shape4 = (2, H // 2, n, d)
+    g3 = api.backward(q, k, v, o, lse, do, **kw)
+    g4 = api.backward(q.reshape(shape4), k.reshape(shape4), v.reshape(shape4),
+                      o.reshape(shape4), lse.reshape(2, H // 2, n), do.reshape(shape4), **kw)
+    _sync()
+    for a, b in zip(g3, g4):
+        assert b.shape == shape4
+        assert torch.equal(a, b.reshape(a.shape))
