@@ -19,10 +19,13 @@
 //  query-major (dQ): a wave owns 32 query rows (their Q and dO fragments in
 //    registers) and streams the rows' key slots through LDS: S^T = K Q^T,
 //    dP^T = V dO^T, then dQ^T += K^T dS^T with the transposing read of K.
-//  key-major (dK, dV): a wave owns 32 key slots (K and V fragments) and
-//    streams the queries that use them: S = Q K^T, dP = dO V^T, then
-//    dV^T += dO^T (w E) and dK^T += Q^T dS with transposing reads of the
-//    dO and Q tiles.
+//  key-major (dK, dV): a wave owns a group of key slots (K and V
+//    fragments) and streams the queries that use them: S = Q K^T,
+//    dP = dO V^T, then dV^T += dO^T (w E) and dK^T += Q^T dS with
+//    transposing reads of the dO and Q tiles, both gradients in one sweep.
+//    32 slots a wave on v_mfma_f32_32x32x16_bf16 at d = 64; 16 slots a wave
+//    on v_mfma_f32_16x16x32_bf16 at d = 128, where the fragments and
+//    accumulators of 32 slots would not fit a wave's registers.
 // HyperAttention: the query-major kernel takes each bucket's queries against
 // the bucket's keys and the node's two samples; the key-major kernel takes
 // each bucket's keys against the bucket's queries, and, separately, every

@@ -34,15 +34,19 @@ def log(msg):
 
 def kernel_source_hash(backward=False):
     """sha256 over the sources of the forward pass's kernels (file names and
-    contents), or with backward=True over every kernel source."""
+    code), or with backward=True over every kernel source. Comments and blank
+    lines are left out, so that editing a comment keeps a profile valid."""
     import hashlib
+    import re
     h = hashlib.sha256()
     src = os.path.join(ROOT, "approximate_softmax_attention_amd", "csrc")
     for name in sorted(os.listdir(src)):
         if name.endswith((".hip", ".h", ".cpp")) and (backward or name != "backward.hip"):
             h.update(name.encode())
-            with open(os.path.join(src, name), "rb") as f:
-                h.update(f.read())
+            with open(os.path.join(src, name)) as f:
+                text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+            code = [re.sub(r"//.*", "", line).rstrip() for line in text.splitlines()]
+            h.update("\n".join(line for line in code if line.strip()).encode())
     return h.hexdigest()
 
 
