@@ -92,12 +92,11 @@ def _add_slots(dQ, dK, dV, Qr, Kr, Vr, qs, keys, dOr, lam, delta, w, u, scale):
 
 
 def hyperattention_backward(Q, K, V, dO, *, causal, b, m, r=8, recursion_base=4096, seed=0,
-                            G=None, head_ids=None, forward=None):
+                            G=None, head_ids=None):
     """dQ, dK, dV [H, n, d] (fp64) of sum(dO * O) for the HyperAttention output O.
 
-    Arguments are those of hyperattention.hyperattention. forward: optional
-    (O, lse) of that call on the same inputs (computed here when absent).
-    The buckets and sample lists are the forward pass's.
+    Arguments are those of hyperattention.hyperattention; the forward output,
+    lse, buckets and sample lists are that function's.
     """
     H, n, d = np.shape(Q)
     scale = 1.0 / np.sqrt(d)
@@ -105,8 +104,6 @@ def hyperattention_backward(Q, K, V, dO, *, causal, b, m, r=8, recursion_base=40
     O, lse = ha.hyperattention(Q, K, V, causal=causal, b=b, m=m, r=r,
                                recursion_base=recursion_base, seed=seed, artifacts=art,
                                G=G, head_ids=head_ids)
-    if forward is not None:
-        O, lse = _as64(forward[0]), _as64(forward[1])
     dQ = np.zeros((H, n, d))
     dK = np.zeros((H, n, d))
     dV = np.zeros((H, n, np.shape(V)[2]))
