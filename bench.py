@@ -71,6 +71,28 @@ def profiled_traffic(workload, kernel, backward=False):
     return val
 
 
+def profiled_mfma(workload, kernel):
+    """(MFMA-busy fraction, clock in GHz) of `kernel` from the committed
+    rocprofv3 MFMA counter summary, or None when there is none or the kernel
+    sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"hyperattn_{workload}_mfma_counters.md")
+    if not os.path.exists(path):
+        return None
+    sha, busy, clock = None, None, None
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("source-sha256:"):
+                sha = line.split(":", 1)[1].strip()
+            elif line.startswith(f"mfma-busy {kernel}:"):
+                busy = float(line.split(":", 1)[1])
+            elif line.startswith(f"clock-ghz {kernel}:"):
+                clock = float(line.split(":", 1)[1])
+    if sha is None or sha != kernel_source_hash(backward=True) or busy is None:
+        return None
+    return busy, clock
+
+
 def algorithmic_flops(w):
     """MFMA flops the method must do, per kernel (per launch)."""
     H, n, d, b, m = w.heads, w.n, w.d, w.b, w.m
@@ -94,6 +116,27 @@ def algorithmic_flops(w):
         be, mm = min(b, n), min(m, n)
         out["bucket_attention"] = H * n * (4 * be * d + 2 * mm * d + 4 * mm * d)
     return out
+
+
+def hbm_bytes(w):
+    """Algorithmic HBM bytes per launch of the bandwidth-bound forward
+    kernels: the hash reads Q and K and writes one code byte per row; the
+    V-norm pass reads V and writes the fp64 squared norms; the sort scatter
+    reads a code byte and writes a 4-byte perm and a 4-byte rank entry per
+    element of every level's segments (n per head per level)."""
+    H, n, d = w.heads, w.n, w.d
+    es = 2 if w.dtype == "bf16" else 4
+    levels = 0
+    if w.causal:
+        size = n
+        while size > w.recursion_base:
+            size //= 2
+            levels += 1
+    else:
+        levels = 1
+    return {"hash": 2 * H * n * d * es + 2 * H * n,
+            "vnorm_rows": H * n * d * es + H * n * 8,
+            "sort_scatter": levels * H * n * 9}
 
 
 def exact_flops(w):
@@ -373,6 +416,9 @@ def backward_mode(args, torch, api, wl):
            "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
                         "unit": "TFLOP/s", "frac": achieved / PEAK_BF16, "traffic": traffic,
                         "kernel": dom, "flops_per_launch": kfl[dom]}}
+    counters = profiled_mfma(w.name, dom)
+    if counters is not None:
+        rec["roofline"]["mfma_busy"], rec["roofline"]["clock_ghz"] = counters
     if not args.no_exact:
         Oe = torch.empty_like(Q)
         le = torch.empty_like(lse)
@@ -422,7 +468,7 @@ def cpu_baseline_backward(w):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -486,16 +532,20 @@ def main():
     log(f"timing {args.steps} steps")
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     with api.KernelTimer() as kt:
         torch.cuda.synchronize()
         e0.record(stream)
         t0 = time.perf_counter()
-        for _ in range(args.steps):
+        marks[0].record(stream)
+        for i in range(args.steps):
             api.forward(Q, K, V, **kw)
+            marks[i + 1].record(stream)
         e1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     tokens_per_s = w.n / (ms / 1e3)
     log(f"{ms:.3f} ms/step, {tokens_per_s:.4g} tokens/s (wall {wall / args.steps * 1e3:.3f} ms)")
 
@@ -509,12 +559,23 @@ def main():
         if name in kernels:
             kernels[name]["tflops"] = f / (kernels[name]["avg_ms"] / 1e3) / 1e12
             kernels[name]["mfma_frac"] = f / (kernels[name]["avg_ms"] / 1e3) / peak
+    for name, nbytes in hbm_bytes(w).items():
+        if name in kernels:
+            t = kernels[name]["avg_ms"] / 1e3
+            kernels[name]["gbs"] = nbytes / t / 1e9
+            kernels[name]["hbm_frac"] = nbytes / t / PEAK_HBM
+            counted = profiled_traffic(w.name, name)
+            if counted is not None:
+                kernels[name]["counter_gbs"] = counted / t / 1e9
     if dom in flops:
         ach = flops[dom] / (kernels[dom]["avg_ms"] / 1e3)
         roofline = {"bound": "mfma", "achieved": ach / 1e12, "peak": peak / 1e12,
                     "unit": "TFLOP/s", "frac": ach / peak,
                     "traffic": profiled_traffic(w.name, dom),
                     "kernel": dom, "flops_per_launch": flops[dom]}
+        counters = profiled_mfma(w.name, dom)
+        if counters is not None:
+            roofline["mfma_busy"], roofline["clock_ghz"] = counters
     else:
         roofline = {"bound": "hbm", "achieved": None, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                     "frac": None, "traffic": None, "kernel": dom}
@@ -523,6 +584,7 @@ def main():
     result = {
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "ms_per_step_median": per_step[len(per_step) // 2], "ms_per_step_min": per_step[0],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded iid N(0,1), RoPE on Q,K)",
         "config": {"workload": w.name, "batch": 1, "heads": w.heads, "seq_len": w.n,
