@@ -39,6 +39,9 @@ SIGNATURES = {
                                   _i32, _i32, _i32, _i32, _i32, _u64, _i32, _vp, _sz, _vp]),
     "hyperattn_backward_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                                  _i32]),
+    "hyperattn_backward_rope": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32,
+                                       _i32, _i32, _i32, _i32, _i32, _i32, _u64, _c.c_double,
+                                       _i32, _vp, _sz, _vp]),
     "exact_attention_backward": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32,
                                         _i32, _i32, _i32, _vp, _sz, _vp]),
     "exact_attention_backward_workspace_bytes": (_sz, [_i64, _i32]),

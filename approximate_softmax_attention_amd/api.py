@@ -9,10 +9,10 @@ Tensors are [heads, n, d] (or [batch, heads, n, d], folded into heads),
 contiguous, on a ROCm device, dtype torch.bfloat16 or torch.float32 (the
 backward pass takes bfloat16).
 
-Entry points: forward, forward_rope, backward, exact, exact_backward,
+Entry points: forward, forward_rope, backward, backward_rope, exact, exact_backward,
 rowsum_estimate, sortlsh_hash, hyperplanes, rope_table, workspace_bytes,
-backward_workspace_bytes, workspace_layout; HyperAttentionFunction wraps
-forward and backward for torch.autograd; KernelTimer collects the library's
+backward_workspace_bytes, workspace_layout; HyperAttentionFunction and
+HyperAttentionRopeFunction wrap forward and backward for torch.autograd; KernelTimer collects the library's
 per-kernel hipEvent timings.
 """
 
@@ -194,6 +194,25 @@ def backward(q, k, v, o, lse, do, *, causal, b=256, m=256, r=8, recursion_base=4
     return dq.reshape(shape), dk.reshape(shape), dv.reshape(shape)
 
 
+def backward_rope(q_rot, k_rot, v, o, lse, do, *, causal, rope_base=10000.0, b=256, m=256,
+                  r=8, recursion_base=4096, seed=0, workspace=None):
+    """Gradients (dq, dk, dv) for a forward_rope call: dq and dk are those of
+    the rows before their rotary embedding. q_rot and k_rot are the rotated
+    rows forward_rope returned (return_rotated=True)."""
+    shape, q, k, v, o, lse, do = _grad_inputs(q_rot, k_rot, v, o, lse, do)
+    H, n, d = q.shape
+    dt = _dtype_code(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nb = backward_workspace_bytes(n, d, H, causal=causal, b=b, m=m, r=r,
+                                  recursion_base=recursion_base, dtype=dt)
+    ws = workspace if workspace is not None else alloc_workspace(nb, q.device)
+    check(lib().hyperattn_backward_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                        _ptr(dq), _ptr(dk), _ptr(dv), n, d, H, int(causal), b, m,
+                                        recursion_base, r, seed, float(rope_base), dt, _ptr(ws),
+                                        ws.numel(), _stream(q.device)))
+    return dq.reshape(shape), dk.reshape(shape), dv.reshape(shape)
+
+
 def exact_backward(q, k, v, o, lse, do, *, causal=False):
     """Gradients (dq, dk, dv) of exact attention (the library's own kernels)."""
     shape, q, k, v, o, lse, do = _grad_inputs(q, k, v, o, lse, do)
@@ -226,6 +245,28 @@ class HyperAttentionFunction(torch.autograd.Function):
         q, k, v, o, lse = ctx.saved_tensors
         dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), **ctx.args)
         return dq, dk, dv, None, None, None, None, None, None
+
+
+class HyperAttentionRopeFunction(torch.autograd.Function):
+    """torch.autograd wrapper of forward_rope (rotary embedding on the device)
+    and backward_rope. HyperAttentionRopeFunction.apply(q, k, v, causal, b, m,
+    r, recursion_base, seed, rope_base) with q and k before rotation."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal, b, m, r, recursion_base, seed, rope_base):
+        o, lse, qr, kr = forward_rope(q, k, v, causal=causal, rope_base=rope_base, b=b, m=m,
+                                      r=r, recursion_base=recursion_base, seed=seed,
+                                      return_lse=True, return_rotated=True)
+        ctx.save_for_backward(qr, kr, v, o, lse)
+        ctx.args = dict(causal=causal, b=b, m=m, r=r, recursion_base=recursion_base, seed=seed,
+                        rope_base=rope_base)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        qr, kr, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = backward_rope(qr, kr, v, o, lse, do.contiguous(), **ctx.args)
+        return dq, dk, dv, None, None, None, None, None, None, None
 
 
 def rowsum_estimate(q, k, *, b=256, m=256, r=8, seed=0):

@@ -288,12 +288,44 @@ size_t hyperattn_backward_workspace_bytes(int64_t n, int d, int heads, int causa
   return p.total;
 }
 
+namespace {
+int backward_impl(const void* Q, const void* K, const void* V, const void* O, const float* lse,
+                  const void* dO, void* dQ, void* dK, void* dV, int64_t n, int d, int heads,
+                  int causal, int b, int m, int recursion_base, int r, uint64_t seed, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
+}  // namespace
+
 int hyperattn_backward(const void* Q, const void* K, const void* V, const void* O,
                        const float* lse, const void* dO, void* dQ, void* dK, void* dV, int64_t n,
                        int d, int heads, int causal, int b, int m, int recursion_base, int r,
                        uint64_t seed, int dtype, void* workspace, size_t workspace_bytes,
                        void* stream) {
   g_error.clear();
+  return backward_impl(Q, K, V, O, lse, dO, dQ, dK, dV, n, d, heads, causal, b, m,
+                       recursion_base, r, seed, dtype, workspace, workspace_bytes, stream);
+}
+
+int hyperattn_backward_rope(const void* Q_rot, const void* K_rot, const void* V, const void* O,
+                            const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                            int64_t n, int d, int heads, int causal, int b, int m,
+                            int recursion_base, int r, uint64_t seed, double rope_base,
+                            int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  g_error.clear();
+  if (!(rope_base > 1.0 && std::isfinite(rope_base)))
+    return fail(HA_ERR_UNSUPPORTED, "rope_base=%g must be a finite number above 1", rope_base);
+  int rc = backward_impl(Q_rot, K_rot, V, O, lse, dO, dQ, dK, dV, n, d, heads, causal, b, m,
+                         recursion_base, r, seed, dtype, workspace, workspace_bytes, stream);
+  if (rc != HA_OK || n == 0 || heads == 0) return rc;
+  const float* tab = nullptr;
+  if ((rc = device_rope_table(n, d, rope_base, &tab)) != HA_OK) return rc;
+  return launch_rope_adjoint(dQ, dK, n, d, heads, dtype, tab, static_cast<hipStream_t>(stream));
+}
+
+namespace {
+int backward_impl(const void* Q, const void* K, const void* V, const void* O, const float* lse,
+                  const void* dO, void* dQ, void* dK, void* dV, int64_t n, int d, int heads,
+                  int causal, int b, int m, int recursion_base, int r, uint64_t seed, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream) {
   Plan p;
   int rc = make_plan(p, n, d, heads, causal, b, m, recursion_base, r, dtype, true, true);
   if (rc != HA_OK) return rc;
@@ -324,6 +356,7 @@ int hyperattn_backward(const void* Q, const void* K, const void* V, const void* 
   if (p.causal) rc = launch_bwd_exact(io, n, d, heads, 1, p.base_block, &p, workspace, queue, s);
   return rc;
 }
+}  // namespace
 
 size_t exact_attention_backward_workspace_bytes(int64_t n, int heads) {
   g_error.clear();

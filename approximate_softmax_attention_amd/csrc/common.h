@@ -129,6 +129,10 @@ int launch_hash(const Plan& p, const void* Q, const void* K, const void* V,
 int launch_rope(const Plan& p, const void* Q, const void* K, void* Qr, void* Kr,
                 const float* tab, bool hash, const float* G, const uint16_t* Gb, void* ws,
                 hipStream_t s);
+// In place: the gradients of the rows before rotation (dQ, dK [heads][n][d])
+// from those of the rotated rows, i.e. the adjoint rotation by -i theta_t.
+int launch_rope_adjoint(void* dQ, void* dK, int64_t n, int d, int heads, int dtype,
+                        const float* tab, hipStream_t s);
 // cos and sin of i * base^(-2t/d) for rows i < n and pairs t < d/2, as
 // [n][d/2][2], fp64 from the C library rounded to fp32 (host), and its
 // per-device cache.

@@ -95,6 +95,53 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(
     }
 }
 
+// ------------------------------------------------- adjoint of the rotation
+// Gradients of the rows before rotation from those of the rotated rows, in
+// place: the rotation of each pair is orthogonal, so its adjoint rotates by
+// -i theta_t:
+//   g_t       =  g'_t cos(i theta_t) + g'_{t+d/2} sin(i theta_t)
+//   g_{t+d/2} = -g'_t sin(i theta_t) + g'_{t+d/2} cos(i theta_t)
+// in fp32 (each product and sum rounded once), then to the row type. Thread
+// layout as rope_kernel's; X holds `sides` tensors one after another.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void rope_adjoint_kernel(T* X0, T* X1,
+                                                                const float* __restrict__ tab,
+                                                                int64_t n, int heads) {
+  constexpr int TPR = D / 8;
+  constexpr int RPB = kThreads / TPR;
+  const int64_t row = int64_t(blockIdx.x) * RPB + threadIdx.x / TPR;
+  const int t0 = (threadIdx.x % TPR) * 4;
+  if (row >= n) return;
+  float c[4], s[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    c[j] = tab[(row * (D / 2) + t0 + j) * 2];
+    s[j] = -tab[(row * (D / 2) + t0 + j) * 2 + 1];
+  }
+  for (int z = 0; z < 2; ++z)
+    for (int h = 0; h < heads; ++h) {
+      T* x = (z == 0 ? X0 : X1) + (int64_t(h) * n + row) * D;
+      T lo[4], hi[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lo[j] = x[t0 + j];
+        hi[j] = x[t0 + j + D / 2];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float y1, y2;
+        rotate_pair(to_f32<T>(lo[j]), to_f32<T>(hi[j]), c[j], s[j], y1, y2);
+        lo[j] = from_f32<T>(y1);
+        hi[j] = from_f32<T>(y2);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[t0 + j] = lo[j];
+        x[t0 + j + D / 2] = hi[j];
+      }
+    }
+}
+
 // ------------------------------------------- rotation + hash (bf16 rows)
 // Rotated value of element t of a raw bf16 row (for the exact-sign fallback).
 template <int D>
@@ -320,6 +367,25 @@ int device_rope_table(int64_t n, int d, double base, const float** out) {
 // Rotates Q and K into Qr and Kr; with hash, also writes the sortLSH codes
 // of the rotated rows into the plan's code regions (bf16: one fused pass;
 // fp32: rotation, then the hash kernel over the rotated rows).
+int launch_rope_adjoint(void* dQ, void* dK, int64_t n, int d, int heads, int dtype,
+                        const float* tab, hipStream_t s) {
+  if (n == 0 || heads == 0) return HA_OK;
+  ProfRange pr("rope_adjoint", s);
+  const int tpr = d / 8;
+  const dim3 grid(unsigned(ceil_div(n, int64_t(kThreads / tpr))));
+  if (dtype == HA_BF16) {
+    auto k = d == 128 ? rope_adjoint_kernel<bf16_t, 128> : rope_adjoint_kernel<bf16_t, 64>;
+    hipLaunchKernelGGL(k, grid, dim3(kThreads), 0, s, static_cast<bf16_t*>(dQ),
+                       static_cast<bf16_t*>(dK), tab, n, heads);
+  } else {
+    auto k = d == 128 ? rope_adjoint_kernel<float, 128> : rope_adjoint_kernel<float, 64>;
+    hipLaunchKernelGGL(k, grid, dim3(kThreads), 0, s, static_cast<float*>(dQ),
+                       static_cast<float*>(dK), tab, n, heads);
+  }
+  HA_LAUNCH_CHECK("rope_adjoint");
+  return HA_OK;
+}
+
 int launch_rope(const Plan& p, const void* Q, const void* K, void* Qr, void* Kr,
                 const float* tab, bool hash, const float* G, const uint16_t* Gb, void* ws,
                 hipStream_t s) {

@@ -226,6 +226,29 @@ size_t hyperattn_backward_workspace_bytes(int64_t n, int d, int heads,
                                           int dtype);
 
 /*
+ * hyperattn_backward_rope — hyperattn_backward for a call of
+ * hyperattn_forward_rope: dQ and dK are the gradients of the rows BEFORE
+ * their rotary embedding. Q_rot and K_rot are the rotated rows that
+ * hyperattn_forward_rope returned. The library runs hyperattn_backward on
+ * them, then applies the adjoint of the rotation to the two gradients in
+ * place. The rotation of each pair is orthogonal, so its adjoint rotates by
+ * -i theta_t:
+ *   g_t = g'_t cos + g'_{t+d/2} sin,   g_{t+d/2} = -g'_t sin + g'_{t+d/2} cos,
+ * in fp32 with each product and sum rounded once, with rope_table's cos and
+ * sin, then rounded to bf16. The rounding of the rotated rows to bf16 is
+ * piecewise constant and, as with the sketch, carries no gradient.
+ * Other arguments, outputs, workspace and errors as hyperattn_backward;
+ * rope_base as hyperattn_forward_rope.
+ */
+int hyperattn_backward_rope(const void* Q_rot, const void* K_rot,
+                            const void* V, const void* O, const float* lse,
+                            const void* dO, void* dQ, void* dK, void* dV,
+                            int64_t n, int d, int heads, int causal, int b,
+                            int m, int recursion_base, int r, uint64_t seed,
+                            double rope_base, int dtype, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * exact_attention_backward — gradients of exact_attention_forward (HA page,
  * "Method overview"; causal: mask M^C): with P = D^-1 A and Delta_i =
  * dO_i . O_i, dV = P^T dO, dS = P (dO V^T - Delta 1^T), dQ = dS K / sqrt(d),

@@ -14,6 +14,11 @@ attention uses). Reading taken, the usual rotary form:
   angle i * theta_t, cos and sin are fp64 values;
 * for bf16 rows the result is rounded to the nearest bf16 (ties to even).
 The fp32 rotation errs by about 1e-7 relative, far inside a bf16 step.
+
+The gradient through the embedding (rope_adjoint) is the transpose of the
+rotation: each pair's rotation is orthogonal, so the transpose turns by
+-i theta_t. The bf16 rounding of the rotated rows is piecewise constant and
+carries no gradient (the reading the backward pass takes for the sketch).
 """
 
 import math
@@ -56,4 +61,24 @@ def rope(X, base=10000.0, dtype="bf16", table=None):
     e = x1 * s
     f = x2 * c
     out = np.concatenate([a - b, e + f], axis=1).astype(np.float32)
+    return round_bf16_array(out) if dtype == "bf16" else out
+
+
+def rope_adjoint(G, base=10000.0, dtype="fp64", table=None):
+    """Gradient of the rows before rotation, from G [n, d], the gradient of
+    the rotated rows: the transpose of each pair's rotation,
+      g_t       =  g'_t cos(i theta_t) + g'_{t+d/2} sin(i theta_t)
+      g_{t+d/2} = -g'_t sin(i theta_t) + g'_{t+d/2} cos(i theta_t).
+    dtype "fp64": exact arithmetic on the fp64 table; "fp32" / "bf16": fp32
+    cos, sin, products and sums each rounded once, then (bf16) rounded to
+    the nearest bf16."""
+    n, d = G.shape
+    half = d // 2
+    c, s = table if table is not None else angle_table(n, d, base)
+    ft = np.float64 if dtype == "fp64" else np.float32
+    c = np.asarray(c, dtype=ft)
+    s = np.asarray(s, dtype=ft)
+    g1 = np.asarray(G[:, :half], dtype=ft)
+    g2 = np.asarray(G[:, half:], dtype=ft)
+    out = np.concatenate([g1 * c + g2 * s, g2 * c - g1 * s], axis=1).astype(ft)
     return round_bf16_array(out) if dtype == "bf16" else out

@@ -99,6 +99,25 @@ def test_backward_validates_before_any_device_call():
     assert rc == -4
 
 
+def test_backward_rope_validates_before_any_device_call():
+    lib = L()
+    p = _vp(256)
+    need = lib.hyperattn_backward_workspace_bytes(1024, 64, 1, 0, 128, 128, 4096, 8, 1)
+    for base in (1.0, float("nan"), float("inf")):
+        rc = lib.hyperattn_backward_rope(p, p, p, p, p, p, p, p, p, 1024, 64, 1, 0, 128, 128,
+                                         4096, 8, 1, base, 1, p, need, None)
+        assert rc == -3 and "rope_base" in _lib.last_error()
+    rc = lib.hyperattn_backward_rope(p, p, p, p, None, p, p, p, p, 1024, 64, 1, 0, 128, 128,
+                                     4096, 8, 1, 10000.0, 1, p, need, None)
+    assert rc == -1 and "lse" in _lib.last_error()
+    rc = lib.hyperattn_backward_rope(p, p, p, p, p, p, p, p, p, 1024, 64, 1, 0, 128, 128, 4096,
+                                     8, 1, 10000.0, 0, p, need, None)
+    assert rc != 0 and "bf16" in _lib.last_error()
+    assert lib.hyperattn_backward_rope(None, None, None, None, None, None, None, None, None, 0,
+                                       64, 2, 1, 256, 256, 4096, 8, 1, 10000.0, 1, None, 0,
+                                       None) == 0
+
+
 def test_backward_layout_regions():
     from approximate_softmax_attention_amd import api
     fwd = api.workspace_layout(8192, 128, 4, causal=1, b=256, m=256, recursion_base=1024)

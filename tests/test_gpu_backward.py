@@ -159,3 +159,47 @@ def test_backward_batch_dimension_folds_into_heads():
     for a, b in zip(g3, g4):
         assert b.shape == shape4
         assert torch.equal(a, b.reshape(a.shape))
+
+
+@pytest.mark.parametrize("name", ["causal_d128", "local_mask"])
+def test_backward_rope(name):
+    """hyperattn_backward_rope: the gradients of the rows before their rotary
+    embedding, against the oracle's backward on the oracle-rotated rows
+    followed by the oracle's fp64 transposed rotation; the autograd wrapper
+    returns the same bytes."""
+    banner(f"hyperattention backward through RoPE ({name})")
+    import torch
+    from oracle import rope as orope
+    base, changes = BACKWARD_CASES[name]
+    w = wl.scaled(wl.WORKLOADS[base], **changes)
+    Q, K, V, _ = wl.make_inputs(w)
+    dO = wl.make_grad(w)
+    api = _api()
+    q, k, v, do = (to_dev(x, "bf16") for x in (Q, K, V, dO))
+    kw = dict(causal=w.causal, b=w.b, m=w.m, r=w.r, recursion_base=w.recursion_base,
+              seed=w.method_seed)
+    o, lse, qr, kr = api.forward_rope(q, k, v, return_lse=True, return_rotated=True, **kw)
+    grads = api.backward_rope(qr, kr, v, o, lse, do, **kw)
+    plain = api.backward(qr, kr, v, o, lse, do, **kw)
+    qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+    out = api.HyperAttentionRopeFunction.apply(qa, ka, va, kw["causal"], kw["b"], kw["m"],
+                                               kw["r"], kw["recursion_base"], kw["seed"],
+                                               10000.0)
+    out.backward(do)
+    _sync()
+    assert torch.equal(plain[2], grads[2])         # dV does not see the rotation
+    assert torch.equal(out.detach(), o)
+    for g, t in zip(grads, (qa, ka, va)):
+        assert torch.equal(g, t.grad)
+    tab = orope.angle_table(w.n, w.d, 10000.0)
+    Qo = np.stack([orope.rope(Q[h], dtype="bf16", table=tab) for h in range(w.heads)])
+    Ko = np.stack([orope.rope(K[h], dtype="bf16", table=tab) for h in range(w.heads)])
+    assert np.array_equal(to_np(qr), Qo) and np.array_equal(to_np(kr), Ko)
+    dq, dk, dv = obw.hyperattention_backward(Qo, Ko, V, dO, causal=w.causal, b=w.b, m=w.m,
+                                             r=w.r, recursion_base=w.recursion_base,
+                                             seed=w.method_seed)
+    refs = [np.stack([orope.rope_adjoint(g[h], table=tab) for h in range(w.heads)])
+            for g in (dq, dk)] + [dv]
+    errs = _errs(grads, refs)
+    print(f"  dQ {errs[0]:.2e} dK {errs[1]:.2e} dV {errs[2]:.2e}", flush=True)
+    assert max(errs) <= TOL["bf16"], errs

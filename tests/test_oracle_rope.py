@@ -58,3 +58,66 @@ def test_bf16_rounding_of_the_fp32_result():
     # 1 + 3 * 2^-9 rounds up to 1 + 2^-7
     assert np.array_equal(rope.round_bf16_array(vals),
                           np.array([1.0, 1.0, 1.0078125, -2.5], dtype=np.float32))
+
+
+def test_adjoint_identity():
+    """<R x, y> = <x, R^T y> for the rotation R of every row: a wrong sign,
+    a swapped half or a forward turn in place of the backward one breaks it."""
+    rs = np.random.default_rng(3)
+    n, d = 40, 32
+    X = rs.standard_normal((n, d))
+    Y = rs.standard_normal((n, d))
+    tab = rope.angle_table(n, d, 10000.0)
+    # the forward rotation in fp64 straight from the table, pair by pair
+    c, s = tab
+    RX = np.empty_like(X)
+    for t in range(d // 2):
+        RX[:, t] = X[:, t] * c[:, t] - X[:, t + d // 2] * s[:, t]
+        RX[:, t + d // 2] = X[:, t] * s[:, t] + X[:, t + d // 2] * c[:, t]
+    lhs = np.einsum("ij,ij->i", RX, Y)
+    rhs = np.einsum("ij,ij->i", X, rope.rope_adjoint(Y, table=tab))
+    assert np.abs(lhs - rhs).max() < 1e-12 * np.abs(lhs).max()
+
+
+def test_adjoint_inverts_the_rotation():
+    """R^T R = I: the adjoint of the rotated rows gives the rows back (fp32
+    rotation, fp64 adjoint: within a few fp32 steps)."""
+    rs = np.random.default_rng(4)
+    X = rs.standard_normal((64, 64)).astype(np.float32)
+    Y = rope.rope(X, dtype="fp32")
+    back = rope.rope_adjoint(Y.astype(np.float64))
+    assert np.abs(back - X).max() < 1e-5
+    # position 0 is the identity, also for the fp32 and bf16 forms
+    Xb = rope.round_bf16_array(X[:1])
+    assert np.array_equal(rope.rope_adjoint(Xb, dtype="bf16"), Xb)
+
+
+def test_adjoint_two_dimensional_closed_form():
+    # d = 2: row i = (cos i, sin i) turns back onto (1, 0)
+    n = 5
+    G = np.array([[math.cos(i), math.sin(i)] for i in range(n)])
+    out = rope.rope_adjoint(G, base=10000.0)
+    assert np.allclose(out, np.tile([1.0, 0.0], (n, 1)), atol=1e-15)
+
+
+def test_adjoint_is_the_gradient_by_finite_differences():
+    """d/dX of sum(G * rope(X)) is rope_adjoint(G), checked by central
+    differences of the fp64 rotation on a few coordinates."""
+    rs = np.random.default_rng(5)
+    n, d = 6, 8
+    tab = rope.angle_table(n, d, 10000.0)
+    c, s = tab
+    X = rs.standard_normal((n, d))
+    G = rs.standard_normal((n, d))
+
+    def f(Z):
+        z1, z2 = Z[:, : d // 2], Z[:, d // 2:]
+        return float(np.sum(G * np.concatenate([z1 * c - z2 * s, z1 * s + z2 * c], axis=1)))
+
+    grad = rope.rope_adjoint(G, table=tab)
+    h = 1e-6
+    for i, j in ((0, 0), (3, 1), (5, 5), (2, 7)):
+        E = np.zeros_like(X)
+        E[i, j] = h
+        fd = (f(X + E) - f(X - E)) / (2 * h)
+        assert abs(fd - grad[i, j]) < 1e-7
