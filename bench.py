@@ -410,7 +410,10 @@ def backward_mode(args, torch, api, wl):
     for k in kfl:
         if k in kernels:
             kernels[k]["tflops"] = kfl[k] / (kernels[k]["avg_ms"] / 1e3) / 1e12
-    rec = {"mode": "forward_backward", "workload": w.name, "steps": args.steps,
+    rec = {"mode": "forward_backward",
+           "metric": "causal HyperAttention fwd+bwd tokens/s at the same workload",
+           "value": w.n / (ms / 1e3), "unit": "tokens/s", "higher_is_better": True,
+           "dtype": "bf16", "data": "synthetic", "workload": w.name, "steps": args.steps,
            "ms_per_step": ms, "tokens_per_s": w.n / (ms / 1e3), "kernels": kernels,
            "backward_ms_approx": bwd_ms, "backward_mfma": mfma,
            "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
