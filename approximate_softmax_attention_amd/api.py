@@ -60,6 +60,34 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
+def _check_buffer(t, name, like, numel, dtype):
+    """A caller-supplied output: contiguous, on `like`'s device, of `dtype`
+    and `numel` elements (the library writes exactly that many)."""
+    if t is None:
+        return
+    if t.device != like.device or t.dtype != dtype or not t.is_contiguous() or \
+            t.numel() != numel:
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of {numel} elements on "
+                         f"{like.device}")
+
+
+def _workspace(ws, nbytes, like):
+    """The caller's workspace (a contiguous uint8 tensor on `like`'s device,
+    its size checked by the library) or a new one of nbytes."""
+    if ws is None:
+        return alloc_workspace(nbytes, like.device)
+    if ws.device != like.device or ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous uint8 tensor on {like.device}")
+    return ws
+
+
+def _call(like, fn, *args):
+    """Calls a library entry point with `like`'s device current (the library
+    launches on the current device and keeps per-device tables)."""
+    with torch.cuda.device(like.device):
+        check(fn(*args, _stream(like.device)))
+
+
 def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
@@ -88,16 +116,17 @@ def forward(q, k, v, *, causal, b=256, m=256, r=8, recursion_base=4096, seed=0,
     shape, q, k, v = _qkv(q, k, v)
     H, n, d = q.shape
     dt = _dtype_code(q)
+    _check_buffer(out, "out", q, q.numel(), q.dtype)
+    _check_buffer(lse_out, "lse_out", q, H * n, torch.float32)
     o = out if out is not None else torch.empty_like(q)
     lse = lse_out
     if return_lse and lse is None:
         lse = torch.empty((H, n), dtype=torch.float32, device=q.device)
     nb = workspace_bytes(n, d, H, causal=causal, b=b, m=m, r=r,
                          recursion_base=recursion_base, dtype=dt)
-    ws = workspace if workspace is not None else alloc_workspace(nb, q.device)
-    check(lib().hyperattn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), n, d, H,
-                                  int(causal), b, m, recursion_base, r, seed, dt, _ptr(ws),
-                                  ws.numel(), _stream(q.device)))
+    ws = _workspace(workspace, nb, q)
+    _call(q, lib().hyperattn_forward, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), n, d, H,
+          int(causal), b, m, recursion_base, r, seed, dt, _ptr(ws), ws.numel())
     o = o.reshape(shape)
     if return_lse:
         return o, lse.reshape(shape[:-1])
@@ -118,11 +147,10 @@ def forward_rope(q, k, v, *, causal, rope_base=10000.0, b=256, m=256, r=8,
     lse = torch.empty((H, n), dtype=torch.float32, device=q.device) if return_lse else None
     nb = workspace_bytes(n, d, H, causal=causal, b=b, m=m, r=r,
                          recursion_base=recursion_base, dtype=dt)
-    ws = workspace if workspace is not None else alloc_workspace(nb, q.device)
-    check(lib().hyperattn_forward_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(qr), _ptr(kr), _ptr(o),
-                                       _ptr(lse), n, d, H, int(causal), b, m, recursion_base, r,
-                                       seed, float(rope_base), dt, _ptr(ws), ws.numel(),
-                                       _stream(q.device)))
+    ws = _workspace(workspace, nb, q)
+    _call(q, lib().hyperattn_forward_rope, _ptr(q), _ptr(k), _ptr(v), _ptr(qr), _ptr(kr), _ptr(o),
+          _ptr(lse), n, d, H, int(causal), b, m, recursion_base, r, seed, float(rope_base), dt,
+          _ptr(ws), ws.numel())
     out = [o.reshape(shape)]
     if return_lse:
         out.append(lse.reshape(shape[:-1]))
@@ -143,12 +171,14 @@ def exact(q, k, v, *, causal=False, return_lse=False, out=None, lse_out=None):
     """Exact softmax attention (the library's own kernel)."""
     shape, q, k, v = _qkv(q, k, v)
     H, n, d = q.shape
+    _check_buffer(out, "out", q, q.numel(), q.dtype)
+    _check_buffer(lse_out, "lse_out", q, H * n, torch.float32)
     o = out if out is not None else torch.empty_like(q)
     lse = lse_out
     if return_lse and lse is None:
         lse = torch.empty((H, n), dtype=torch.float32, device=q.device)
-    check(lib().exact_attention_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), n, d, H,
-                                        int(causal), _dtype_code(q), _stream(q.device)))
+    _call(q, lib().exact_attention_forward, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), n, d,
+          H, int(causal), _dtype_code(q))
     o = o.reshape(shape)
     if return_lse:
         return o, lse.reshape(shape[:-1])
@@ -162,7 +192,8 @@ def _grad_inputs(q, k, v, o, lse, do):
         if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
             raise ValueError(f"{name} must have the shape, dtype and device of q")
     H, n, _ = q.shape
-    if not lse.is_contiguous() or lse.dtype != torch.float32 or lse.numel() != H * n:
+    if lse.device != q.device or not lse.is_contiguous() or lse.dtype != torch.float32 or \
+            lse.numel() != H * n:
         raise ValueError("lse must be the forward pass's contiguous fp32 [heads, n] output")
     return shape, q, k, v, o, lse, do
 
@@ -186,11 +217,10 @@ def backward(q, k, v, o, lse, do, *, causal, b=256, m=256, r=8, recursion_base=4
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     nb = backward_workspace_bytes(n, d, H, causal=causal, b=b, m=m, r=r,
                                   recursion_base=recursion_base, dtype=dt)
-    ws = workspace if workspace is not None else alloc_workspace(nb, q.device)
-    check(lib().hyperattn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
-                                   _ptr(dq), _ptr(dk), _ptr(dv), n, d, H, int(causal), b, m,
-                                   recursion_base, r, seed, dt, _ptr(ws), ws.numel(),
-                                   _stream(q.device)))
+    ws = _workspace(workspace, nb, q)
+    _call(q, lib().hyperattn_backward, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+          _ptr(dq), _ptr(dk), _ptr(dv), n, d, H, int(causal), b, m, recursion_base, r, seed, dt,
+          _ptr(ws), ws.numel())
     return dq.reshape(shape), dk.reshape(shape), dv.reshape(shape)
 
 
@@ -205,11 +235,10 @@ def backward_rope(q_rot, k_rot, v, o, lse, do, *, causal, rope_base=10000.0, b=2
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     nb = backward_workspace_bytes(n, d, H, causal=causal, b=b, m=m, r=r,
                                   recursion_base=recursion_base, dtype=dt)
-    ws = workspace if workspace is not None else alloc_workspace(nb, q.device)
-    check(lib().hyperattn_backward_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
-                                        _ptr(dq), _ptr(dk), _ptr(dv), n, d, H, int(causal), b, m,
-                                        recursion_base, r, seed, float(rope_base), dt, _ptr(ws),
-                                        ws.numel(), _stream(q.device)))
+    ws = _workspace(workspace, nb, q)
+    _call(q, lib().hyperattn_backward_rope, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+          _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), n, d, H, int(causal), b, m, recursion_base, r,
+          seed, float(rope_base), dt, _ptr(ws), ws.numel())
     return dq.reshape(shape), dk.reshape(shape), dv.reshape(shape)
 
 
@@ -219,10 +248,9 @@ def exact_backward(q, k, v, o, lse, do, *, causal=False):
     H, n, d = q.shape
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = alloc_workspace(lib().exact_attention_backward_workspace_bytes(n, H), q.device)
-    check(lib().exact_attention_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
-                                         _ptr(dq), _ptr(dk), _ptr(dv), n, d, H, int(causal),
-                                         _dtype_code(q), _ptr(ws), ws.numel(),
-                                         _stream(q.device)))
+    _call(q, lib().exact_attention_backward, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+          _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), n, d, H, int(causal), _dtype_code(q), _ptr(ws),
+          ws.numel())
     return dq.reshape(shape), dk.reshape(shape), dv.reshape(shape)
 
 
@@ -277,8 +305,8 @@ def rowsum_estimate(q, k, *, b=256, m=256, r=8, seed=0):
     out = torch.empty((H, n), dtype=torch.float32, device=q.device)
     nb = workspace_bytes(n, d, H, causal=False, b=b, m=m, r=r, recursion_base=1, dtype=dt)
     ws = alloc_workspace(nb, q.device)
-    check(lib().rowsum_estimate(_ptr(q), _ptr(k), n, d, H, b, m, r, seed, dt, _ptr(out),
-                                _ptr(ws), ws.numel(), _stream(q.device)))
+    _call(q, lib().rowsum_estimate, _ptr(q), _ptr(k), n, d, H, b, m, r, seed, dt, _ptr(out),
+          _ptr(ws), ws.numel())
     return out.reshape(shape[:-1])
 
 
@@ -291,8 +319,8 @@ def sortlsh_hash(x, *, r=8, seed=0, with_perm=False):
     perm = torch.empty((H, n), dtype=torch.int32, device=x.device) if with_perm else None
     nb = lib().sortlsh_hash_workspace_bytes(n, H, int(with_perm))
     ws = alloc_workspace(nb, x.device) if with_perm else None
-    check(lib().sortlsh_hash(_ptr(x), n, d, H, r, seed, _dtype_code(x), _ptr(codes), _ptr(perm),
-                             _ptr(ws), nb, _stream(x.device)))
+    _call(x, lib().sortlsh_hash, _ptr(x), n, d, H, r, seed, _dtype_code(x), _ptr(codes),
+          _ptr(perm), _ptr(ws), nb)
     codes = codes.reshape(shape[:-1])
     return (codes, perm.reshape(shape[:-1])) if with_perm else codes
 

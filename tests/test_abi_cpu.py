@@ -258,3 +258,27 @@ def test_product_path_has_no_cpu_fallback():
             mod.lib()
     finally:
         mod._LIB, mod.LIB_PATH = saved
+
+
+def test_binding_checks_caller_buffers():
+    """Caller-supplied outputs and workspaces are checked before any call: the
+    library writes exactly q.numel() output elements and H * n lse values."""
+    import torch
+    from approximate_softmax_attention_amd import api
+    q = torch.zeros(2, 8, 64, dtype=torch.bfloat16)
+    api._check_buffer(None, "out", q, q.numel(), q.dtype)
+    api._check_buffer(torch.empty(2, 8, 64, dtype=torch.bfloat16), "out", q, q.numel(), q.dtype)
+    api._check_buffer(torch.empty(1, 2, 8, 64, dtype=torch.bfloat16), "out", q, q.numel(),
+                      q.dtype)
+    bad = [torch.empty(2, 8, 63, dtype=torch.bfloat16),          # too few elements
+           torch.empty(2, 8, 64, dtype=torch.float32),           # wrong dtype
+           torch.empty(2, 64, 8, dtype=torch.bfloat16).transpose(1, 2)]   # not contiguous
+    for t in bad:
+        with pytest.raises(ValueError):
+            api._check_buffer(t, "out", q, q.numel(), q.dtype)
+    with pytest.raises(ValueError):
+        api._check_buffer(torch.empty(2, 9), "lse_out", q, 16, torch.float32)
+    ws = torch.empty(4096, dtype=torch.uint8)
+    assert api._workspace(ws, 4096, q) is ws
+    with pytest.raises(ValueError):
+        api._workspace(torch.empty(1024, dtype=torch.float32), 4096, q)

@@ -327,6 +327,21 @@ def test_empty_and_error_paths():
     q3 = torch.randn((1, 96, 32), device="cuda", dtype=torch.bfloat16)
     with pytest.raises(HyperAttnError, match="HA_ERR_UNSUPPORTED"):
         api.exact(q3, q3, q3)
+    # caller buffers of the wrong size or type are refused before any launch
+    q = torch.randn((1, 128, 64), device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="out"):
+        api.forward(q, q, q, causal=False, b=64, m=32, out=torch.empty_like(q)[:, :64])
+    with pytest.raises(ValueError, match="lse_out"):
+        api.exact(q, q, q, return_lse=True,
+                  lse_out=torch.empty((1, 64), device="cuda", dtype=torch.float32))
+    with pytest.raises(ValueError, match="workspace"):
+        api.forward(q, q, q, causal=False, b=64, m=32,
+                    workspace=torch.empty(1 << 20, device="cuda", dtype=torch.float32))
+    # a workspace one byte short is refused by the library itself
+    nb = api.workspace_bytes(128, 64, 1, causal=False, b=64, m=32)
+    with pytest.raises(HyperAttnError):
+        api.forward(q, q, q, causal=False, b=64, m=32,
+                    workspace=torch.empty(nb - 1, device="cuda", dtype=torch.uint8))
 
 
 def test_deterministic_repeat():
