@@ -19,6 +19,10 @@ Recipe (numpy only, deterministic):
 * Values are then rounded to fp32 and, for bf16 workloads, to bf16 by
   round-to-nearest-even on the fp32 bit pattern. Both sides of every parity
   check read these same bytes.
+* Very long single heads (make_inputs_large, for the tests at the largest
+  sizes the library takes) draw the same distribution in row chunks of
+  2^18, chunk c of (data seed, tensor, head) from its own PCG64 stream
+  [data seed, tensor, head, c + 1], on a thread pool.
 """
 
 from dataclasses import dataclass, field
@@ -154,6 +158,33 @@ def make_grad(w, heads=None):
             x32 = bf16_bits_to_f32(f32_to_bf16_bits(x32))
         out.append(x32)
     return np.stack(out)
+
+
+def make_inputs_large(w, chunk=1 << 18, workers=None):
+    """(Q, K, V) as fp32 arrays [heads, n, d] for very long heads: iid N(0, 1)
+    in row chunks, each from its own stream, generated in parallel (no
+    planting or RoPE), rounded like make_head's values."""
+    import concurrent.futures as cf
+    import os
+    if w.planted or w.rope:
+        raise ValueError("make_inputs_large draws plain iid inputs only")
+    workers = workers or max(1, min(16, len(os.sched_getaffinity(0))))
+    out = [np.empty((w.heads, w.n, w.d), dtype=np.float32) for _ in range(3)]
+    jobs = [(t, h, c) for t in range(3) for h in range(w.heads)
+            for c in range((w.n + chunk - 1) // chunk)]
+
+    def fill(job):
+        t, h, c = job
+        lo, hi = c * chunk, min(w.n, (c + 1) * chunk)
+        g = np.random.Generator(np.random.PCG64([w.data_seed, t, h, c + 1]))
+        x32 = g.standard_normal((hi - lo, w.d)).astype(np.float32)
+        if w.dtype == "bf16":
+            x32 = bf16_bits_to_f32(f32_to_bf16_bits(x32))
+        out[t][h, lo:hi] = x32
+
+    with cf.ThreadPoolExecutor(workers) as ex:
+        list(ex.map(fill, jobs))
+    return out[0], out[1], out[2]
 
 
 def make_inputs_parallel(w, heads=None, workers=None):

@@ -190,3 +190,49 @@ def test_fullsize_rope_forward_and_backward_sampled_rows():
         assert max(errs) <= TOL[w.dtype], errs
     for g in grads:
         assert torch.isfinite(g).all()
+
+
+MAX_CASES = {
+    # the longest head the library takes at d = 128 in bf16: n d 2 bytes just
+    # under 2 GiB, so row byte offsets reach the top of their 31-bit range
+    "noncausal_n8388352": dict(n=8388352, causal=False),
+    # causal: eleven halvings down to base blocks of 3072 rows
+    "causal_n6291456": dict(n=6291456, causal=True),
+}
+
+
+@pytest.mark.parametrize("case", sorted(MAX_CASES))
+def test_max_head_size_sampled_rows(case):
+    """One head at the largest size the library takes, with the local block
+    mask (r = 0) so that the oracle's cost stays in seconds: every integer
+    artefact bit-exact, O and lse on sampled rows; then the sortLSH hash
+    (r = 8) of the same head, its codes bit-exact on the sampled rows."""
+    import torch
+
+    from approximate_softmax_attention_amd import api
+    from oracle import sortlsh
+    from tests.gpu_util import to_dev
+
+    w = wl.scaled(wl.WORKLOADS["longctx_noncausal_n131072_d64_h8_bf16"], heads=1, d=128, r=0,
+                  **MAX_CASES[case])
+    banner(f"max size {case}: inputs")
+    Q, K, V = wl.make_inputs_large(w)
+    kw = dict(causal=w.causal, b=w.b, m=w.m, r=w.r, recursion_base=w.recursion_base)
+    banner(f"max size {case}: gpu forward")
+    O, L, ws, layout = run_forward(w, Q, K, V)
+    rows = sample_rows(w, count=48)
+    banner(f"max size {case}: oracle on {len(rows)} rows")
+    art = {}
+    Oref, Lref = oha.hyperattention(Q, K, V, seed=w.method_seed, rows=rows, artifacts=art, **kw)
+    check_artifacts(w, ws, layout, art, [0])
+    ref = Oref[0][rows]
+    err = np.abs(to_np(O[0][rows]) - ref).max() / np.abs(ref).max()
+    lerr = np.abs(to_np(L[0][rows]) - Lref[0][rows]).max()
+    print(f"{case}: max-rel {err:.2e}, lse {lerr:.2e}", flush=True)
+    assert err <= TOL[w.dtype] and lerr <= TOL[w.dtype]
+    del O, L, ws
+    banner(f"max size {case}: sortLSH hash with r = 8")
+    codes = api.sortlsh_hash(to_dev(Q, w.dtype), r=8, seed=w.method_seed)
+    torch.cuda.synchronize()
+    G = sortlsh.hyperplanes(w.method_seed, 1, 8, w.d)[0]
+    assert np.array_equal(codes[0].cpu().numpy()[rows], sortlsh.hash_codes(Q[0][rows], G))
