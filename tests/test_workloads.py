@@ -46,3 +46,17 @@ def test_inputs_deterministic_and_planted():
     # stored values are bf16-representable
     bits = wl.f32_to_bf16_bits(V)
     assert np.array_equal(wl.bf16_bits_to_f32(bits), V)
+
+
+def test_make_inputs_large_is_deterministic_and_rounded():
+    w = wl.scaled(wl.WORKLOADS["longctx_noncausal_n131072_d64_h8_bf16"], heads=2, n=1000)
+    a = wl.make_inputs_large(w, chunk=256, workers=1)
+    b = wl.make_inputs_large(w, chunk=256, workers=4)
+    for x, y in zip(a, b):
+        assert x.shape == (2, 1000, 64) and np.array_equal(x, y)
+        # bf16 values: the low 16 bits of every fp32 pattern are zero
+        assert not np.any(x.view(np.uint32) & 0xFFFF)
+        assert abs(x.mean()) < 0.05 and abs(x.std() - 1) < 0.05
+    # Q, K, V and the heads are different streams; chunks too
+    assert not np.array_equal(a[0], a[1]) and not np.array_equal(a[0][0], a[0][1])
+    assert not np.array_equal(a[0][0, :256], a[0][0, 256:512])
