@@ -104,6 +104,6 @@ def header_functions():
 WS_REGIONS = ["CODES_Q", "CODES_K", "VNORM_A", "VNORM_W", "VNORM_P", "VNORM_BLK",
               "PERM_Q", "PERM_K", "RANK_K", "SORT_HIST", "SORT_OFFS",
               "U_IDX", "U_BKT", "V_IDX", "V_BKT", "V_W", "NODE_META",
-              "PART_O", "PART_LSE", "SCHED",
+              "PART_O", "PART_LSE", "SCHED", "PLANES",
               "DELTA", "PART_DQ", "PART_DK", "PART_DV",
               "SLOT_FIRST", "SLOT_NEXT", "SLOT_DK", "SLOT_DV"]

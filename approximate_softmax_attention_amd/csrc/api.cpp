@@ -199,7 +199,9 @@ int forward_impl(const void* Q, const void* K, const void* V, void* O, float* ls
   if (rc != HA_OK) return rc;
   const float* G = nullptr;
   const uint16_t* Gb = nullptr;
-  if ((rc = device_hyperplanes(seed, heads, r, d, &G, &Gb)) != HA_OK) return rc;
+  if ((rc = device_hyperplanes(seed, heads, r, d, &G, &Gb,
+                               static_cast<char*>(workspace) + p.off[HA_WS_PLANES], s)) != HA_OK)
+    return rc;
   if (rope) {
     if ((rc = launch_rope(p, Q, K, rope->Qr, rope->Kr, tab, true, G, Gb, workspace, s)) != HA_OK)
       return rc;
@@ -272,7 +274,10 @@ int rowsum_estimate(const void* Q, const void* K, int64_t n, int d, int heads, i
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float* G = nullptr;
   const uint16_t* Gb = nullptr;
-  if ((rc = device_hyperplanes(seed, heads, r, d, &G, &Gb)) != HA_OK) return rc;
+  if ((rc = device_hyperplanes(seed, heads, r, d, &G, &Gb,
+                               static_cast<char*>(workspace) + full.off[HA_WS_PLANES], s)) !=
+      HA_OK)
+    return rc;
   if ((rc = launch_hash(p, Q, K, nullptr, G, Gb, workspace, s)) != HA_OK) return rc;
   if ((rc = launch_sort(p, workspace, 2, s)) != HA_OK) return rc;
   if ((rc = launch_samples(p, seed, workspace, s)) != HA_OK) return rc;
@@ -345,7 +350,8 @@ int backward_impl(const void* Q, const void* K, const void* V, const void* O, co
   // the forward pass's buckets and sample lists, recomputed from the seed
   const float* G = nullptr;
   const uint16_t* Gb = nullptr;
-  if ((rc = device_hyperplanes(seed, heads, r, d, &G, &Gb)) != HA_OK) return rc;
+  if ((rc = device_hyperplanes(seed, heads, r, d, &G, &Gb, w + p.off[HA_WS_PLANES], s)) != HA_OK)
+    return rc;
   if ((rc = launch_hash(p, Q, K, V, G, Gb, workspace, s)) != HA_OK) return rc;
   if ((rc = launch_vnorm_scan(p, workspace, s)) != HA_OK) return rc;
   if ((rc = launch_sort(p, workspace, 2, s)) != HA_OK) return rc;

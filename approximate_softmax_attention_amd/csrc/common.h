@@ -112,11 +112,17 @@ int make_plan(Plan& p, int64_t n, int d, int heads, int causal, int b, int m,
               int base, int r, int dtype, bool product, bool backward = false);
 int check_workspace(const Plan& p, const void* ws, size_t ws_bytes);
 
-// Hyperplanes on the device for (seed, heads, r, d); cached per device.
+// Hyperplanes on the device for (seed, heads, r, d).
 // *out: fp32 values [heads][r][d]; *out_bf16 (optional): the same values as
 // bf16 bit patterns in [heads][16][d], hyperplanes r..15 zero.
+// Up to 16 keys are kept per device (copied once). For other keys, with a
+// stage (hyperplane_stage_bytes device bytes, e.g. a workspace region) the
+// values are copied there on stream s; without one the least recently used
+// entry is replaced, which waits for the device first.
 int device_hyperplanes(uint64_t seed, int heads, int r, int d, const float** out,
-                       const uint16_t** out_bf16 = nullptr);
+                       const uint16_t** out_bf16 = nullptr, void* stage = nullptr,
+                       hipStream_t s = nullptr);
+int64_t hyperplane_stage_bytes(int heads, int r, int d);
 void host_hyperplanes(uint64_t seed, int heads, int r, int d, float* G);
 
 // --------------------------------------------------------------- launchers
@@ -137,6 +143,8 @@ int launch_rope_adjoint(void* dQ, void* dK, int64_t n, int d, int heads, int dty
 // [n][d/2][2], fp64 from the C library rounded to fp32 (host), and its
 // per-device cache.
 void host_rope_table(int64_t n, int d, double base, float* out);
+// Device cos/sin table of at least n positions for (d, base); rows are
+// positions, so a longer table serves every shorter n. Grows by doubling.
 int device_rope_table(int64_t n, int d, double base, const float** out);
 int launch_hash_one(const void* X, int64_t n, int d, int heads, int r, int dtype,
                     const float* G, const uint16_t* Gb, uint8_t* codes, hipStream_t s);

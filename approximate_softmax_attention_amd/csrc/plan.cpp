@@ -134,6 +134,7 @@ int make_plan(Plan& p, int64_t n, int d, int heads, int causal, int b, int m,
     add_region(p, HA_WS_PART_LSE, slots * 4);
   }
   add_region(p, HA_WS_SCHED, 2 * kQueues * 4);
+  add_region(p, HA_WS_PLANES, hyperplane_stage_bytes(heads, r, d));
   if (backward) {
     add_region(p, HA_WS_DELTA, H * n * 4);
     if (p.causal && p.L > 0) {

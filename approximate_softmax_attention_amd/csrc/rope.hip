@@ -21,6 +21,7 @@
 // Signs the fp32 MFMA projection cannot settle are recomputed in fp64 in
 // order t from the raw row and the table (the rotation is recomputed exactly).
 // fp32 rows, and rotation without hashing: rope_kernel.
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 #include <vector>
@@ -305,8 +306,9 @@ struct TableEntry {
 };
 std::mutex g_mu;
 std::vector<TableEntry> g_cache;
+std::vector<float*> g_retired;   // tables outgrown while launches may still read them
 uint64_t g_clock = 0;
-constexpr size_t kCacheEntries = 4;
+constexpr size_t kCacheEntries = 4;   // (d, base) pairs per device
 
 }  // namespace
 
@@ -331,26 +333,25 @@ int device_rope_table(int64_t n, int d, double base, const float** out) {
   int dev = 0;
   HA_HIP_TRY(hipGetDevice(&dev));
   std::lock_guard<std::mutex> lock(g_mu);
-  for (TableEntry& e : g_cache)
-    if (e.device == dev && e.n == n && e.d == d && e.base == base) {
-      e.stamp = ++g_clock;
-      *out = e.ptr;
-      return HA_OK;
-    }
-  if (g_cache.size() >= kCacheEntries) {
-    size_t old = 0;
-    for (size_t i = 1; i < g_cache.size(); ++i)
-      if (g_cache[i].stamp < g_cache[old].stamp) old = i;
-    int cur = dev;
-    HA_HIP_TRY(hipSetDevice(g_cache[old].device));
-    HA_HIP_TRY(hipDeviceSynchronize());          // earlier launches may still read it
-    HA_HIP_TRY(hipFree(g_cache[old].ptr));
-    HA_HIP_TRY(hipSetDevice(cur));
-    g_cache.erase(g_cache.begin() + old);
+  TableEntry* hit = nullptr;
+  size_t held = 0;
+  for (TableEntry& e : g_cache) {
+    if (e.device != dev) continue;
+    ++held;
+    if (e.d == d && e.base == base) hit = &e;
   }
-  const size_t count = size_t(n) * size_t(d);     // n rows x d/2 pairs x (cos, sin)
+  if (hit && hit->n >= n) {      // rows are positions: a longer table serves
+    hit->stamp = ++g_clock;
+    *out = hit->ptr;
+    return HA_OK;
+  }
+  // a new or longer table: at least twice the old length, so that a run of
+  // growing n reallocates only a logarithmic number of times
+  int64_t rows = n;
+  if (hit) rows = std::max(n, std::min(2 * hit->n, (int64_t(1) << 31) - 1));
+  const size_t count = size_t(rows) * size_t(d);  // rows x d/2 pairs x (cos, sin)
   std::vector<float> host(count);
-  host_rope_table(n, d, base, host.data());
+  host_rope_table(rows, d, base, host.data());
   float* ptr = nullptr;
   HA_HIP_TRY(hipMalloc(&ptr, count * sizeof(float)));
   const hipError_t e = hipMemcpy(ptr, host.data(), count * sizeof(float), hipMemcpyHostToDevice);
@@ -359,7 +360,29 @@ int device_rope_table(int64_t n, int d, double base, const float** out) {
     return fail(HA_ERR_HIP, "copy of the rotary table to the device failed: %s",
                 hipGetErrorString(e));
   }
-  g_cache.push_back(TableEntry{dev, n, d, base, ptr, ++g_clock});
+  if (hit) {
+    // launches already enqueued may still read the shorter table: it is
+    // kept (never freed) rather than waited for; with doubling, the tables
+    // kept add up to less than the current one
+    g_retired.push_back(hit->ptr);
+    hit->ptr = ptr;
+    hit->n = rows;
+    hit->stamp = ++g_clock;
+    *out = ptr;
+    return HA_OK;
+  }
+  if (held >= kCacheEntries) {
+    // another (d, base) pair past the cache's size: replace this device's
+    // least recently used table after draining the device
+    size_t old = g_cache.size();
+    for (size_t i = 0; i < g_cache.size(); ++i)
+      if (g_cache[i].device == dev && (old == g_cache.size() || g_cache[i].stamp < g_cache[old].stamp))
+        old = i;
+    HA_HIP_TRY(hipDeviceSynchronize());
+    HA_HIP_TRY(hipFree(g_cache[old].ptr));
+    g_cache.erase(g_cache.begin() + old);
+  }
+  g_cache.push_back(TableEntry{dev, rows, d, base, ptr, ++g_clock});
   *out = ptr;
   return HA_OK;
 }

@@ -304,12 +304,16 @@ int sortlsh_hyperplanes(uint64_t seed, int heads, int r, int d, float* G_host);
  *                                 V-norm count, alpha (float bits), b_eff
  *   HA_WS_SCHED                   uint32 [2][8] work-queue counters of the
  *                                 attention kernels (scratch, reset by each call)
+ *   HA_WS_PLANES                  staging area of the hyperplanes (see below)
  *   HA_WS_DELTA ... HA_WS_SLOT_DV backward pass only (hyperattn_backward's
  *                                 workspace; bytes 0 in the forward layout):
  *                                 HA_WS_DELTA float [heads][n] = dO_i . O_i
- * The hyperplanes themselves are not in the workspace: the library keeps
- * them per device, keyed by (seed, heads, r, d); sortlsh_hyperplanes returns
- * the same values on the host.
+ * Hyperplanes: the library keeps them on each device for up to 16 keys
+ * (seed, heads, r, d), each copied once when first used. Once 16 are held, a
+ * call with another key generates them on the host and copies them into
+ * HA_WS_PLANES on the call's stream (no allocation, no device-wide wait), so
+ * a fresh seed per call costs one small copy. sortlsh_hyperplanes returns the
+ * same values on the host.
  */
 enum ha_ws_region {
   HA_WS_CODES_Q = 0, HA_WS_CODES_K,
@@ -319,7 +323,7 @@ enum ha_ws_region {
   HA_WS_U_IDX, HA_WS_U_BKT, HA_WS_V_IDX, HA_WS_V_BKT, HA_WS_V_W,
   HA_WS_NODE_META,
   HA_WS_PART_O, HA_WS_PART_LSE,
-  HA_WS_SCHED,
+  HA_WS_SCHED, HA_WS_PLANES,
   HA_WS_DELTA, HA_WS_PART_DQ, HA_WS_PART_DK, HA_WS_PART_DV,
   HA_WS_SLOT_FIRST, HA_WS_SLOT_NEXT, HA_WS_SLOT_DK, HA_WS_SLOT_DV,
   HA_WS_COUNT

@@ -143,7 +143,8 @@ def test_workspace_sizes_and_validation_messages():
     assert ws_bytes(d=96) == 0 and "d=96" in _lib.last_error()
     assert ws_bytes(r=9) == 0 and "r=9" in _lib.last_error()
     assert ws_bytes(r=-1) == 0 and "r=-1" in _lib.last_error()
-    assert ws_bytes(r=0) == ws_bytes(r=8) > 0
+    # r only changes the hyperplane staging area (fp32 [heads][r][d])
+    assert ws_bytes(r=8) - ws_bytes(r=0) == 1 * 8 * 64 * 4 and ws_bytes(r=0) > 0
     assert ws_bytes(b=100) == 0 and "divide" in _lib.last_error()
     assert ws_bytes(n=96, causal=1, b=1, base=2) == 0 and "odd" in _lib.last_error()
     assert ws_bytes(m=0) == 0
@@ -172,6 +173,8 @@ def test_layout_regions_disjoint_and_aligned():
         assert lay["PERM_Q"][1] == levels * 4 * S * 4
         assert lay["VNORM_P"][1] == 4 * 8193 * 8
         assert (lay["PART_O"][1] > 0) == bool(causal)
+        # hyperplane staging: fp32 [4][8][128] (256-aligned), then bf16 [4][16][128]
+        assert lay["PLANES"][1] == 4 * 8 * 128 * 4 + 4 * 16 * 128 * 2
 
 
 def _vp(x):

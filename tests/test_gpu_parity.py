@@ -357,3 +357,62 @@ def test_deterministic_repeat():
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     assert not torch.equal(a, c)
+
+
+def test_more_seeds_than_the_device_keeps():
+    """The library keeps the hyperplanes of 16 keys on each device; calls with
+    further seeds stage theirs through the workspace on the call's stream.
+    Twenty seeds, the last four enqueued back to back without a wait: every
+    call's codes are bit-exact for its own seed, O and lse match the oracle
+    for a staged seed, and a repeat call gives the same bytes."""
+    banner("hyperplane staging: 20 seeds")
+    import torch
+    api = _api()
+    w, Q, K, V, _ = _inputs("planted_noncausal_n8192_d64_h8_bf16", heads=2, n=1024, b=128, m=64,
+                            planted=0)
+    q, k, v = (to_dev(x, "bf16") for x in (Q, K, V))
+    kw = dict(causal=False, b=w.b, m=w.m, r=w.r)
+    layout = api.workspace_layout(w.n, w.d, w.heads, **kw)
+    nb = api.workspace_bytes(w.n, w.d, w.heads, **kw)
+    seeds = list(range(7000, 7020))
+    outs = {}
+    for i, sd in enumerate(seeds):
+        ws = api.alloc_workspace(nb, "cuda")
+        ws.fill_(0xAB)
+        o, lse = api.forward(q, k, v, seed=sd, return_lse=True, workspace=ws, **kw)
+        outs[sd] = (o, lse, ws)
+        if i < 16:
+            _sync()
+    _sync()
+    for sd in seeds:
+        cq = region(outs[sd][2], layout, "CODES_Q", np.uint8).reshape(w.heads, w.n)
+        G = osl.hyperplanes(sd, w.heads, w.r, w.d)
+        for h in range(w.heads):
+            assert np.array_equal(cq[h], osl.hash_codes(Q[h], G[h])), (sd, h)
+    sd = seeds[-1]
+    Oref, Lref = oha.hyperattention(Q, K, V, seed=sd, **kw)
+    assert max_rel(to_np(outs[sd][0]), Oref) <= TOL["bf16"]
+    assert np.abs(to_np(outs[sd][1]) - Lref).max() <= TOL["bf16"]
+    again = api.forward(q, k, v, seed=sd, **kw)
+    _sync()
+    assert torch.equal(again, outs[sd][0])
+
+
+def test_rope_table_serves_shorter_and_grows():
+    """One rotary table per (d, base) on the device, indexed by position: a
+    longer call grows it, a shorter one reads its first rows. The rotated rows
+    stay bit-exact throughout."""
+    banner("rope table growth")
+    from oracle import rope as orope
+    api = _api()
+    for n in (512, 2048, 512, 1024):
+        w, Q, K, V, _ = _inputs("chatglm2_causal_n32768_d128_h32_bf16", heads=1, n=n, b=128,
+                                m=64, recursion_base=256, rope=False)
+        q, k, v = (to_dev(x, "bf16") for x in (Q, K, V))
+        _, qr, kr = api.forward_rope(q, k, v, causal=True, b=w.b, m=w.m,
+                                     recursion_base=w.recursion_base, rope_base=5000.0,
+                                     return_rotated=True)
+        _sync()
+        tab = orope.angle_table(n, w.d, 5000.0)
+        assert np.array_equal(to_np(qr)[0], orope.rope(Q[0], dtype="bf16", table=tab)), n
+        assert np.array_equal(to_np(kr)[0], orope.rope(K[0], dtype="bf16", table=tab)), n
