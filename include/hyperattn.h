@@ -117,8 +117,10 @@ int hyperattn_forward(const void* Q, const void* K, const void* V, void* O,
  * (the attention then reads them). All other arguments, outputs and errors
  * as hyperattn_forward, with the same workspace size; rope_base must be a
  * finite number above 1 (HA_ERR_UNSUPPORTED). The cos/sin table
- * (n * d * 4 bytes) is computed on the host on first use and kept on the
- * device in a small cache keyed by (n, d, rope_base), like the hyperplanes.
+ * (4 d bytes per position) is computed on the host and kept on the device,
+ * one per (d, rope_base), indexed by position: a call with a longer n grows
+ * it to at least twice its length (the outgrown table stays allocated, as
+ * launches already enqueued may read it), a shorter n reads its first rows.
  */
 int hyperattn_forward_rope(const void* Q, const void* K, const void* V,
                            void* Q_rot, void* K_rot, void* O, float* lse,
@@ -153,6 +155,9 @@ size_t hyperattn_workspace_bytes(int64_t n, int d, int heads, int causal,
  * codes: output [heads][n] uint8. perm: optional output [heads][n] int32,
  * perm[h][p] = the row at sorted position p.
  * workspace: >= sortlsh_hash_workspace_bytes(n, heads, perm != NULL).
+ * This entry point has no hyperplane staging area: a seed beyond the 16
+ * keys kept on the device replaces the least recently used one, which
+ * first waits for the whole device.
  */
 int sortlsh_hash(const void* X, int64_t n, int d, int heads, int r,
                  uint64_t seed, int dtype, uint8_t* codes, int32_t* perm,
