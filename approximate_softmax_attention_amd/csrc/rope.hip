@@ -21,6 +21,9 @@
 // Signs the fp32 MFMA projection cannot settle are recomputed in fp64 in
 // order t from the raw row and the table (the rotation is recomputed exactly).
 // fp32 rows, and rotation without hashing: rope_kernel.
+// Backward: rope_adjoint_kernel applies the transpose of each pair's rotation
+// (a turn by -i theta_t, same table and rounding) to dQ and dK in place, so
+// that they become the gradients of the rows before rotation.
 #include <algorithm>
 #include <cmath>
 #include <mutex>
