@@ -8,7 +8,9 @@ constants, tables or helpers with the HIP library under
 
 Everything here is plain, slow and meant to be checked by eye against the
 source pages. All floating-point arithmetic is fp64 (inputs given in fp32 or
-bf16 are upcast exactly); all index arithmetic is exact integer arithmetic.
+bf16 are upcast exactly), except the rotary embedding, whose reading fixes
+fp32 steps (rope.py states it and offers an fp64 adjoint); all index
+arithmetic is exact integer arithmetic.
 
 Sources
 -------
@@ -35,5 +37,6 @@ sortlsh        hyperplanes, Hamming-sorted hash, sortLSH buckets
 sampling       uniform column samples and V-row-norm samples
 hyperattention ApproxD + HyperAttention (non-causal), causal recursion, merge
 backward       gradients of exact attention and of the HyperAttention estimator
-rope           rotary position embedding of Q and K before hashing
+rope           rotary position embedding of Q and K before hashing, and its
+               transpose (the gradient through it)
 """
