@@ -285,3 +285,37 @@ def test_binding_checks_caller_buffers():
     assert api._workspace(ws, 4096, q) is ws
     with pytest.raises(ValueError):
         api._workspace(torch.empty(1024, dtype=torch.float32), 4096, q)
+
+
+def test_oracle_and_product_never_import_each_other():
+    """Static check of the separation: no module of the package imports the
+    oracle, no oracle module imports the package, and bench.py touches the
+    oracle only inside its CPU-baseline functions."""
+    import ast
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+    def imports(tree):
+        for node in ast.walk(tree):
+            if isinstance(node, ast.Import):
+                for a in node.names:
+                    yield node, a.name
+            elif isinstance(node, ast.ImportFrom) and node.module:
+                yield node, node.module
+
+    pkg = os.path.join(root, "approximate_softmax_attention_amd")
+    for f in os.listdir(pkg):
+        if f.endswith(".py"):
+            tree = ast.parse(open(os.path.join(pkg, f)).read())
+            assert not any(m.split(".")[0] == "oracle" for _, m in imports(tree)), f
+    odir = os.path.join(root, "oracle")
+    for f in os.listdir(odir):
+        if f.endswith(".py"):
+            tree = ast.parse(open(os.path.join(odir, f)).read())
+            assert not any(m.split(".")[0] == "approximate_softmax_attention_amd"
+                           for _, m in imports(tree)), f
+    tree = ast.parse(open(os.path.join(root, "bench.py")).read())
+    for fn in tree.body:
+        uses = [m for _, m in imports(fn) if m.split(".")[0] == "oracle"]
+        if uses:
+            assert isinstance(fn, ast.FunctionDef) and fn.name.startswith("cpu_baseline"), \
+                (getattr(fn, "name", None), uses)
