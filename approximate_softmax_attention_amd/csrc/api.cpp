@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -103,6 +104,36 @@ ProfRange::~ProfRange() {
   if (size_t(slot) < g_pending.size()) (void)hipEventRecord(g_pending[slot].stop, stream);
 }
 
+// ------------------------------------------------------------ overlaps
+namespace {
+
+struct Span {
+  const void* p;
+  size_t bytes;
+  const char* name;
+};
+
+bool overlap(const Span& a, const Span& b) {
+  if (!a.p || !b.p || !a.bytes || !b.bytes) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+}  // namespace
+
+// Every written range (outputs and the workspace) must be disjoint from
+// every read range and from the other written ranges; inputs may share
+// memory with each other.
+int check_disjoint(std::initializer_list<Span> written, std::initializer_list<Span> read) {
+  for (const Span* o = written.begin(); o != written.end(); ++o) {
+    for (const Span& i : read)
+      if (overlap(*o, i)) return fail(HA_ERR_SHAPE, "%s overlaps the input %s", o->name, i.name);
+    for (const Span* o2 = o + 1; o2 != written.end(); ++o2)
+      if (overlap(*o, *o2)) return fail(HA_ERR_SHAPE, "%s overlaps %s", o->name, o2->name);
+  }
+  return HA_OK;
+}
+
 }  // namespace ha
 
 using namespace ha;
@@ -156,6 +187,12 @@ int exact_attention_forward(const void* Q, const void* K, const void* V, void* O
     return fail(HA_ERR_SHAPE, "one head of n=%lld rows exceeds 2 GiB", (long long)n);
   if (n == 0 || heads == 0) return HA_OK;
   if (!Q || !K || !V || !O) return fail(HA_ERR_NULL, "Q, K, V and O must not be NULL");
+  {
+    const size_t t = size_t(n) * d * heads * (dtype == HA_BF16 ? 2 : 4);
+    const int rc = check_disjoint({{O, t, "O"}, {lse, size_t(n) * heads * 4, "lse"}},
+                                  {{Q, t, "Q"}, {K, t, "K"}, {V, t, "V"}});
+    if (rc != HA_OK) return rc;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   return launch_exact(Q, K, V, O, lse, n, d, heads, causal ? 1 : 0, dtype, n, nullptr, nullptr, s);
 }
@@ -182,6 +219,18 @@ int forward_impl(const void* Q, const void* K, const void* V, void* O, float* ls
   if (n == 0 || heads == 0) return HA_OK;
   if (!Q || !K || !V || !O) return fail(HA_ERR_NULL, "Q, K, V and O must not be NULL");
   if (rope && (!rope->Qr || !rope->Kr)) return fail(HA_ERR_NULL, "Q_rot and K_rot must not be NULL");
+  // the single-block causal case uses no workspace; otherwise it is checked first
+  const bool single = p.causal && p.L == 0;
+  if (!single && (rc = check_workspace(p, workspace, workspace_bytes)) != HA_OK) return rc;
+  {
+    const size_t t = size_t(n) * d * heads * p.esize;
+    rc = check_disjoint({{O, t, "O"}, {lse, size_t(n) * heads * 4, "lse"},
+                         {rope ? rope->Qr : nullptr, t, "Q_rot"},
+                         {rope ? rope->Kr : nullptr, t, "K_rot"},
+                         {single ? nullptr : workspace, p.total, "workspace"}},
+                        {{Q, t, "Q"}, {K, t, "K"}, {V, t, "V"}});
+    if (rc != HA_OK) return rc;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float* tab = nullptr;
   if (rope && (rc = device_rope_table(n, d, rope->base, &tab)) != HA_OK) return rc;
@@ -195,8 +244,6 @@ int forward_impl(const void* Q, const void* K, const void* V, void* O, float* ls
     }
     return launch_exact(Q, K, V, O, lse, n, d, heads, 1, dtype, n, nullptr, nullptr, s);
   }
-  rc = check_workspace(p, workspace, workspace_bytes);
-  if (rc != HA_OK) return rc;
   const float* G = nullptr;
   const uint16_t* Gb = nullptr;
   if ((rc = device_hyperplanes(seed, heads, r, d, &G, &Gb,
@@ -271,6 +318,12 @@ int rowsum_estimate(const void* Q, const void* K, int64_t n, int d, int heads, i
   if (rc != HA_OK) return rc;
   rc = check_workspace(full, workspace, workspace_bytes);
   if (rc != HA_OK) return rc;
+  {
+    const size_t t = size_t(n) * d * heads * p.esize;
+    rc = check_disjoint({{log_d, size_t(n) * heads * 4, "log_d"}, {workspace, full.total, "workspace"}},
+                        {{Q, t, "Q"}, {K, t, "K"}});
+    if (rc != HA_OK) return rc;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float* G = nullptr;
   const uint16_t* Gb = nullptr;
@@ -339,6 +392,14 @@ int backward_impl(const void* Q, const void* K, const void* V, const void* O, co
     return fail(HA_ERR_NULL, "Q, K, V, O, lse, dO, dQ, dK and dV must not be NULL");
   rc = check_workspace(p, workspace, workspace_bytes);
   if (rc != HA_OK) return rc;
+  {
+    const size_t t = size_t(n) * d * heads * 2;
+    rc = check_disjoint({{dQ, t, "dQ"}, {dK, t, "dK"}, {dV, t, "dV"},
+                         {workspace, p.total, "workspace"}},
+                        {{Q, t, "Q"}, {K, t, "K"}, {V, t, "V"}, {O, t, "O"},
+                         {lse, size_t(n) * heads * 4, "lse"}, {dO, t, "dO"}});
+    if (rc != HA_OK) return rc;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(workspace);
   float* delta = reinterpret_cast<float*>(w + p.off[HA_WS_DELTA]);
@@ -390,6 +451,14 @@ int exact_attention_backward(const void* Q, const void* K, const void* V, const 
     return fail(HA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
   if (workspace_bytes < need)
     return fail(HA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  {
+    const size_t t = size_t(n) * d * heads * 2;
+    const int rc = check_disjoint({{dQ, t, "dQ"}, {dK, t, "dK"}, {dV, t, "dV"},
+                                   {workspace, need, "workspace"}},
+                                  {{Q, t, "Q"}, {K, t, "K"}, {V, t, "V"}, {O, t, "O"},
+                                   {lse, size_t(n) * heads * 4, "lse"}, {dO, t, "dO"}});
+    if (rc != HA_OK) return rc;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* delta = static_cast<float*>(workspace);
   uint32_t* queue = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
@@ -426,10 +495,14 @@ int sortlsh_hash(const void* X, int64_t n, int d, int heads, int r, uint64_t see
     if (workspace_bytes < need)
       return fail(HA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
   }
+  int rc = check_disjoint({{codes, size_t(n) * heads, "codes"},
+                           {perm, size_t(n) * heads * 4, "perm"},
+                           {perm ? workspace : nullptr, need, "workspace"}},
+                          {{X, size_t(n) * d * heads * (dtype == HA_BF16 ? 2 : 4), "X"}});
+  if (rc != HA_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float* G = nullptr;
   const uint16_t* Gb = nullptr;
-  int rc;
   if ((rc = device_hyperplanes(seed, heads, r, d, &G, &Gb)) != HA_OK) return rc;
   if ((rc = launch_hash_one(X, n, d, heads, r, dtype, G, Gb, codes, s)) != HA_OK) return rc;
   if (perm) rc = launch_sort_single(codes, n, heads, perm, workspace, s);

@@ -36,6 +36,9 @@
  *   bit-identical outputs (no floating-point atomics are used).
  * - Workspaces must be 256-byte aligned and at least the size the matching
  *   *_workspace_bytes function returns; their contents on entry do not matter.
+ * - Written ranges (outputs and the workspace) must not overlap any input or
+ *   each other; inputs may share memory (Q, K and V may be one tensor).
+ *   Overlaps are refused with HA_ERR_SHAPE before anything is enqueued.
  * - n == 0 or heads == 0 is valid and enqueues nothing.
  */
 #ifndef HYPERATTN_H

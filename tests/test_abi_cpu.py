@@ -233,9 +233,47 @@ def test_no_device_reports_hip_error():
     except ImportError:
         pass
     lib = L()
-    p = _vp(256)
-    rc = lib.sortlsh_hash(p, 64, 64, 1, 8, 1, 1, p, None, None, 0, None)
+    rc = lib.sortlsh_hash(_vp(256), 64, 64, 1, 8, 1, 1, _vp(1 << 20), None, None, 0, None)
     assert rc == -5 and _lib.last_error()
+
+
+def test_outputs_must_not_overlap_inputs_or_each_other():
+    """Written ranges (outputs, workspace) overlapping a read range or each
+    other are refused with HA_ERR_SHAPE before anything is enqueued; inputs
+    may share memory."""
+    lib = L()
+    t = 1024 * 64 * 2                       # one bf16 [1][1024][64] tensor
+    q, k, v, o, ws = (_vp(i << 24) for i in range(1, 6))
+    need = ws_bytes()
+    # the forward's output over Q, over the workspace; lse inside O
+    rc = lib.hyperattn_forward(q, k, v, q, None, 1024, 64, 1, 0, 128, 128, 4096, 8, 1, 1,
+                               ws, need, None)
+    assert rc == -2 and "O overlaps the input Q" in _lib.last_error()
+    rc = lib.hyperattn_forward(q, k, v, _vp((5 << 24) + 256), None, 1024, 64, 1, 0, 128, 128,
+                               4096, 8, 1, 1, ws, need, None)
+    assert rc == -2 and "workspace" in _lib.last_error()
+    rc = lib.hyperattn_forward(q, k, v, o, _vp((4 << 24) + t - 4), 1024, 64, 1, 0, 128, 128,
+                               4096, 8, 1, 1, ws, need, None)
+    assert rc == -2 and "O overlaps lse" in _lib.last_error()
+    # Q, K and V may be one tensor (no error from the overlap check: the
+    # call then fails at its first device call, here without a GPU)
+    rc = lib.exact_attention_forward(q, q, q, _vp((1 << 24) + t), None, 1024, 64, 1, 0, 1, None)
+    assert rc != -2
+    rc = lib.exact_attention_forward(q, k, v, _vp((3 << 24) + 128), None, 1024, 64, 1, 0, 1,
+                                     None)
+    assert rc == -2 and "O overlaps the input V" in _lib.last_error()
+    # backward: a gradient over dO, and two gradients in one buffer
+    bneed = lib.hyperattn_backward_workspace_bytes(1024, 64, 1, 0, 128, 128, 4096, 8, 1)
+    do, dq, dk, dv, lse = (_vp(i << 24) for i in range(6, 11))
+    rc = lib.hyperattn_backward(q, k, v, o, lse, do, do, dk, dv, 1024, 64, 1, 0, 128, 128,
+                                4096, 8, 1, 1, _vp(12 << 24), bneed, None)
+    assert rc == -2 and "dQ overlaps the input dO" in _lib.last_error()
+    rc = lib.exact_attention_backward(q, k, v, o, lse, do, dq, dq, dv, 1024, 64, 1, 0, 1,
+                                      _vp(12 << 24), 1 << 20, None)
+    assert rc == -2 and "dQ overlaps dK" in _lib.last_error()
+    # hash codes written over the rows they hash
+    rc = lib.sortlsh_hash(q, 1024, 64, 1, 8, 1, 1, _vp((1 << 24) + 100), None, None, 0, None)
+    assert rc == -2 and "codes overlaps the input X" in _lib.last_error()
 
 
 def test_profile_api_without_launches():
