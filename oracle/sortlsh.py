@@ -21,20 +21,17 @@ The definition and the algorithm were lost in extraction. Readings taken:
   the key rows by (code, index), stably; cut both sorted lists into chunks of
   b_eff = min(b, n_k) rows; query chunk k is paired with key chunk k.
 * Hyperplanes are Gaussian via Box-Muller (Box and Muller, 1958) from two
-  counter-based uniforms: u1 = (draw >> 11 + 1) 2^-53 in (0, 1],
-  u2 = (draw >> 11) 2^-53 in [0, 1); g = sqrt(-2 ln u1) cos(2 pi u2), rounded
-  to fp32 and then to the nearest bfloat16 (ties to even), so that the
-  product of a bf16 input with a hyperplane entry is exact in fp32. Element
-  (k, t) of head h uses counters 2(k d + t) and 2(k d + t)+1 of purpose
-  "hyperplane" with node 0. Python's math module (the C library) evaluates
-  log, sqrt and cos.
+  counter-based draws, evaluated as gaussian.py defines it (only IEEE-754
+  binary64 basic operations, so any platform gets the same bits), rounded to
+  fp32 and then to the nearest bfloat16 (ties to even), so that the product
+  of a bf16 input with a hyperplane entry is exact in fp32. Element (k, t)
+  of head h uses counters 2(k d + t) and 2(k d + t)+1 of purpose
+  "hyperplane" with node 0.
 """
-
-import math
 
 import numpy as np
 
-from . import rng
+from . import gaussian
 
 
 def round_bf16(x32):
@@ -45,21 +42,19 @@ def round_bf16(x32):
     return np.array(bits & 0xFFFFFFFF, dtype=np.uint32).view(np.float32)
 
 
+def round_bf16_array(x32):
+    """Nearest bfloat16 of each fp32 value (ties to even), returned as fp32."""
+    bits = np.asarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    bits = ((bits + 0x7FFF + ((bits >> 16) & 1)) >> 16) << 16
+    return (bits & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
+
+
 def hyperplanes(seed, heads, r, d):
     """G[h, k, t]: r Gaussian hyperplanes of dimension d per head (bf16 values
     held in fp32)."""
-    G = np.empty((heads, r, d), dtype=np.float32)
-    for h in range(heads):
-        for k in range(r):
-            for t in range(d):
-                e = k * d + t
-                a = rng.draw(seed, rng.PURPOSE_HYPERPLANE, h, 0, 2 * e)
-                b = rng.draw(seed, rng.PURPOSE_HYPERPLANE, h, 0, 2 * e + 1)
-                u1 = ((a >> 11) + 1) * 2.0 ** -53
-                u2 = (b >> 11) * 2.0 ** -53
-                g = math.sqrt(-2.0 * math.log(u1)) * math.cos(2.0 * math.pi * u2)
-                G[h, k, t] = round_bf16(np.float32(g))
-    return G
+    a, b = gaussian.hyperplane_draws(seed, heads, r, d)
+    g = gaussian.box_muller(a.ravel(), b.ravel()).astype(np.float32)
+    return round_bf16_array(g).reshape(heads, r, d)
 
 
 def projections_sequential(X, Gh):
