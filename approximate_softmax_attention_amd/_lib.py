@@ -25,28 +25,32 @@ SIGNATURES = {
                                  _i32, _i32, _u64, _i32, _vp, _sz, _vp]),
     "hyperattn_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "sortlsh_hash": (_i32, [_vp, _i64, _i32, _i32, _i32, _u64, _i32, _vp, _vp, _vp, _sz, _vp]),
-    "sortlsh_hash_workspace_bytes": (_sz, [_i64, _i32, _i32]),
+    "sortlsh_hash_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32]),
     "exact_attention_forward": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
                                        _vp]),
     "rowsum_estimate": (_i32, [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _u64, _i32, _vp,
                                _vp, _sz, _vp]),
     "sortlsh_hyperplanes": (_i32, [_u64, _i32, _i32, _i32, _fp]),
-    "hyperattn_forward_rope": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
-                                      _i32, _i32, _i32, _i32, _u64, _c.c_double, _i32, _vp, _sz,
+    "sortlsh_gaussians": (_i32, [_c.POINTER(_u64), _c.POINTER(_u64), _i64,
+                                 _c.POINTER(_c.c_double)]),
+    "hyperattn_forward_rope": (_i32, [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _i32,
+                                      _i32, _i32, _i32, _i32, _i32, _i32, _u64, _i32, _vp, _sz,
                                       _vp]),
     "rope_table": (_i32, [_i64, _i32, _c.c_double, _fp]),
     "hyperattn_backward": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
                                   _i32, _i32, _i32, _i32, _i32, _u64, _i32, _vp, _sz, _vp]),
     "hyperattn_backward_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                                  _i32]),
-    "hyperattn_backward_rope": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32,
-                                       _i32, _i32, _i32, _i32, _i32, _i32, _u64, _c.c_double,
+    "hyperattn_backward_rope": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
+                                       _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _u64,
                                        _i32, _vp, _sz, _vp]),
     "exact_attention_backward": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32,
                                         _i32, _i32, _i32, _vp, _sz, _vp]),
     "exact_attention_backward_workspace_bytes": (_sz, [_i64, _i32]),
     "hyperattn_workspace_layout": (_i32, [_i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                           _c.POINTER(_i64), _c.POINTER(_i64)]),
+    "hyperattn_debug_artifacts": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _i32,
+                                         _i32, _u64, _i32, _vp, _sz, _vp, _vp]),
     "hyperattn_last_error": (_c.c_char_p, []),
     "hyperattn_profile_enable": (_i32, [_i32]),
     "hyperattn_profile_collect": (_i32, []),
@@ -54,8 +58,21 @@ SIGNATURES = {
     "hyperattn_profile_count": (_i32, []),
     "hyperattn_profile_name": (_c.c_char_p, [_i32]),
     "hyperattn_profile_launches": (_i64, [_i32]),
+    "hyperattn_profile_groups": (_i64, [_i32]),
     "hyperattn_profile_total_ms": (_c.c_double, [_i32]),
 }
+
+# struct ha_artifacts of include/hyperattn.h: host pointers, one per region
+ARTIFACT_FIELDS = [("codes_q", "CODES_Q"), ("codes_k", "CODES_K"), ("vnorm_w", "VNORM_W"),
+                   ("vnorm_p", "VNORM_P"), ("perm_q", "PERM_Q"), ("perm_k", "PERM_K"),
+                   ("rank_k", "RANK_K"), ("u_idx", "U_IDX"), ("u_bkt", "U_BKT"),
+                   ("v_idx", "V_IDX"), ("v_bkt", "V_BKT"), ("v_w", "V_W"),
+                   ("node_meta", "NODE_META")]
+
+
+class HaArtifacts(_c.Structure):
+    _fields_ = [(name, _vp) for name, _ in ARTIFACT_FIELDS]
+
 
 _LIB = None
 

@@ -10,8 +10,9 @@ contiguous, on a ROCm device, dtype torch.bfloat16 or torch.float32 (the
 backward pass takes bfloat16).
 
 Entry points: forward, forward_rope, backward, backward_rope, exact, exact_backward,
-rowsum_estimate, sortlsh_hash, hyperplanes, rope_table, workspace_bytes,
-backward_workspace_bytes, workspace_layout; HyperAttentionFunction and
+rowsum_estimate, sortlsh_hash, hyperplanes, gaussians, rope_table,
+rope_device_table, debug_artifacts, workspace_bytes, backward_workspace_bytes,
+workspace_layout; HyperAttentionFunction and
 HyperAttentionRopeFunction wrap forward and backward for torch.autograd; KernelTimer collects the library's
 per-kernel hipEvent timings.
 """
@@ -81,11 +82,12 @@ def _workspace(ws, nbytes, like):
     return ws
 
 
-def _call(like, fn, *args):
+def _call(like, fn, *args, after=()):
     """Calls a library entry point with `like`'s device current (the library
-    launches on the current device and keeps per-device tables)."""
+    launches on the current device) on torch's current stream there; `after`
+    are arguments that follow the stream."""
     with torch.cuda.device(like.device):
-        check(fn(*args, _stream(like.device)))
+        check(fn(*args, _stream(like.device), *after))
 
 
 def _stream(dev):
@@ -133,24 +135,55 @@ def forward(q, k, v, *, causal, b=256, m=256, r=8, recursion_base=4096, seed=0,
     return o
 
 
+# Device copies of rope_table, one per (device, d, rope_base), indexed by
+# position: a longer call replaces the table by one at least twice as long, a
+# shorter call reads its first rows. torch owns the memory.
+_ROPE_TABLES = {}
+
+
+def rope_device_table(n, d, rope_base, device):
+    """The cos/sin table of at least n positions on `device` (fp32 tensor
+    [rows, d/2, 2]) for forward_rope and backward_rope."""
+    key = (torch.device(device), int(d), float(rope_base))
+    t = _ROPE_TABLES.get(key)
+    if t is None or t.shape[0] < n:
+        rows = max(int(n), 2 * t.shape[0] if t is not None else 0, 1)
+        rows = min(rows, max(int(n), (1 << 31) - 1))
+        t = torch.from_numpy(rope_table(rows, d, rope_base)).to(key[0])
+        _ROPE_TABLES[key] = t
+    return t
+
+
+def _check_table(cos_sin, n, d, like):
+    if cos_sin.device != like.device or cos_sin.dtype != torch.float32 or \
+            not cos_sin.is_contiguous() or cos_sin.dim() != 3 or \
+            tuple(cos_sin.shape[1:]) != (d // 2, 2) or cos_sin.shape[0] < n:
+        raise ValueError(f"cos_sin must be a contiguous fp32 [>= {n}, {d // 2}, 2] tensor on "
+                         f"{like.device}")
+    return cos_sin
+
+
 def forward_rope(q, k, v, *, causal, rope_base=10000.0, b=256, m=256, r=8,
                  recursion_base=4096, seed=0, return_lse=False, return_rotated=False,
-                 workspace=None):
+                 workspace=None, cos_sin=None):
     """HyperAttention forward on Q and K before their rotary embedding, which
     the library applies on the device in the pass that hashes them; returns O
-    (then lse, then the rotated Q and K, as asked)."""
+    (then lse, then the rotated Q and K, as asked). cos_sin: the device table
+    (rope_device_table(n, d, rope_base, device) unless given)."""
     shape, q, k, v = _qkv(q, k, v)
     H, n, d = q.shape
     dt = _dtype_code(q)
+    tab = _check_table(cos_sin if cos_sin is not None else
+                       rope_device_table(n, d, rope_base, q.device), n, d, q)
     o = torch.empty_like(q)
     qr, kr = torch.empty_like(q), torch.empty_like(k)
     lse = torch.empty((H, n), dtype=torch.float32, device=q.device) if return_lse else None
     nb = workspace_bytes(n, d, H, causal=causal, b=b, m=m, r=r,
                          recursion_base=recursion_base, dtype=dt)
     ws = _workspace(workspace, nb, q)
-    _call(q, lib().hyperattn_forward_rope, _ptr(q), _ptr(k), _ptr(v), _ptr(qr), _ptr(kr), _ptr(o),
-          _ptr(lse), n, d, H, int(causal), b, m, recursion_base, r, seed, float(rope_base), dt,
-          _ptr(ws), ws.numel())
+    _call(q, lib().hyperattn_forward_rope, _ptr(q), _ptr(k), _ptr(v), _ptr(tab), tab.shape[0],
+          _ptr(qr), _ptr(kr), _ptr(o), _ptr(lse), n, d, H, int(causal), b, m, recursion_base, r,
+          seed, dt, _ptr(ws), ws.numel())
     out = [o.reshape(shape)]
     if return_lse:
         out.append(lse.reshape(shape[:-1]))
@@ -225,20 +258,22 @@ def backward(q, k, v, o, lse, do, *, causal, b=256, m=256, r=8, recursion_base=4
 
 
 def backward_rope(q_rot, k_rot, v, o, lse, do, *, causal, rope_base=10000.0, b=256, m=256,
-                  r=8, recursion_base=4096, seed=0, workspace=None):
+                  r=8, recursion_base=4096, seed=0, workspace=None, cos_sin=None):
     """Gradients (dq, dk, dv) for a forward_rope call: dq and dk are those of
     the rows before their rotary embedding. q_rot and k_rot are the rotated
     rows forward_rope returned (return_rotated=True)."""
     shape, q, k, v, o, lse, do = _grad_inputs(q_rot, k_rot, v, o, lse, do)
     H, n, d = q.shape
     dt = _dtype_code(q)
+    tab = _check_table(cos_sin if cos_sin is not None else
+                       rope_device_table(n, d, rope_base, q.device), n, d, q)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     nb = backward_workspace_bytes(n, d, H, causal=causal, b=b, m=m, r=r,
                                   recursion_base=recursion_base, dtype=dt)
     ws = _workspace(workspace, nb, q)
     _call(q, lib().hyperattn_backward_rope, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-          _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), n, d, H, int(causal), b, m, recursion_base, r,
-          seed, float(rope_base), dt, _ptr(ws), ws.numel())
+          _ptr(do), _ptr(tab), tab.shape[0], _ptr(dq), _ptr(dk), _ptr(dv), n, d, H, int(causal),
+          b, m, recursion_base, r, seed, dt, _ptr(ws), ws.numel())
     return dq.reshape(shape), dk.reshape(shape), dv.reshape(shape)
 
 
@@ -317,10 +352,12 @@ def sortlsh_hash(x, *, r=8, seed=0, with_perm=False):
     H, n, d = x.shape
     codes = torch.empty((H, n), dtype=torch.uint8, device=x.device)
     perm = torch.empty((H, n), dtype=torch.int32, device=x.device) if with_perm else None
-    nb = lib().sortlsh_hash_workspace_bytes(n, H, int(with_perm))
-    ws = alloc_workspace(nb, x.device) if with_perm else None
+    nb = lib().sortlsh_hash_workspace_bytes(n, d, H, r, int(with_perm))
+    if nb == 0 and _lib.last_error():
+        raise _lib.HyperAttnError(-2, _lib.last_error())
+    ws = alloc_workspace(nb, x.device)
     _call(x, lib().sortlsh_hash, _ptr(x), n, d, H, r, seed, _dtype_code(x), _ptr(codes),
-          _ptr(perm), _ptr(ws), nb)
+          _ptr(perm), _ptr(ws), ws.numel())
     codes = codes.reshape(shape[:-1])
     return (codes, perm.reshape(shape[:-1])) if with_perm else codes
 
@@ -333,6 +370,46 @@ def hyperplanes(seed, heads, r, d):
     return G
 
 
+def gaussians(a, b):
+    """The library's binary64 Box-Muller normals of the uint64 draws a and b."""
+    a = np.ascontiguousarray(a, dtype=np.uint64)
+    b = np.ascontiguousarray(b, dtype=np.uint64)
+    if a.shape != b.shape:
+        raise ValueError("a and b must have the same shape")
+    out = np.empty(a.shape, dtype=np.float64)
+    u64p = ctypes.POINTER(ctypes.c_uint64)
+    check(lib().sortlsh_gaussians(a.ctypes.data_as(u64p), b.ctypes.data_as(u64p), a.size,
+                                  out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))))
+    return out
+
+
+_ARTIFACT_DTYPES = {"CODES_Q": np.uint8, "CODES_K": np.uint8, "VNORM_W": np.uint64,
+                    "VNORM_P": np.uint64, "V_W": np.float32}
+
+
+def debug_artifacts(q, k, v, *, causal, b=256, m=256, r=8, recursion_base=4096, seed=0,
+                    workspace=None):
+    """hyperattn_debug_artifacts: {region: host numpy array} of the forward
+    pass's codes, V-norm weights and prefix sums, sorted orders and sample
+    lists (flat, in the layout of workspace_layout)."""
+    _, q, k, v = _qkv(q, k, v)
+    H, n, d = q.shape
+    dt = _dtype_code(q)
+    kw = dict(causal=causal, b=b, m=m, r=r, recursion_base=recursion_base, dtype=dt)
+    layout = workspace_layout(n, d, H, **kw)
+    ws = _workspace(workspace, workspace_bytes(n, d, H, **kw), q)
+    arrays, st = {}, _lib.HaArtifacts()
+    for field, region in _lib.ARTIFACT_FIELDS:
+        nbytes = layout[region][1]
+        a = np.zeros(nbytes // np.dtype(_ARTIFACT_DTYPES.get(region, np.int32)).itemsize,
+                     dtype=_ARTIFACT_DTYPES.get(region, np.int32))
+        arrays[region] = a
+        setattr(st, field, a.ctypes.data if a.size else None)
+    _call(q, lib().hyperattn_debug_artifacts, _ptr(q), _ptr(k), _ptr(v), n, d, H, int(causal), b,
+          m, recursion_base, r, seed, dt, _ptr(ws), ws.numel(), after=(ctypes.byref(st),))
+    return arrays
+
+
 def workspace_layout(n, d, heads, *, causal, b, m, r=8, recursion_base=4096, dtype=HA_BF16):
     """{region: (offset, bytes)} of hyperattn_forward's workspace."""
     off = (ctypes.c_int64 * len(_lib.WS_REGIONS))()
@@ -343,7 +420,8 @@ def workspace_layout(n, d, heads, *, causal, b, m, r=8, recursion_base=4096, dty
 
 
 class KernelTimer:
-    """Per-kernel durations from hipEvents the library records around launches."""
+    """Per-kernel durations from hipEvents the library records around launches
+    (stats: name -> (launches, total ms); groups: name -> work-groups launched)."""
 
     def __enter__(self):
         L = lib()
@@ -356,10 +434,11 @@ class KernelTimer:
         L = lib()
         check(L.hyperattn_profile_enable(0))
         check(L.hyperattn_profile_collect())
-        self.stats = {}
+        self.stats, self.groups = {}, {}
         for i in range(L.hyperattn_profile_count()):
             name = L.hyperattn_profile_name(i).decode()
             launches = L.hyperattn_profile_launches(i)
             if launches:
                 self.stats[name] = (launches, L.hyperattn_profile_total_ms(i))
+                self.groups[name] = L.hyperattn_profile_groups(i)
         return False

@@ -743,19 +743,21 @@ int launch_grid(Kern k, const AttnArgs& a, unsigned per_row, dim3& grid) {
 }
 
 template <typename T, int D>
-int launch_exact_t(const AttnArgs& a, hipStream_t s) {
+int launch_exact_t(const AttnArgs& a, hipStream_t s, ProfRange& pr) {
   auto k = a.causal ? exact_kernel<T, D, true> : exact_kernel<T, D, false>;
   dim3 grid;
   if (int rc = launch_grid(k, a, a.items_per_head, grid)) return rc;
+  pr.groups = int64_t(grid.x) * grid.y;
   hipLaunchKernelGGL(k, grid, dim3(kThreads), 0, s, a);
   return HA_OK;
 }
 
 template <typename T, int D>
-int launch_bucket_t(const AttnArgs& a, bool product, hipStream_t s) {
+int launch_bucket_t(const AttnArgs& a, bool product, hipStream_t s, ProfRange& pr) {
   auto k = product ? bucket_kernel<T, D, MODE_BUCKET> : bucket_kernel<T, D, MODE_ROWSUM>;
   dim3 grid;
   if (int rc = launch_grid(k, a, a.items, grid)) return rc;
+  pr.groups = int64_t(grid.x) * grid.y;
   hipLaunchKernelGGL(k, grid, dim3(kThreads), 0, s, a);
   return HA_OK;
 }
@@ -796,9 +798,9 @@ int launch_exact(const void* Q, const void* K, const void* V, void* O, float* ls
   ProfRange pr(merge ? "exact_base_merge" : "exact_attention", s);
   int rc;
   if (dtype == HA_BF16)
-    rc = d == 128 ? launch_exact_t<bf16_t, 128>(a, s) : launch_exact_t<bf16_t, 64>(a, s);
+    rc = d == 128 ? launch_exact_t<bf16_t, 128>(a, s, pr) : launch_exact_t<bf16_t, 64>(a, s, pr);
   else
-    rc = d == 128 ? launch_exact_t<float, 128>(a, s) : launch_exact_t<float, 64>(a, s);
+    rc = d == 128 ? launch_exact_t<float, 128>(a, s, pr) : launch_exact_t<float, 64>(a, s, pr);
   if (rc) return rc;
   HA_LAUNCH_CHECK("exact_attention");
   return HA_OK;
@@ -843,11 +845,11 @@ int launch_bucket_attention(const Plan& p, const void* Q, const void* K, const v
   ProfRange pr(p.product ? "bucket_attention" : "bucket_rowsum", s);
   int rc;
   if (p.dtype == HA_BF16)
-    rc = p.d == 128 ? launch_bucket_t<bf16_t, 128>(a, p.product, s)
-                    : launch_bucket_t<bf16_t, 64>(a, p.product, s);
+    rc = p.d == 128 ? launch_bucket_t<bf16_t, 128>(a, p.product, s, pr)
+                    : launch_bucket_t<bf16_t, 64>(a, p.product, s, pr);
   else
-    rc = p.d == 128 ? launch_bucket_t<float, 128>(a, p.product, s)
-                    : launch_bucket_t<float, 64>(a, p.product, s);
+    rc = p.d == 128 ? launch_bucket_t<float, 128>(a, p.product, s, pr)
+                    : launch_bucket_t<float, 64>(a, p.product, s, pr);
   if (rc) return rc;
   HA_LAUNCH_CHECK("bucket_attention");
   return HA_OK;

@@ -1592,6 +1592,7 @@ int launch_items(Kern k, BwdArgs a, int64_t items, bool persistent, const char* 
     a.queue = nullptr;
   }
   ProfRange pr(name, s);
+  pr.groups = grid;
   hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), 0, s, a);
   HA_LAUNCH_CHECK(name);
   return HA_OK;

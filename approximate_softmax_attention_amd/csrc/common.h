@@ -37,12 +37,19 @@ int fail(int code, const char* fmt, ...);
 
 // ------------------------------------------------------------- profiling
 // Brackets one launch with events on its stream when profiling is enabled.
+// `groups` (set by the launcher) is the launch's work-group count.
 struct ProfRange {
   ProfRange(const char* name, hipStream_t s);
   ~ProfRange();
   int slot;
   hipStream_t stream;
+  int64_t groups = 0;
 };
+
+// Work-groups of `threads` threads of the kernel `kernel` that the current
+// device holds at once (occupancy query, cached per device and kernel); 0 if
+// the query fails.
+int resident_groups_of(const void* kernel, int threads);
 
 // ------------------------------------------------------- level geometry
 // One level of the flattened causal recursion (or the single non-causal
@@ -112,18 +119,17 @@ int make_plan(Plan& p, int64_t n, int d, int heads, int causal, int b, int m,
               int base, int r, int dtype, bool product, bool backward = false);
 int check_workspace(const Plan& p, const void* ws, size_t ws_bytes);
 
-// Hyperplanes on the device for (seed, heads, r, d).
-// *out: fp32 values [heads][r][d]; *out_bf16 (optional): the same values as
-// bf16 bit patterns in [heads][16][d], hyperplanes r..15 zero.
-// Up to 16 keys are kept per device (copied once). For other keys, with a
-// stage (hyperplane_stage_bytes device bytes, e.g. a workspace region) the
-// values are copied there on stream s; without one the least recently used
-// entry is replaced, which waits for the device first.
-int device_hyperplanes(uint64_t seed, int heads, int r, int d, const float** out,
-                       const uint16_t** out_bf16 = nullptr, void* stage = nullptr,
-                       hipStream_t s = nullptr);
+// Hyperplanes of (seed, heads, r, d), drawn on the device into `stage`
+// (hyperplane_stage_bytes bytes, the workspace region HA_WS_PLANES) on
+// stream s. *out: fp32 values [heads][r][d]; *out_bf16 (optional): the same
+// values as bf16 bit patterns in [heads][16][d], hyperplanes r..15 zero.
+int launch_hyperplanes(uint64_t seed, int heads, int r, int d, void* stage, hipStream_t s,
+                       const float** out, const uint16_t** out_bf16 = nullptr);
 int64_t hyperplane_stage_bytes(int heads, int r, int d);
+// The same values computed on the host ([heads][r][d] floats).
 void host_hyperplanes(uint64_t seed, int heads, int r, int d, float* G);
+// Box-Muller normals (binary64, before rounding) from pairs of draws.
+void host_gaussians(const uint64_t* a, const uint64_t* b, int64_t count, double* out);
 
 // --------------------------------------------------------------- launchers
 // All return HA_OK or HA_ERR_HIP; arguments are validated by the caller.
@@ -131,7 +137,8 @@ void host_hyperplanes(uint64_t seed, int heads, int r, int d, float* G);
 int launch_hash(const Plan& p, const void* Q, const void* K, const void* V,
                 const float* G, const uint16_t* Gb, void* ws, hipStream_t s);
 // Rotary embedding of Q and K into Qr and Kr (rope.hip); with hash, also the
-// sortLSH codes of the rotated rows. tab: device_rope_table's.
+// sortLSH codes of the rotated rows. tab: the caller's cos/sin table
+// [>= n][d/2][2] in device memory.
 int launch_rope(const Plan& p, const void* Q, const void* K, void* Qr, void* Kr,
                 const float* tab, bool hash, const float* G, const uint16_t* Gb, void* ws,
                 hipStream_t s);
@@ -140,12 +147,8 @@ int launch_rope(const Plan& p, const void* Q, const void* K, void* Qr, void* Kr,
 int launch_rope_adjoint(void* dQ, void* dK, int64_t n, int d, int heads, int dtype,
                         const float* tab, hipStream_t s);
 // cos and sin of i * base^(-2t/d) for rows i < n and pairs t < d/2, as
-// [n][d/2][2], fp64 from the C library rounded to fp32 (host), and its
-// per-device cache.
+// [n][d/2][2], fp64 from the C library rounded to fp32 (host).
 void host_rope_table(int64_t n, int d, double base, float* out);
-// Device cos/sin table of at least n positions for (d, base); rows are
-// positions, so a longer table serves every shorter n. Grows by doubling.
-int device_rope_table(int64_t n, int d, double base, const float** out);
 int launch_hash_one(const void* X, int64_t n, int d, int heads, int r, int dtype,
                     const float* G, const uint16_t* Gb, uint8_t* codes, hipStream_t s);
 int launch_vnorm_scan(const Plan& p, void* ws, hipStream_t s);

@@ -81,15 +81,15 @@ __device__ __forceinline__ uint64_t wave_incl_scan(uint64_t x) {
 // SplitMix64 output for the state x (Steele, Lea and Flood, OOPSLA 2014) and
 // the counter-based draw: mix64(mix64(seed) ^ (purpose<<60 | head<<44 |
 // node<<24 | counter)).
-__device__ __forceinline__ uint64_t mix64(uint64_t x) {
+__host__ __device__ inline uint64_t mix64(uint64_t x) {
   uint64_t z = x + 0x9E3779B97F4A7C15ull;
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
   z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
   return z ^ (z >> 31);
 }
 
-__device__ __forceinline__ uint64_t draw(uint64_t key, uint64_t purpose, uint64_t head,
-                                         uint64_t node, uint64_t counter) {
+__host__ __device__ inline uint64_t draw(uint64_t key, uint64_t purpose, uint64_t head,
+                                          uint64_t node, uint64_t counter) {
   return mix64(key ^ ((purpose << 60) | (head << 44) | (node << 24) | counter));
 }
 

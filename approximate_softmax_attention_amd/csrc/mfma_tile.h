@@ -344,20 +344,11 @@ __device__ __forceinline__ int64_t queue_resolve(uint32_t* ctr, uint32_t items, 
 }
 
 
-// Work-groups of kernel k that the device holds at once (cached per device).
+// Work-groups of kernel k (kThreads threads each) that the device holds at
+// once, cached per device and kernel.
 template <typename Kern>
 int resident_groups(Kern k) {
-  static int cache[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  const int r = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
-  if (dev >= 0 && dev < 64) cache[dev] = r;
-  return r;
+  return resident_groups_of(reinterpret_cast<const void*>(k), kThreads);
 }
 
 

@@ -9,8 +9,9 @@
 //   x'_{t+d/2} = x_t sin(i theta_t) + x_{t+d/2} cos(i theta_t)
 // in fp32 with every product and sum rounded once (no fused multiply-add),
 // then, for bf16 rows, rounded to the nearest bf16. cos and sin come from a
-// table the host fills with the C library's pow, cos and sin (fp64, rounded
-// once to fp32), so the rotated rows are fixed numbers, not just close ones.
+// table the caller passes in device memory, filled by rope_table on the host
+// with the C library's pow, cos and sin (fp64, rounded once to fp32), so the
+// rotated rows are fixed numbers, not just close ones.
 //
 // bf16 rows: rope_hash_kernel. Lane l of a wave owns row l%16 of the wave's
 // 16 rows and the 16-byte chunks at elements 32s + 8(l/16), s < d/32 (the
@@ -24,9 +25,7 @@
 // Backward: rope_adjoint_kernel applies the transpose of each pair's rotation
 // (a turn by -i theta_t, same table and rounding) to dQ and dK in place, so
 // that they become the gradients of the rows before rotation.
-#include <algorithm>
 #include <cmath>
-#include <mutex>
 #include <vector>
 
 #include "common.h"
@@ -298,21 +297,6 @@ __global__ __launch_bounds__(kThreads) void rope_hash_kernel(
     }
 }
 
-// --------------------------------------------------------- host table
-struct TableEntry {
-  int device;
-  int64_t n;
-  int d;
-  double base;
-  float* ptr;          // [n][d/2][2]: cos, sin
-  uint64_t stamp;
-};
-std::mutex g_mu;
-std::vector<TableEntry> g_cache;
-std::vector<float*> g_retired;   // tables outgrown while launches may still read them
-uint64_t g_clock = 0;
-constexpr size_t kCacheEntries = 4;   // (d, base) pairs per device
-
 }  // namespace
 
 void host_rope_table(int64_t n, int d, double base, float* out) {
@@ -330,64 +314,6 @@ void host_rope_table(int64_t n, int d, double base, float* out) {
       out[(i * half + t) * 2] = float(cs(a));
       out[(i * half + t) * 2 + 1] = float(sn(a));
     }
-}
-
-int device_rope_table(int64_t n, int d, double base, const float** out) {
-  int dev = 0;
-  HA_HIP_TRY(hipGetDevice(&dev));
-  std::lock_guard<std::mutex> lock(g_mu);
-  TableEntry* hit = nullptr;
-  size_t held = 0;
-  for (TableEntry& e : g_cache) {
-    if (e.device != dev) continue;
-    ++held;
-    if (e.d == d && e.base == base) hit = &e;
-  }
-  if (hit && hit->n >= n) {      // rows are positions: a longer table serves
-    hit->stamp = ++g_clock;
-    *out = hit->ptr;
-    return HA_OK;
-  }
-  // a new or longer table: at least twice the old length, so that a run of
-  // growing n reallocates only a logarithmic number of times
-  int64_t rows = n;
-  if (hit) rows = std::max(n, std::min(2 * hit->n, (int64_t(1) << 31) - 1));
-  const size_t count = size_t(rows) * size_t(d);  // rows x d/2 pairs x (cos, sin)
-  std::vector<float> host(count);
-  host_rope_table(rows, d, base, host.data());
-  float* ptr = nullptr;
-  HA_HIP_TRY(hipMalloc(&ptr, count * sizeof(float)));
-  const hipError_t e = hipMemcpy(ptr, host.data(), count * sizeof(float), hipMemcpyHostToDevice);
-  if (e != hipSuccess) {
-    (void)hipFree(ptr);
-    return fail(HA_ERR_HIP, "copy of the rotary table to the device failed: %s",
-                hipGetErrorString(e));
-  }
-  if (hit) {
-    // launches already enqueued may still read the shorter table: it is
-    // kept (never freed) rather than waited for; with doubling, the tables
-    // kept add up to less than the current one
-    g_retired.push_back(hit->ptr);
-    hit->ptr = ptr;
-    hit->n = rows;
-    hit->stamp = ++g_clock;
-    *out = ptr;
-    return HA_OK;
-  }
-  if (held >= kCacheEntries) {
-    // another (d, base) pair past the cache's size: replace this device's
-    // least recently used table after draining the device
-    size_t old = g_cache.size();
-    for (size_t i = 0; i < g_cache.size(); ++i)
-      if (g_cache[i].device == dev && (old == g_cache.size() || g_cache[i].stamp < g_cache[old].stamp))
-        old = i;
-    HA_HIP_TRY(hipDeviceSynchronize());
-    HA_HIP_TRY(hipFree(g_cache[old].ptr));
-    g_cache.erase(g_cache.begin() + old);
-  }
-  g_cache.push_back(TableEntry{dev, rows, d, base, ptr, ++g_clock});
-  *out = ptr;
-  return HA_OK;
 }
 
 // Rotates Q and K into Qr and Kr; with hash, also writes the sortLSH codes

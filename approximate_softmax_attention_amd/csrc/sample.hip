@@ -107,12 +107,6 @@ __global__ __launch_bounds__(kThreads) void samples_kernel(SampleArgs a) {
   }
 }
 
-uint64_t host_mix64(uint64_t x) {
-  uint64_t z = x + 0x9E3779B97F4A7C15ull;
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  return z ^ (z >> 31);
-}
 
 }  // namespace
 
@@ -125,7 +119,7 @@ int launch_samples(const Plan& p, uint64_t seed, void* ws, hipStream_t s) {
   a.n = p.n;
   a.S = p.S;
   a.nodes = p.nodes;
-  a.key = host_mix64(seed);
+  a.key = mix64(seed);
   a.rank_k = reinterpret_cast<const int32_t*>(w + p.off[HA_WS_RANK_K]);
   a.P = p.product ? reinterpret_cast<const uint64_t*>(w + p.off[HA_WS_VNORM_P]) : nullptr;
   a.u_idx = reinterpret_cast<int32_t*>(w + p.off[HA_WS_U_IDX]);

@@ -110,34 +110,36 @@ int hyperattn_forward(const void* Q, const void* K, const void* V, void* O,
  * them (the long-context layers rotate Q and K before attention, and the
  * hash must see the rotated rows: HA page, "Algorithm", Definition 1 applied
  * to the rows the attention uses).
- * Rotation: pairs (t, t + d/2) for t < d/2, theta_t = rope_base^(-2t/d), row
- * i at position i:
- *   x'_t = x_t cos(i theta_t) - x_{t+d/2} sin(i theta_t),
- *   x'_{t+d/2} = x_t sin(i theta_t) + x_{t+d/2} cos(i theta_t),
- * in fp32 with each product and sum rounded once, cos and sin as rope_table
- * returns them, then (bf16 rows) rounded to the nearest bf16, ties to even.
+ * Rotation: pairs (t, t + d/2) for t < d/2, row i at position i, with
+ * c = cos_sin[(i * d/2 + t) * 2] and s = cos_sin[(i * d/2 + t) * 2 + 1]:
+ *   x'_t = x_t c - x_{t+d/2} s,   x'_{t+d/2} = x_t s + x_{t+d/2} c,
+ * in fp32 with each product and sum rounded once, then (bf16 rows) rounded
+ * to the nearest bf16, ties to even.
+ * cos_sin: DEVICE table owned by the caller, at least cos_sin_rows >= n rows
+ * of d floats ([rows][d/2][2]); rope_table fills it on the host (theta_t =
+ * rope_base^(-2t/d), angle i theta_t). Rows are positions, so one table of
+ * the longest n serves every shorter call. The library only reads it.
  * Q_rot, K_rot: outputs [heads][n][d] in the input dtype, the rotated rows
  * (the attention then reads them). All other arguments, outputs and errors
- * as hyperattn_forward, with the same workspace size; rope_base must be a
- * finite number above 1 (HA_ERR_UNSUPPORTED). The cos/sin table
- * (4 d bytes per position) is computed on the host and kept on the device,
- * one per (d, rope_base), indexed by position: a call with a longer n grows
- * it to at least twice its length (the outgrown table stays allocated, as
- * launches already enqueued may read it), a shorter n reads its first rows.
+ * as hyperattn_forward, with the same workspace size; HA_ERR_NULL if
+ * cos_sin is NULL, HA_ERR_SHAPE if cos_sin_rows < n.
  */
 int hyperattn_forward_rope(const void* Q, const void* K, const void* V,
+                           const float* cos_sin, int64_t cos_sin_rows,
                            void* Q_rot, void* K_rot, void* O, float* lse,
                            int64_t n, int d, int heads, int causal, int b,
                            int m, int recursion_base, int r, uint64_t seed,
-                           double rope_base, int dtype, void* workspace,
-                           size_t workspace_bytes, void* stream);
+                           int dtype, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
- * rope_table — host-only: the cos/sin table hyperattn_forward_rope uses.
+ * rope_table — host-only: the cos/sin table hyperattn_forward_rope and
+ * hyperattn_backward_rope read (the caller copies it to the device).
  * table_host[(i * d/2 + t) * 2 + 0] = cos(i * theta_t) and [... + 1] =
  * sin(i * theta_t), with theta_t = pow(rope_base, -2t/d), the angle, cos and
  * sin in fp64 from the C library, each entry rounded once to fp32.
- * table_host holds n * d floats.
+ * table_host holds n * d floats. rope_base must be a finite number above 1
+ * (HA_ERR_UNSUPPORTED).
  */
 int rope_table(int64_t n, int d, double rope_base, float* table_host);
 
@@ -153,19 +155,18 @@ size_t hyperattn_workspace_bytes(int64_t n, int d, int heads, int causal,
  * stable sort of each head's rows by (code, index).
  * codes[h][i] = GrayRank(sum_k [<x_i, g_hk> > 0] 2^k), where the sign is that
  * of the fp64 sum of x_it * g_hkt taken in order t = 0..d-1 and g_hk are the
- * hyperplanes sortlsh_hyperplanes(seed, heads, r, d) returns.
+ * hyperplanes sortlsh_hyperplanes(seed, heads, r, d) returns (drawn on the
+ * device into the workspace by this call).
  * r in [0, 8]; with r = 0 every code is 0 and perm is the identity.
  * codes: output [heads][n] uint8. perm: optional output [heads][n] int32,
  * perm[h][p] = the row at sorted position p.
- * workspace: >= sortlsh_hash_workspace_bytes(n, heads, perm != NULL).
- * This entry point has no hyperplane staging area: a seed beyond the 16
- * keys kept on the device replaces the least recently used one, which
- * first waits for the whole device.
+ * workspace: >= sortlsh_hash_workspace_bytes(n, d, heads, r, perm != NULL).
  */
 int sortlsh_hash(const void* X, int64_t n, int d, int heads, int r,
                  uint64_t seed, int dtype, uint8_t* codes, int32_t* perm,
                  void* workspace, size_t workspace_bytes, void* stream);
-size_t sortlsh_hash_workspace_bytes(int64_t n, int heads, int with_perm);
+size_t sortlsh_hash_workspace_bytes(int64_t n, int d, int heads, int r,
+                                    int with_perm);
 
 /*
  * exact_attention_forward — Att = D^-1 A V with A = exp(QK^T / sqrt(d)) and
@@ -241,20 +242,22 @@ size_t hyperattn_backward_workspace_bytes(int64_t n, int d, int heads,
  * them, then applies the adjoint of the rotation to the two gradients in
  * place. The rotation of each pair is orthogonal, so its adjoint rotates by
  * -i theta_t:
- *   g_t = g'_t cos + g'_{t+d/2} sin,   g_{t+d/2} = -g'_t sin + g'_{t+d/2} cos,
- * in fp32 with each product and sum rounded once, with rope_table's cos and
- * sin, then rounded to bf16. The rounding of the rotated rows to bf16 is
- * piecewise constant and, as with the sketch, carries no gradient.
+ *   g_t = g'_t c + g'_{t+d/2} s,   g_{t+d/2} = -g'_t s + g'_{t+d/2} c,
+ * in fp32 with each product and sum rounded once, with c and s from the
+ * caller's cos_sin table (as hyperattn_forward_rope), then rounded to bf16.
+ * The rounding of the rotated rows to bf16 is piecewise constant and, as
+ * with the sketch, carries no gradient.
  * Other arguments, outputs, workspace and errors as hyperattn_backward;
- * rope_base as hyperattn_forward_rope.
+ * cos_sin and cos_sin_rows as hyperattn_forward_rope.
  */
 int hyperattn_backward_rope(const void* Q_rot, const void* K_rot,
                             const void* V, const void* O, const float* lse,
-                            const void* dO, void* dQ, void* dK, void* dV,
+                            const void* dO, const float* cos_sin,
+                            int64_t cos_sin_rows, void* dQ, void* dK, void* dV,
                             int64_t n, int d, int heads, int causal, int b,
                             int m, int recursion_base, int r, uint64_t seed,
-                            double rope_base, int dtype, void* workspace,
-                            size_t workspace_bytes, void* stream);
+                            int dtype, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /*
  * exact_attention_backward — gradients of exact_attention_forward (HA page,
@@ -276,14 +279,40 @@ size_t exact_attention_backward_workspace_bytes(int64_t n, int heads);
 /*
  * sortlsh_hyperplanes — host-only: the r Gaussian hyperplanes per head the
  * hash uses (HA page, "Algorithm", Definition 1; hash family as read here).
- * G_host[h][k][t] (fp32 holding a bf16 value) = Box-Muller normal from two
- * counter-based SplitMix64 draws (purpose 1, head h, node 0, counters 2e and
- * 2e+1 with e = k*d + t): sqrt(-2 ln u1) cos(2 pi u2), u1 in (0,1],
- * u2 in [0,1), rounded to fp32 and then to the nearest bf16 (ties to even).
+ * G_host[h][k][t] (fp32 holding a bf16 value) = the Box-Muller normal g that
+ * sortlsh_gaussians computes from two counter-based SplitMix64 draws
+ * (purpose 1, head h, node 0, counters 2e and 2e+1 with e = k*d + t), rounded
+ * to fp32 and then to the nearest bf16 (ties to even). Every entry point
+ * that hashes draws the same values on the device from the seed, bit for bit.
  * Touches no device. G_host must hold heads*r*d floats (r = 0: nothing is
  * written and G_host may be NULL).
  */
 int sortlsh_hyperplanes(uint64_t seed, int heads, int r, int d, float* G_host);
+
+/*
+ * sortlsh_gaussians — host-only: out[i] = the binary64 Box-Muller normal of
+ * the draws a[i] and b[i], before any rounding:
+ *   g = sqrt(-2 ln u1) cos(2 pi u2), u1 = ((a >> 11) + 1) 2^-53,
+ *   u2 = (b >> 11) 2^-53,
+ * with ln, sqrt and cos evaluated by fixed series and Newton steps in
+ * correctly rounded binary64 additions, subtractions, multiplications and
+ * divisions only (no fused multiply-add, no library function), so that every
+ * IEEE-754 platform, the GPU included, computes the same bits:
+ *   ln u:   u = f 2^e, f in [1,2); if f > sqrt 2: f = f/2, e = e+1;
+ *           s = (f-1)/(f+1), z = s s, p = Horner in z of 1/(2k+1) for
+ *           k = 11..0, ln u = e ln2 + (2s) p;
+ *   sqrt y: y = m 2^e, m in [1,2); if e odd: m = 2m, e = e-1;
+ *           x = (1+m)/2, then x = (x + m/x)/2 six times; result x 2^(e/2)
+ *           (y <= 0 gives 0);
+ *   cos 2 pi u, u = B 2^-53: q = (B + 2^50) >> 51, r = (B - q 2^51) 2^-51,
+ *           theta = r (pi/2), t = theta^2, C = Horner in t of (-1)^k/(2k)!
+ *           for k = 9..0, S = theta times Horner in t of (-1)^k/(2k+1)! for
+ *           k = 8..0; result C, -S, -C, S for q mod 4 = 0, 1, 2, 3.
+ * Constants are the binary64 values nearest to ln 2, sqrt 2, pi/2 and the
+ * coefficients. a, b and out are host arrays of count elements.
+ */
+int sortlsh_gaussians(const uint64_t* a, const uint64_t* b, int64_t count,
+                      double* out);
 
 /*
  * hyperattn_workspace_layout — where hyperattn_forward keeps its
@@ -312,16 +341,13 @@ int sortlsh_hyperplanes(uint64_t seed, int heads, int r, int d, float* G_host);
  *                                 V-norm count, alpha (float bits), b_eff
  *   HA_WS_SCHED                   uint32 [2][8] work-queue counters of the
  *                                 attention kernels (scratch, reset by each call)
- *   HA_WS_PLANES                  staging area of the hyperplanes (see below)
+ *   HA_WS_PLANES                  the call's hyperplanes, drawn on the device
+ *                                 from the seed: fp32 [heads][r][d], then at
+ *                                 the next 256-byte boundary bf16
+ *                                 [heads][16][d] (rows r..15 zero)
  *   HA_WS_DELTA ... HA_WS_SLOT_DV backward pass only (hyperattn_backward's
  *                                 workspace; bytes 0 in the forward layout):
  *                                 HA_WS_DELTA float [heads][n] = dO_i . O_i
- * Hyperplanes: the library keeps them on each device for up to 16 keys
- * (seed, heads, r, d), each copied once when first used. Once 16 are held, a
- * call with another key generates them on the host and copies them into
- * HA_WS_PLANES on the call's stream (no allocation, no device-wide wait), so
- * a fresh seed per call costs one small copy. sortlsh_hyperplanes returns the
- * same values on the host.
  */
 enum ha_ws_region {
   HA_WS_CODES_Q = 0, HA_WS_CODES_K,
@@ -340,6 +366,46 @@ int hyperattn_workspace_layout(int64_t n, int d, int heads, int causal, int b,
                                int m, int recursion_base, int r, int dtype,
                                int64_t* offsets, int64_t* bytes);
 
+/*
+ * hyperattn_debug_artifacts — the intermediate results of hyperattn_forward
+ * with the same arguments, copied to host memory for inspection: the sortLSH
+ * codes (Definition 1), the V-norm weights and prefix sums, every level's
+ * sorted order of queries and keys (Algorithm 1), and every node's uniform
+ * and V-norm sample lists with their key buckets and weights (Algorithms 2
+ * and 3) (HA page, "Algorithm"). It runs the forward pass's front end (the
+ * hyperplanes, hash, V norms, sort and samples) on `stream` into the
+ * workspace, copies each requested region, and waits for `stream` before it
+ * returns (a debugging call; nothing else is waited for). No attention is
+ * computed.
+ * Every field of `out` is a HOST pointer or NULL (region not copied); each
+ * must hold the bytes hyperattn_workspace_layout reports for its region, in
+ * the layout described there. A causal call with n <= recursion_base (one
+ * exact block) has no sub-problems: only the codes, W and P are produced.
+ * Arguments, workspace and errors as hyperattn_forward (Q, K, V, dtype and
+ * workspace size); workspace: >= hyperattn_workspace_bytes(...).
+ */
+typedef struct ha_artifacts {
+  uint8_t* codes_q;    /* HA_WS_CODES_Q  uint8  [heads][n]            */
+  uint8_t* codes_k;    /* HA_WS_CODES_K  uint8  [heads][n]            */
+  uint64_t* vnorm_w;   /* HA_WS_VNORM_W  uint64 [heads][n]            */
+  uint64_t* vnorm_p;   /* HA_WS_VNORM_P  uint64 [heads][n+1]          */
+  int32_t* perm_q;     /* HA_WS_PERM_Q   int32  [L][heads][S]         */
+  int32_t* perm_k;     /* HA_WS_PERM_K   int32  [L][heads][S]         */
+  int32_t* rank_k;     /* HA_WS_RANK_K   int32  [L][heads][S]         */
+  int32_t* u_idx;      /* HA_WS_U_IDX    int32  [heads][nodes][m]     */
+  int32_t* u_bkt;      /* HA_WS_U_BKT    int32  [heads][nodes][m]     */
+  int32_t* v_idx;      /* HA_WS_V_IDX    int32  [heads][nodes][m]     */
+  int32_t* v_bkt;      /* HA_WS_V_BKT    int32  [heads][nodes][m]     */
+  float* v_w;          /* HA_WS_V_W      float  [heads][nodes][m]     */
+  int32_t* node_meta;  /* HA_WS_NODE_META int32 [heads][nodes][4]     */
+} ha_artifacts;
+int hyperattn_debug_artifacts(const void* Q, const void* K, const void* V,
+                              int64_t n, int d, int heads, int causal, int b,
+                              int m, int recursion_base, int r, uint64_t seed,
+                              int dtype, void* workspace,
+                              size_t workspace_bytes, void* stream,
+                              const ha_artifacts* out);
+
 /* Message for the last error on the calling thread ("" if none); valid until
  * the next call into the library on this thread. */
 const char* hyperattn_last_error(void);
@@ -357,6 +423,9 @@ int hyperattn_profile_reset(void);
 int hyperattn_profile_count(void);                 /* number of kernel names */
 const char* hyperattn_profile_name(int i);
 int64_t hyperattn_profile_launches(int i);
+/* work-groups launched under name i, summed over its launches (persistent
+ * launches: the resident work-groups the occupancy query gave) */
+int64_t hyperattn_profile_groups(int i);
 double hyperattn_profile_total_ms(int i);
 
 #ifdef __cplusplus

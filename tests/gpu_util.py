@@ -47,28 +47,34 @@ def banner(msg):
     print(f"[gpu-case] {msg}", flush=True)
 
 
-def check_artifacts(w, ws, layout, art, gpu_heads):
+def check_artifacts(w, ws, layout, art, gpu_heads, get=None):
     """Compare the library's integer artefacts for the listed heads (bit-exact)
-    with the oracle's artefact dict (oracle head index k <-> gpu_heads[k])."""
+    with the oracle's artefact dict (oracle head index k <-> gpu_heads[k]).
+    The regions come from the workspace ws (layout: workspace_layout's), or
+    from get(name, dtype) when given (e.g. hyperattn_debug_artifacts' host
+    copies)."""
     H, n = w.heads, w.n
-    cq = region(ws, layout, "CODES_Q", np.uint8).reshape(H, n)
-    ck = region(ws, layout, "CODES_K", np.uint8).reshape(H, n)
-    Wg = region(ws, layout, "VNORM_W", np.uint64).reshape(H, n)
-    Pg = region(ws, layout, "VNORM_P", np.uint64).reshape(H, n + 1)
+    if get is None:
+        def get(name, dtype):
+            return region(ws, layout, name, dtype)
+    cq = get("CODES_Q", np.uint8).reshape(H, n)
+    ck = get("CODES_K", np.uint8).reshape(H, n)
+    Wg = get("VNORM_W", np.uint64).reshape(H, n)
+    Pg = get("VNORM_P", np.uint64).reshape(H, n + 1)
     subs = art["subs"]
     L = max(s[0] for s in subs)
     S = n if not w.causal else n // 2
-    permq = region(ws, layout, "PERM_Q", np.int32).reshape(L, H, S)
-    permk = region(ws, layout, "PERM_K", np.int32).reshape(L, H, S)
-    rankk = region(ws, layout, "RANK_K", np.int32).reshape(L, H, S)
+    permq = get("PERM_Q", np.int32).reshape(L, H, S)
+    permk = get("PERM_K", np.int32).reshape(L, H, S)
+    rankk = get("RANK_K", np.int32).reshape(L, H, S)
     nodes = 2 ** L - 1 if w.causal else 1
     m = w.m
-    uidx = region(ws, layout, "U_IDX", np.int32).reshape(H, nodes, m)
-    ubkt = region(ws, layout, "U_BKT", np.int32).reshape(H, nodes, m)
-    vidx = region(ws, layout, "V_IDX", np.int32).reshape(H, nodes, m)
-    vbkt = region(ws, layout, "V_BKT", np.int32).reshape(H, nodes, m)
-    vw = region(ws, layout, "V_W", np.float32).reshape(H, nodes, m)
-    meta = region(ws, layout, "NODE_META", np.int32).reshape(H, nodes, 4)
+    uidx = get("U_IDX", np.int32).reshape(H, nodes, m)
+    ubkt = get("U_BKT", np.int32).reshape(H, nodes, m)
+    vidx = get("V_IDX", np.int32).reshape(H, nodes, m)
+    vbkt = get("V_BKT", np.int32).reshape(H, nodes, m)
+    vw = get("V_W", np.float32).reshape(H, nodes, m)
+    meta = get("NODE_META", np.int32).reshape(H, nodes, 4)
     for k, h in enumerate(gpu_heads):
         assert np.array_equal(cq[h], art["codes_q"][k]), f"codes_q head {h}"
         assert np.array_equal(ck[h], art["codes_k"][k]), f"codes_k head {h}"
@@ -93,8 +99,9 @@ def check_artifacts(w, ws, layout, art, gpu_heads):
                                   a["v_w"].view(np.uint32))
 
 
-def run_forward(w, Q, K, V, fill=True):
-    """hyperattn_forward through the C ABI with a visible workspace."""
+def run_forward(w, Q, K, V, fill=True, nan_outputs=False):
+    """hyperattn_forward through the C ABI with a visible workspace; with
+    nan_outputs, O and lse start as NaN (so unwritten rows show)."""
     import torch
     from approximate_softmax_attention_amd import api
     dt = 1 if w.dtype == "bf16" else 0
@@ -104,8 +111,12 @@ def run_forward(w, Q, K, V, fill=True):
     if fill:
         ws.fill_(0xAB)
     q, k, v = (to_dev(x, w.dtype) for x in (Q, K, V))
+    out = lse_out = None
+    if nan_outputs:
+        out = torch.full_like(q, float("nan"))
+        lse_out = torch.full((w.heads, w.n), float("nan"), device=q.device)
     O, L = api.forward(q, k, v, causal=w.causal, b=w.b, m=w.m, r=w.r,
                        recursion_base=w.recursion_base, seed=w.method_seed, return_lse=True,
-                       workspace=ws)
+                       workspace=ws, out=out, lse_out=lse_out)
     torch.cuda.synchronize()
     return O, L, ws, layout

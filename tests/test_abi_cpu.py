@@ -60,14 +60,21 @@ def test_rope_table_equals_oracle(n, d, base):
 def test_forward_rope_validates_before_any_device_call():
     lib = L()
     p = _vp(256)
-    rc = lib.hyperattn_forward_rope(p, p, p, p, p, p, None, 1024, 64, 1, 0, 128, 128, 4096, 8,
-                                    1, 1.0, 1, p, 1 << 20, None)
-    assert rc == -3 and "rope_base" in _lib.last_error()
-    rc = lib.hyperattn_forward_rope(p, p, p, None, p, p, None, 1024, 64, 1, 0, 128, 128, 4096,
-                                    8, 1, 10000.0, 1, p, 1 << 20, None)
+    # Q, K, V, cos_sin, rows, Q_rot, K_rot, O, lse, n, d, heads, causal, b, m, base, r, seed,
+    # dtype, workspace, bytes, stream
+    rc = lib.hyperattn_forward_rope(p, p, p, None, 1024, p, p, p, None, 1024, 64, 1, 0, 128, 128,
+                                    4096, 8, 1, 1, p, 1 << 20, None)
+    assert rc == -1 and "cos/sin" in _lib.last_error()
+    rc = lib.hyperattn_forward_rope(p, p, p, p, 1000, p, p, p, None, 1024, 64, 1, 0, 128, 128,
+                                    4096, 8, 1, 1, p, 1 << 20, None)
+    assert rc == -2 and "1000 rows" in _lib.last_error()
+    rc = lib.hyperattn_forward_rope(p, p, p, p, 1024, None, p, p, None, 1024, 64, 1, 0, 128, 128,
+                                    4096, 8, 1, 1, p, 1 << 20, None)
     assert rc == -1 and "Q_rot" in _lib.last_error()
     rc = lib.rope_table(16, 96, 10000.0, None)
     assert rc == -3
+    for base in (1.0, float("nan"), float("inf")):
+        assert lib.rope_table(16, 64, base, None) == -3 and "rope_base" in _lib.last_error()
 
 
 def test_backward_validates_before_any_device_call():
@@ -103,19 +110,58 @@ def test_backward_rope_validates_before_any_device_call():
     lib = L()
     p = _vp(256)
     need = lib.hyperattn_backward_workspace_bytes(1024, 64, 1, 0, 128, 128, 4096, 8, 1)
-    for base in (1.0, float("nan"), float("inf")):
-        rc = lib.hyperattn_backward_rope(p, p, p, p, p, p, p, p, p, 1024, 64, 1, 0, 128, 128,
-                                         4096, 8, 1, base, 1, p, need, None)
-        assert rc == -3 and "rope_base" in _lib.last_error()
-    rc = lib.hyperattn_backward_rope(p, p, p, p, None, p, p, p, p, 1024, 64, 1, 0, 128, 128,
-                                     4096, 8, 1, 10000.0, 1, p, need, None)
+    # Q_rot, K_rot, V, O, lse, dO, cos_sin, rows, dQ, dK, dV, n, d, heads, causal, b, m, base,
+    # r, seed, dtype, workspace, bytes, stream
+    rc = lib.hyperattn_backward_rope(p, p, p, p, p, p, None, 1024, p, p, p, 1024, 64, 1, 0, 128,
+                                     128, 4096, 8, 1, 1, p, need, None)
+    assert rc == -1 and "cos/sin" in _lib.last_error()
+    rc = lib.hyperattn_backward_rope(p, p, p, p, p, p, p, 512, p, p, p, 1024, 64, 1, 0, 128,
+                                     128, 4096, 8, 1, 1, p, need, None)
+    assert rc == -2 and "512 rows" in _lib.last_error()
+    rc = lib.hyperattn_backward_rope(p, p, p, p, None, p, p, 1024, p, p, p, 1024, 64, 1, 0, 128,
+                                     128, 4096, 8, 1, 1, p, need, None)
     assert rc == -1 and "lse" in _lib.last_error()
-    rc = lib.hyperattn_backward_rope(p, p, p, p, p, p, p, p, p, 1024, 64, 1, 0, 128, 128, 4096,
-                                     8, 1, 10000.0, 0, p, need, None)
+    rc = lib.hyperattn_backward_rope(p, p, p, p, p, p, p, 1024, p, p, p, 1024, 64, 1, 0, 128,
+                                     128, 4096, 8, 1, 0, p, need, None)
     assert rc != 0 and "bf16" in _lib.last_error()
-    assert lib.hyperattn_backward_rope(None, None, None, None, None, None, None, None, None, 0,
-                                       64, 2, 1, 256, 256, 4096, 8, 1, 10000.0, 1, None, 0,
+    # the gradients must not be written over the table
+    rc = lib.hyperattn_backward_rope(p, p, p, p, _vp(1 << 30), p, _vp(3 << 24), 1024,
+                                     _vp(3 << 24), _vp(4 << 24), _vp(5 << 24), 1024, 64, 1, 0,
+                                     128, 128, 4096, 8, 1, 1, _vp(6 << 24), need, None)
+    assert rc == -2 and "cos_sin" in _lib.last_error()
+    assert lib.hyperattn_backward_rope(None, None, None, None, None, None, None, 0, None, None,
+                                       None, 0, 64, 2, 1, 256, 256, 4096, 8, 1, 1, None, 0,
                                        None) == 0
+
+
+def test_gaussians_equal_oracle_bit_for_bit():
+    """The library's Box-Muller normals (binary64, before any rounding) are
+    the oracle's bit for bit: both follow the same sequence of correctly
+    rounded binary64 operations."""
+    from approximate_softmax_attention_amd import api
+    from oracle import gaussian
+    rs = np.random.default_rng(12)
+    a = rs.integers(0, 2 ** 64, 200000, dtype=np.uint64, endpoint=False)
+    b = rs.integers(0, 2 ** 64, 200000, dtype=np.uint64, endpoint=False)
+    # edges: u1 = 1 and u1 = 2^-53, the quadrant boundaries of u2, f next to sqrt 2
+    edge_a = np.array([2 ** 64 - 1, 0, 2 ** 63, (2 ** 52) << 11, ((1 << 53) - 1) << 11],
+                      dtype=np.uint64)
+    edge_b = np.array([0, (1 << 50) << 11, ((1 << 50) - 1) << 11, (3 << 50) << 11,
+                       ((7 << 50) + 1) << 11], dtype=np.uint64)
+    a = np.concatenate([a, edge_a])
+    b = np.concatenate([b, edge_b])
+    got = api.gaussians(a, b)
+    ref = gaussian.box_muller(a, b)
+    assert np.array_equal(got.view(np.uint64), ref.view(np.uint64))
+
+
+def test_sortlsh_hash_workspace_holds_the_hyperplanes():
+    lib = L()
+    planes = 3 * 8 * 64 * 4 + 3 * 16 * 64 * 2
+    assert lib.sortlsh_hash_workspace_bytes(1000, 64, 3, 8, 0) == planes
+    assert lib.sortlsh_hash_workspace_bytes(1000, 64, 3, 8, 1) > planes
+    assert lib.sortlsh_hash_workspace_bytes(1000, 96, 3, 8, 0) == 0
+    assert "d=96" in _lib.last_error()
 
 
 def test_backward_layout_regions():
@@ -143,8 +189,8 @@ def test_workspace_sizes_and_validation_messages():
     assert ws_bytes(d=96) == 0 and "d=96" in _lib.last_error()
     assert ws_bytes(r=9) == 0 and "r=9" in _lib.last_error()
     assert ws_bytes(r=-1) == 0 and "r=-1" in _lib.last_error()
-    # r only changes the hyperplane staging area (fp32 [heads][r][d])
-    assert ws_bytes(r=8) - ws_bytes(r=0) == 1 * 8 * 64 * 4 and ws_bytes(r=0) > 0
+    # r only changes the hyperplane area (fp32 [heads][max(r, 1)][d])
+    assert ws_bytes(r=8) - ws_bytes(r=0) == 1 * 7 * 64 * 4 and ws_bytes(r=0) > 0
     assert ws_bytes(b=100) == 0 and "divide" in _lib.last_error()
     assert ws_bytes(n=96, causal=1, b=1, base=2) == 0 and "odd" in _lib.last_error()
     assert ws_bytes(m=0) == 0
@@ -173,7 +219,7 @@ def test_layout_regions_disjoint_and_aligned():
         assert lay["PERM_Q"][1] == levels * 4 * S * 4
         assert lay["VNORM_P"][1] == 4 * 8193 * 8
         assert (lay["PART_O"][1] > 0) == bool(causal)
-        # hyperplane staging: fp32 [4][8][128] (256-aligned), then bf16 [4][16][128]
+        # hyperplanes: fp32 [4][8][128] (256-aligned), then bf16 [4][16][128]
         assert lay["PLANES"][1] == 4 * 8 * 128 * 4 + 4 * 16 * 128 * 2
 
 
@@ -217,6 +263,8 @@ def test_entry_points_validate_before_any_device_call():
     assert rc == -4
     rc = lib.sortlsh_hash(p, 5000, 64, 1, 8, 1, 1, p, p, None, 0, None)
     assert rc == -4
+    rc = lib.sortlsh_hash(p, 5000, 64, 1, 8, 1, 1, p, None, p, 100, None)
+    assert rc == -4 and "needed" in _lib.last_error()
     # empty problems are valid and touch nothing
     assert lib.hyperattn_forward(None, None, None, None, None, 0, 64, 4, 1, 256, 256, 4096,
                                  8, 1, 1, None, 0, None) == 0
@@ -233,7 +281,8 @@ def test_no_device_reports_hip_error():
     except ImportError:
         pass
     lib = L()
-    rc = lib.sortlsh_hash(_vp(256), 64, 64, 1, 8, 1, 1, _vp(1 << 20), None, None, 0, None)
+    rc = lib.sortlsh_hash(_vp(256), 64, 64, 1, 8, 1, 1, _vp(1 << 20), None, _vp(1 << 24),
+                          1 << 20, None)
     assert rc == -5 and _lib.last_error()
 
 
@@ -272,7 +321,8 @@ def test_outputs_must_not_overlap_inputs_or_each_other():
                                       _vp(12 << 24), 1 << 20, None)
     assert rc == -2 and "dQ overlaps dK" in _lib.last_error()
     # hash codes written over the rows they hash
-    rc = lib.sortlsh_hash(q, 1024, 64, 1, 8, 1, 1, _vp((1 << 24) + 100), None, None, 0, None)
+    rc = lib.sortlsh_hash(q, 1024, 64, 1, 8, 1, 1, _vp((1 << 24) + 100), None, ws, 1 << 20,
+                          None)
     assert rc == -2 and "codes overlaps the input X" in _lib.last_error()
 
 

@@ -83,6 +83,9 @@ BACKWARD_CASES = {
     "causal_exhaustive_d128": ("chatglm2_causal_n32768_d128_h32_bf16",
                                dict(heads=1, n=1024, b=64, m=200, recursion_base=128,
                                     rope=False)),
+    # the sizes of the forward's bf16 slot-window refill (b + 2m > 1024)
+    "slot_refill_d128": ("chatglm2_causal_n32768_d128_h32_bf16",
+                         dict(heads=1, n=8192, b=512, m=300, recursion_base=1024, rope=False)),
 }
 
 
@@ -206,10 +209,10 @@ def test_backward_rope(name):
 
 
 def test_forward_and_backward_replay_in_a_hip_graph():
-    """Once its tables are on the device (a first eager call), a forward +
-    backward call enqueues only kernels and copies between device buffers, so
-    it can be captured in a HIP graph. Three replays, with eager work and
-    synchronisations between them, each equal the eager result byte for byte."""
+    """A forward + backward call enqueues only kernels on the caller's stream
+    (the hyperplanes are drawn on the device), so it can be captured in a HIP
+    graph. Three replays, with eager work and synchronisations between them,
+    each equal the eager result byte for byte."""
     banner("forward + backward in a HIP graph")
     import torch
     base, changes = BACKWARD_CASES["causal_d128"]

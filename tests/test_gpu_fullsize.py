@@ -1,19 +1,26 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times (all heads in one hyperattn_forward call).
 
-The oracle cannot run every row of a 131072-token, 32-head layer in seconds,
-so for two heads per workload it recomputes the integer artefacts in full
-(hash codes, V-norm weights and prefix sums, every level's sorts and sample
-lists; bit-exact) and O and lse on a seeded sample of rows that covers every
-recursion level and base block (tolerance as for the small cases).
+The oracle cannot run every row of a 131072-token, 32-head layer in seconds.
+For every head it recomputes the integer artefacts in full (hash codes,
+V-norm weights and prefix sums, every level's sorts and sample lists;
+bit-exact), and O and lse on position-stratified rows: 4096 on the first and
+the last head, 256 on every other head (tolerance as for the small cases).
+The outputs are prefilled with NaN, so every row of every head must have been
+written. The oracle's heads run in parallel worker processes, each of which
+regenerates its head's seeded inputs.
 """
+
+import concurrent.futures as cf
+import multiprocessing as mp
+import os
 
 import numpy as np
 import pytest
 
 from approximate_softmax_attention_amd import workloads as wl
 from oracle import hyperattention as oha
-from tests.gpu_util import TOL, banner, check_artifacts, run_forward, to_np
+from tests.gpu_util import TOL, banner, check_artifacts, region, run_forward, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -34,32 +41,100 @@ def sample_rows(w, count=160, seed=7):
     return np.array(sorted(rows))
 
 
+def stratified_rows(w, count, seed):
+    """One seeded row in each of `count` equal position strata, plus the
+    sequence ends and (causal) every base-block edge."""
+    rs = np.random.default_rng(seed)
+    edges = np.linspace(0, w.n, count + 1).astype(np.int64)
+    rows = {int(rs.integers(lo, hi)) for lo, hi in zip(edges[:-1], edges[1:]) if hi > lo}
+    rows |= {0, w.n - 1}
+    if w.causal:
+        B = w.n
+        while B > w.recursion_base:
+            B //= 2
+        rows |= {x for k in range(w.n // B) for x in (k * B, k * B + B - 1)}
+    return np.array(sorted(rows))
+
+
+def _oracle_head(job):
+    """The oracle's forward on one head, in a worker process: the head's
+    inputs are regenerated there from the workload's seeds (no GPU state and
+    no input arrays cross the process boundary)."""
+    name, h, rows = job
+    w = wl.WORKLOADS[name]
+    Q, K, V, _ = wl.make_inputs(w, heads=[h])
+    art = {}
+    O, L = oha.hyperattention(Q, K, V, causal=w.causal, b=w.b, m=w.m, r=w.r,
+                              recursion_base=w.recursion_base, seed=w.method_seed, rows=rows,
+                              artifacts=art, head_ids=[h])
+    return h, rows, O[0][rows], L[0][rows], art
+
+
+def oracle_heads(jobs):
+    """_oracle_head of each (workload name, head, rows) job on at most eight
+    freshly spawned worker processes."""
+    workers = max(1, min(8, len(os.sched_getaffinity(0)), len(jobs)))
+    with cf.ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn")) as ex:
+        return list(ex.map(_oracle_head, jobs))
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_fullsize_sampled_rows_and_artifacts(name):
+    import torch
     w = wl.WORKLOADS[name]
     banner(f"fullsize {name}: inputs")
     Q, K, V, _ = wl.make_inputs_parallel(w)
-    banner(f"fullsize {name}: gpu forward")
-    O, L, ws, layout = run_forward(w, Q, K, V)
-    heads = [0, w.heads - 1]
-    rows = sample_rows(w)
-    banner(f"fullsize {name}: oracle on heads {heads}, {len(rows)} rows")
-    art = {}
-    Oref, Lref = oha.hyperattention(Q[heads], K[heads], V[heads], causal=w.causal, b=w.b,
-                                    m=w.m, r=w.r, recursion_base=w.recursion_base,
-                                    seed=w.method_seed, rows=rows, artifacts=art,
-                                    head_ids=heads)
-    check_artifacts(w, ws, layout, art, heads)
-    Og = to_np(O[heads][:, rows])
-    Lg = to_np(L[heads][:, rows])
-    for k in range(len(heads)):
-        ref = Oref[k][rows]
-        err = np.abs(Og[k] - ref).max() / np.abs(ref).max()
-        lerr = np.abs(Lg[k] - Lref[k][rows]).max()
-        print(f"{name} head {heads[k]}: max-rel {err:.2e}, lse {lerr:.2e}")
-        assert err <= TOL[w.dtype]
-        assert lerr <= TOL[w.dtype]
-    assert np.isfinite(to_np(O)).all()
+    banner(f"fullsize {name}: gpu forward (outputs prefilled with NaN)")
+    O, L, ws, layout = run_forward(w, Q, K, V, nan_outputs=True)
+    assert bool(torch.isfinite(O).all()) and bool(torch.isfinite(L).all()), \
+        "an output row was not written"
+    jobs = [(name, h, stratified_rows(w, 4096 if h in (0, w.heads - 1) else 256, seed=100 + h))
+            for h in range(w.heads)]
+    banner(f"fullsize {name}: oracle on all {w.heads} heads "
+           f"({sum(len(r) for _, _, r in jobs)} rows)")
+    res = oracle_heads(jobs)
+    Og, Lg = to_np(O), to_np(L)
+    host = {name: region(ws, layout, name, np.uint8) for name in layout if layout[name][1]}
+    worst = (0.0, 0.0)
+    for h, rows, Oref, Lref, art in res:
+        check_artifacts(w, ws, layout, art, [h], get=lambda nm, dt: host[nm].view(dt))
+        err = np.abs(Og[h][rows] - Oref).max() / np.abs(Oref).max()
+        lerr = np.abs(Lg[h][rows] - Lref).max()
+        worst = (max(worst[0], err), max(worst[1], lerr))
+        assert err <= TOL[w.dtype], (h, err)
+        assert lerr <= TOL[w.dtype], (h, lerr)
+    print(f"{name}: {w.heads} heads, artefacts bit-exact; worst max-rel {worst[0]:.2e}, "
+          f"lse {worst[1]:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("n", [32768, 131072])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fullsize_exact_attention_sampled_rows(n, causal):
+    """The plain exact attention (the speed baseline and the recursion's base
+    case) at the long sizes, on sampled rows of two heads."""
+    import torch
+    from approximate_softmax_attention_amd import api
+    from oracle import exact as oexact
+    from tests.gpu_util import to_dev
+    w = wl.scaled(wl.WORKLOADS["longctx_causal_n131072_d128_h32_bf16"], heads=2, n=n,
+                  causal=causal)
+    banner(f"exact n={n} causal={causal}: inputs")
+    Q, K, V, _ = wl.make_inputs(w)
+    q, k, v = (to_dev(x, "bf16") for x in (Q, K, V))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((2, n), float("nan"), device="cuda")
+    api.exact(q, k, v, causal=causal, out=o, lse_out=lse)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    rows = stratified_rows(wl.scaled(w, causal=False), 48, seed=5)
+    Og, Lg = to_np(o), to_np(lse)
+    for h in range(2):
+        Oref, Lref = oexact.exact_attention_rows(Q[h], K[h], V[h], rows, causal=causal)
+        err = np.abs(Og[h][rows] - Oref).max() / np.abs(Oref).max()
+        lerr = np.abs(Lg[h][rows] - Lref).max()
+        print(f"exact n={n} causal={causal} head {h}: max-rel {err:.2e}, lse {lerr:.2e}",
+              flush=True)
+        assert err <= TOL["bf16"] and lerr <= TOL["bf16"]
 
 
 def backward_rows(w, art, seed=11):

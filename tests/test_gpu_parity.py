@@ -40,7 +40,7 @@ def _sync():
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("n", [1, 77, 300])
+@pytest.mark.parametrize("n", [1, 77, 300, 5000])
 def test_exact_attention(dtype, d, causal, n):
     banner(f"exact dtype={dtype} d={d} causal={causal} n={n}")
     w, Q, K, V, _ = _inputs("single_head_noncausal_n1024_d64_fp32", heads=2, n=n, d=d,
@@ -156,6 +156,21 @@ FORWARD_CASES = {
                          dict(heads=2, n=4096, b=128, m=100, recursion_base=512)),
     "causal_bf16_ragged_base": ("chatglm2_causal_n32768_d128_h32_bf16",
                                 dict(heads=1, n=1536, b=96, m=300, recursion_base=200)),
+    # fp32 at d = 128: 64-key fp32 tiles (16 per slot window), causal with
+    # recursion and merge, and non-causal
+    "causal_fp32_d128": ("chatglm2_causal_n32768_d128_h32_bf16",
+                         dict(heads=2, n=2048, dtype="fp32", b=64, m=48, recursion_base=256)),
+    "noncausal_fp32_d128": ("single_head_noncausal_n1024_d64_fp32",
+                            dict(heads=2, n=1024, d=128, b=128, m=96)),
+    # bf16 items of more than 8 tiles (b + 2m > 1024 slots): the slot window
+    # is refilled inside the item
+    "noncausal_bf16_d128_slot_refill": ("single_head_noncausal_n1024_d64_fp32",
+                                        dict(heads=2, n=4096, d=128, dtype="bf16", b=512,
+                                             m=512)),
+    "noncausal_bf16_d64_slot_refill": ("single_head_noncausal_n1024_d64_fp32",
+                                       dict(heads=2, n=4096, dtype="bf16", b=256, m=512)),
+    "causal_bf16_d128_slot_refill": ("chatglm2_causal_n32768_d128_h32_bf16",
+                                     dict(heads=1, n=8192, b=512, m=300, recursion_base=1024)),
     # r = 0: the local block mask in place of sortLSH
     "local_mask_causal_bf16_d128": ("chatglm2_causal_n32768_d128_h32_bf16",
                                     dict(heads=2, n=4096, b=128, m=100, r=0,
@@ -279,16 +294,17 @@ def test_planted_workload_full():
     assert hits / tot > 0.5
 
 
-def test_rowsum_estimate_matches_oracle():
-    banner("rowsum")
-    w, Q, K, V, _ = _inputs("single_head_noncausal_n1024_d64_fp32", heads=2, n=2048, d=128,
-                            dtype="bf16", b=128, m=96)
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp32", 128), ("fp32", 64)])
+def test_rowsum_estimate_matches_oracle(dtype, d):
+    banner(f"rowsum {dtype} d={d}")
+    w, Q, K, V, _ = _inputs("single_head_noncausal_n1024_d64_fp32", heads=2, n=2048, d=d,
+                            dtype=dtype, b=128, m=96)
     api = _api()
-    ld = api.rowsum_estimate(to_dev(Q, "bf16"), to_dev(K, "bf16"), b=w.b, m=w.m, r=w.r,
+    ld = api.rowsum_estimate(to_dev(Q, dtype), to_dev(K, dtype), b=w.b, m=w.m, r=w.r,
                              seed=w.method_seed)
     _sync()
     ref = oha.rowsum_estimate(Q, K, b=w.b, m=w.m, r=w.r, seed=w.method_seed)
-    assert np.abs(to_np(ld) - ref).max() <= TOL["bf16"]
+    assert np.abs(to_np(ld) - ref).max() <= TOL[dtype]
 
 
 # ---------------------------------------------------------------- edge cases
@@ -359,13 +375,12 @@ def test_deterministic_repeat():
     assert not torch.equal(a, c)
 
 
-def test_more_seeds_than_the_device_keeps():
-    """The library keeps the hyperplanes of 16 keys on each device; calls with
-    further seeds stage theirs through the workspace on the call's stream.
-    Twenty seeds, the last four enqueued back to back without a wait: every
-    call's codes are bit-exact for its own seed, O and lse match the oracle
-    for a staged seed, and a repeat call gives the same bytes."""
-    banner("hyperplane staging: 20 seeds")
+def test_fresh_seed_every_call():
+    """Every call draws its hyperplanes on the device from its own seed, into
+    its own workspace, on the call's stream: twenty seeds enqueued back to
+    back without a wait each give the codes of their own seed, O and lse match
+    the oracle, and a repeat call gives the same bytes."""
+    banner("hyperplanes drawn per call: 20 seeds back to back")
     import torch
     api = _api()
     w, Q, K, V, _ = _inputs("planted_noncausal_n8192_d64_h8_bf16", heads=2, n=1024, b=128, m=64,
@@ -376,13 +391,11 @@ def test_more_seeds_than_the_device_keeps():
     nb = api.workspace_bytes(w.n, w.d, w.heads, **kw)
     seeds = list(range(7000, 7020))
     outs = {}
-    for i, sd in enumerate(seeds):
+    for sd in seeds:
         ws = api.alloc_workspace(nb, "cuda")
         ws.fill_(0xAB)
         o, lse = api.forward(q, k, v, seed=sd, return_lse=True, workspace=ws, **kw)
         outs[sd] = (o, lse, ws)
-        if i < 16:
-            _sync()
     _sync()
     for sd in seeds:
         cq = region(outs[sd][2], layout, "CODES_Q", np.uint8).reshape(w.heads, w.n)
@@ -396,6 +409,116 @@ def test_more_seeds_than_the_device_keeps():
     again = api.forward(q, k, v, seed=sd, **kw)
     _sync()
     assert torch.equal(again, outs[sd][0])
+
+
+@pytest.mark.parametrize("d,r", [(128, 8), (64, 8), (128, 3)])
+def test_device_hyperplanes_equal_oracle(d, r):
+    """The hyperplanes the device draws into the workspace (fp32 values and
+    the bf16 layout with rows r..15 zero) equal the oracle's bit for bit, for
+    64 heads and three seeds (the binary64 Box-Muller is evaluated with the
+    same correctly rounded operations on both sides)."""
+    banner(f"device hyperplanes d={d} r={r}")
+    import torch
+    api = _api()
+    H, n = 64, 256
+    x = torch.randn((H, n, d), device="cuda", dtype=torch.bfloat16)
+    kw = dict(causal=False, b=128, m=64, r=r)
+    layout = api.workspace_layout(n, d, H, **kw)
+    for sd in (0, 1004, 2 ** 63 + 12345):
+        ws = api.alloc_workspace(api.workspace_bytes(n, d, H, **kw), "cuda")
+        ws.fill_(0xCD)
+        api.forward(x, x, x, seed=sd, workspace=ws, **kw)
+        _sync()
+        planes = region(ws, layout, "PLANES", np.uint8)
+        f32 = planes[:H * r * d * 4].view(np.float32).reshape(H, r, d)
+        off16 = (H * r * d * 4 + 255) // 256 * 256
+        b16 = planes[off16:off16 + H * 16 * d * 2].view(np.uint16).reshape(H, 16, d)
+        ref = osl.hyperplanes(sd, H, r, d)
+        assert np.array_equal(f32.view(np.uint32), ref.view(np.uint32)), sd
+        assert np.array_equal(b16[:, :r].astype(np.uint32) << 16, ref.view(np.uint32)), sd
+        assert not b16[:, r:].any()
+        assert np.array_equal(api.hyperplanes(sd, H, r, d), ref)
+
+
+def test_first_call_of_a_fresh_seed_captured_in_a_graph():
+    """The very first call with a new seed (and a new shape), rotary forward
+    and backward, is captured in a HIP graph: the library allocates nothing
+    and copies nothing from the host, so the capture holds kernels only.
+    Three replays, with eager work and synchronisations between them, each
+    equal the eager call with the same seed byte for byte and the oracle
+    within tolerance."""
+    banner("first call of a fresh seed in a HIP graph")
+    import torch
+    from oracle import rope as orope
+    api = _api()
+    w, Q, K, V, _ = _inputs("chatglm2_causal_n32768_d128_h32_bf16", heads=2, n=3072, b=96,
+                            m=80, recursion_base=384, rope=False)
+    dO = wl.make_grad(w)
+    seed = 0x5EED_F1E5
+    kw = dict(causal=True, b=w.b, m=w.m, r=w.r, recursion_base=w.recursion_base, seed=seed)
+    q, k, v, do = (to_dev(x, "bf16") for x in (Q, K, V, dO))
+    tab = api.rope_device_table(w.n, w.d, 10000.0, q.device)
+    ws_f = api.alloc_workspace(api.workspace_bytes(w.n, w.d, w.heads, causal=True, b=w.b, m=w.m,
+                                                   r=w.r, recursion_base=w.recursion_base),
+                               "cuda")
+    ws_b = api.alloc_workspace(api.backward_workspace_bytes(
+        w.n, w.d, w.heads, causal=True, b=w.b, m=w.m, r=w.r, recursion_base=w.recursion_base),
+        "cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        o, lse, qr, kr = api.forward_rope(q, k, v, return_lse=True, return_rotated=True,
+                                          workspace=ws_f, cos_sin=tab, **kw)
+        grads = api.backward_rope(qr, kr, v, o, lse, do, workspace=ws_b, cos_sin=tab, **kw)
+    outs = (o, lse, qr, kr) + tuple(grads)
+    replays = []
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        (q.float() * 2).sum().item()          # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        replays.append([t.clone() for t in outs])
+    eo, else_, eqr, ekr = api.forward_rope(q, k, v, return_lse=True, return_rotated=True,
+                                           cos_sin=tab, **kw)
+    egrads = api.backward_rope(eqr, ekr, v, eo, else_, do, cos_sin=tab, **kw)
+    torch.cuda.synchronize()
+    for rep, got in enumerate(replays):
+        for a_, b_ in zip(got, (eo, else_, eqr, ekr) + tuple(egrads)):
+            assert torch.equal(a_, b_), rep
+    ang = orope.angle_table(w.n, w.d, 10000.0)
+    Qo = np.stack([orope.rope(Q[h], dtype="bf16", table=ang) for h in range(w.heads)])
+    Ko = np.stack([orope.rope(K[h], dtype="bf16", table=ang) for h in range(w.heads)])
+    Oref, Lref = oha.hyperattention(Qo, Ko, V, **kw)
+    assert max_rel(to_np(replays[0][0]), Oref) <= TOL["bf16"]
+    assert np.abs(to_np(replays[0][1]) - Lref).max() <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_debug_artifacts_match_oracle_and_forward(causal):
+    """hyperattn_debug_artifacts copies the front end's results to the host:
+    bit-exact against the oracle's artefacts and against the regions a
+    forward call leaves in its workspace."""
+    banner(f"debug artifacts causal={causal}")
+    api = _api()
+    if causal:
+        w, Q, K, V, _ = _inputs("chatglm2_causal_n32768_d128_h32_bf16", heads=2, n=4096, b=128,
+                                m=100, recursion_base=512)
+    else:
+        w, Q, K, V, _ = _inputs("single_head_noncausal_n1024_d64_fp32", heads=3, n=2048, b=128,
+                                m=96)
+    q, k, v = (to_dev(x, w.dtype) for x in (Q, K, V))
+    arts = api.debug_artifacts(q, k, v, causal=w.causal, b=w.b, m=w.m, r=w.r,
+                               recursion_base=w.recursion_base, seed=w.method_seed)
+    art = {}
+    oha.hyperattention(Q, K, V, causal=w.causal, b=w.b, m=w.m, r=w.r,
+                       recursion_base=w.recursion_base, seed=w.method_seed,
+                       rows=np.zeros(0, dtype=np.int64), artifacts=art)
+    check_artifacts(w, None, None, art, list(range(w.heads)),
+                    get=lambda name, dtype: arts[name].view(dtype))
+    _, _, ws, layout = _run_forward(w, Q, K, V)
+    for name in arts:
+        assert np.array_equal(arts[name].view(np.uint8), region(ws, layout, name, np.uint8)), name
 
 
 def test_rope_table_serves_shorter_and_grows():
@@ -416,3 +539,26 @@ def test_rope_table_serves_shorter_and_grows():
         tab = orope.angle_table(n, w.d, 5000.0)
         assert np.array_equal(to_np(qr)[0], orope.rope(Q[0], dtype="bf16", table=tab)), n
         assert np.array_equal(to_np(kr)[0], orope.rope(K[0], dtype="bf16", table=tab)), n
+
+
+def test_persistent_grids_follow_each_kernels_occupancy():
+    """Persistent launches size their grid from the occupancy of the kernel
+    they launch: bf16 d = 64 attention kernels fit two work-groups per CU,
+    d = 128 ones one, whichever runs first in the process."""
+    banner("persistent grid per kernel")
+    import torch
+    api = _api()
+    groups = {}
+    for d in (128, 64, 128):
+        x = torch.randn((4, 65536, d), device="cuda", dtype=torch.bfloat16)
+        with api.KernelTimer() as t:
+            api.forward(x, x, x, causal=False, b=256, m=256, seed=1)
+            api.forward(x, x, x, causal=True, b=256, m=256, recursion_base=4096, seed=1)
+            _sync()
+        got = (t.groups["bucket_attention"] // 2, t.groups["exact_base_merge"])
+        assert d not in groups or groups[d] == got, (d, groups[d], got)
+        groups[d] = got
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    print(f"resident groups: d=128 {groups[128]}, d=64 {groups[64]} on {cus} CUs", flush=True)
+    assert groups[64][0] == 2 * groups[128][0] == 2 * cus
+    assert groups[64][1] == 2 * groups[128][1] == 2 * cus
