@@ -24,6 +24,9 @@ SIGNATURES = {
     "hyperattn_forward": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32,
                                  _i32, _i32, _u64, _i32, _vp, _sz, _vp]),
     "hyperattn_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "hyperattn_forward_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
+                                         _i32, _i32, _i32, _u64, _i32, _vp]),
+    "hyperattn_noalloc_scratch_bytes": (_sz, []),
     "sortlsh_hash": (_i32, [_vp, _i64, _i32, _i32, _i32, _u64, _i32, _vp, _vp, _vp, _sz, _vp]),
     "sortlsh_hash_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32]),
     "exact_attention_forward": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,

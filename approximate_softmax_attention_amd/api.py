@@ -163,6 +163,19 @@ def _check_table(cos_sin, n, d, like):
     return cos_sin
 
 
+def forward_noalloc(q, k, v, *, causal, b=256, m=256, r=8, recursion_base=4096, seed=0,
+                    out, lse_out=None):
+    """hyperattn_forward_noalloc: the forward pass in the library's static
+    per-GPU scratch, with caller-supplied outputs (nothing is allocated)."""
+    shape, q, k, v = _qkv(q, k, v)
+    H, n, d = q.shape
+    _check_buffer(out, "out", q, q.numel(), q.dtype)
+    _check_buffer(lse_out, "lse_out", q, H * n, torch.float32)
+    _call(q, lib().hyperattn_forward_noalloc, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+          _ptr(lse_out), n, d, H, int(causal), b, m, recursion_base, r, seed, _dtype_code(q))
+    return out.reshape(shape)
+
+
 def forward_rope(q, k, v, *, causal, rope_base=10000.0, b=256, m=256, r=8,
                  recursion_base=4096, seed=0, return_lse=False, return_rotated=False,
                  workspace=None, cos_sin=None):

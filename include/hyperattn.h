@@ -105,6 +105,27 @@ int hyperattn_forward(const void* Q, const void* K, const void* V, void* O,
                       void* stream);
 
 /*
+ * hyperattn_forward_noalloc — hyperattn_forward for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * hosts that forbid allocation): it takes no workspace and allocates nothing.
+ * Its workspace is a fixed array of hyperattn_noalloc_scratch_bytes() bytes
+ * (64 MiB) in the library's device code, one per GPU, held by each GPU the
+ * library runs on until the process ends; its address is looked up once per
+ * device on that device's first call. Sizes whose workspace
+ * (hyperattn_workspace_bytes) exceeds it are refused with HA_ERR_WORKSPACE
+ * before anything is enqueued. All calls on one GPU share its array: calls
+ * that overlap on one GPU (other streams or threads) race and must be
+ * serialised by the caller. Arguments, outputs and other errors as
+ * hyperattn_forward; the same inputs and seed give the same bytes as
+ * hyperattn_forward.
+ */
+int hyperattn_forward_noalloc(const void* Q, const void* K, const void* V,
+                              void* O, float* lse, int64_t n, int d, int heads,
+                              int causal, int b, int m, int recursion_base,
+                              int r, uint64_t seed, int dtype, void* stream);
+size_t hyperattn_noalloc_scratch_bytes(void);
+
+/*
  * hyperattn_forward_rope — hyperattn_forward on Q and K that still need their
  * rotary position embedding, applied on the device in the pass that hashes
  * them (the long-context layers rotate Q and K before attention, and the

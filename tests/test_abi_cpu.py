@@ -407,3 +407,24 @@ def test_oracle_and_product_never_import_each_other():
         if uses:
             assert isinstance(fn, ast.FunctionDef) and fn.name.startswith("cpu_baseline"), \
                 (getattr(fn, "name", None), uses)
+
+
+def test_noalloc_forward_validates_before_any_device_call():
+    """hyperattn_forward_noalloc refuses sizes whose workspace exceeds its
+    64 MiB static scratch, and validates like hyperattn_forward, before any
+    device call."""
+    lib = L()
+    p = _vp(256)
+    assert lib.hyperattn_noalloc_scratch_bytes() == 64 << 20
+    # 32 heads, n = 32768, d = 128, causal: 438 MiB of workspace
+    rc = lib.hyperattn_forward_noalloc(p, p, p, p, None, 32768, 128, 32, 1, 256, 256, 4096, 8,
+                                       1, 1, None)
+    assert rc == -4 and "static scratch" in _lib.last_error()
+    rc = lib.hyperattn_forward_noalloc(p, p, p, p, None, 1000, 64, 1, 0, 128, 128, 4096, 8, 1,
+                                       1, None)
+    assert rc == -2 and "divide" in _lib.last_error()
+    rc = lib.hyperattn_forward_noalloc(None, p, p, p, None, 1024, 64, 1, 0, 128, 128, 4096, 8,
+                                       1, 1, None)
+    assert rc == -1
+    assert lib.hyperattn_forward_noalloc(None, None, None, None, None, 0, 64, 2, 1, 256, 256,
+                                         4096, 8, 1, 1, None) == 0
