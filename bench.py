@@ -23,6 +23,37 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "causal HyperAttention fwd tokens/s at n=131k,d=128,32 heads; % MFMA peak"
+
+
+def metric_for(w):
+    """The headline metric for the headline workload; the same wording with
+    the workload's own shape for the others."""
+    from approximate_softmax_attention_amd import workloads as wl
+    if w.name == wl.HEADLINE:
+        return METRIC
+    kind = "causal" if w.causal else "non-causal"
+    return f"{kind} HyperAttention fwd tokens/s at n={w.n},d={w.d},{w.heads} heads"
+
+
+def data_for(w):
+    parts = ["seeded iid N(0,1)"]
+    if w.planted:
+        parts.append(f"{w.planted} planted keys per query")
+    if w.rope:
+        parts.append("RoPE on Q,K")
+    return "synthetic (" + ", ".join(parts) + ")"
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
 PEAK_BF16 = 2.5e15        # MI355X dense bf16 MFMA, FLOP/s
 PEAK_FP32_MFMA = 157.3e12
 PEAK_HBM = 8.0e12         # bytes/s
@@ -139,12 +170,42 @@ def hbm_bytes(w):
             "sort_scatter": levels * H * n * 9}
 
 
+def levels_of(w):
+    """Sub-problem sizes of the causal recursion (non-causal: [n])."""
+    if not w.causal:
+        return [w.n]
+    out, size = [], w.n
+    while size > w.recursion_base:
+        size //= 2
+        out.append(size)
+    return out
+
+
+def attention_bytes(w):
+    """Algorithmic HBM bytes per launch of the attention kernels: the bucket
+    kernel reads each query, key and value row of every level's sub-problems
+    once (gathered in bucket order) and writes each query row's partial
+    output and lse once; the base case reads Q, K and V once, reads every
+    level's partials once and writes O and lse."""
+    H, n, d = w.heads, w.n, w.d
+    es = 2 if w.dtype == "bf16" else 4
+    row, out_row = d * es, d * es + 4
+    lv = levels_of(w)
+    rows = n // 2 if w.causal else n
+    out = {"bucket_attention": H * len(lv) * rows * (3 * row + out_row)}
+    if w.causal:
+        out["exact_base_merge"] = H * (3 * n * row + len(lv) * rows * out_row + n * out_row)
+    return out
+
+
 def exact_flops(w):
     H, n, d = w.heads, w.n, w.d
     return H * 4.0 * d * (n * (n + 1) / 2 if w.causal else n * n)
 
 
-def make_device_inputs(w, torch):
+def make_device_inputs(w, torch, pairs=None):
+    """Q, K, V on the device; the planted pairs of each head go to `pairs`
+    (a list) when given."""
     from approximate_softmax_attention_amd import workloads as wl
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     Q = torch.empty((w.heads, w.n, w.d), dtype=dt, device="cuda")
@@ -152,16 +213,40 @@ def make_device_inputs(w, torch):
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
 
     def one(h):
-        q, k, v, _ = wl.make_head(w, h)
-        return h, q, k, v
+        q, k, v, pr = wl.make_head(w, h)
+        return h, q, k, v, pr
 
     with cf.ThreadPoolExecutor(workers) as ex:
-        for h, q, k, v in ex.map(one, range(w.heads)):
+        for h, q, k, v, pr in ex.map(one, range(w.heads)):
             Q[h].copy_(torch.from_numpy(q).to(dt))
             K[h].copy_(torch.from_numpy(k).to(dt))
             V[h].copy_(torch.from_numpy(v).to(dt))
+            if pairs is not None:
+                pairs.append(pr)
     torch.cuda.synchronize()
     return Q, K, V
+
+
+def planted_recall(w, api, Q, K, V, pairs):
+    """Fraction of planted (query, key) pairs whose query and key land in the
+    same sortLSH bucket, from the library's own sorted orders."""
+    import numpy as np
+    art = api.debug_artifacts(Q, K, V, causal=w.causal, b=w.b, m=w.m, r=w.r,
+                              recursion_base=w.recursion_base, seed=w.method_seed)
+    perm_q = art["PERM_Q"].reshape(w.heads, w.n)
+    perm_k = art["PERM_K"].reshape(w.heads, w.n)
+    be = min(w.b, w.n)
+    hits = tot = 0
+    for h in range(w.heads):
+        bq = np.empty(w.n, dtype=np.int64)
+        bq[perm_q[h]] = np.arange(w.n) // be
+        bk = np.empty(w.n, dtype=np.int64)
+        bk[perm_k[h]] = np.arange(w.n) // be
+        p = pairs[h]
+        hits += int((bq[p[:, 0]] == bk[p[:, 1]]).sum())
+        tot += len(p)
+    return {"recall": hits / tot, "pairs": tot,
+            "meaning": "planted pairs whose query and key share a sortLSH bucket"}
 
 
 def cpu_baseline(w):
@@ -182,7 +267,43 @@ def cpu_baseline(w):
             "kind": "oracle",
             "sample": f"1 of {w.heads} heads of the same workload (full n={w.n} "
                       f"forward, fp64 numpy), {dt:.1f} s, scaled x{w.heads}",
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+            "exact_oracle": cpu_baseline_exact(w)}
+
+
+def cpu_baseline_exact(w):
+    """The oracle's exact attention as it stands: the whole workload when its
+    score matrices are small (heads * n^2 <= 2^31), else 256 position-
+    stratified query rows of head 0 scaled by the number of (query, key)
+    pairs of the whole forward ("extrapolated")."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from approximate_softmax_attention_amd import workloads as wl
+    from oracle import exact as oexact
+    pairs_total = w.heads * (w.n * (w.n + 1) / 2 if w.causal else float(w.n) * w.n)
+    if w.heads * w.n * w.n <= (1 << 31):
+        Q, K, V, _ = wl.make_inputs(w)
+        t0 = time.perf_counter()
+        for h in range(w.heads):
+            oexact.exact_attention(Q[h], K[h], V[h], causal=w.causal)
+        dt = time.perf_counter() - t0
+        full, sample = dt, f"the whole workload ({w.heads} heads), {dt:.1f} s"
+    else:
+        q, k, v, _ = wl.make_head(w, 0)
+        edges = np.linspace(0, w.n, 257).astype(np.int64)
+        rs = np.random.default_rng(0)
+        rows = np.array([rs.integers(lo, hi) for lo, hi in zip(edges[:-1], edges[1:])])
+        t0 = time.perf_counter()
+        oexact.exact_attention_rows(q, k, v, rows, causal=w.causal)
+        dt = time.perf_counter() - t0
+        pairs = float((rows + 1).sum()) if w.causal else float(len(rows)) * w.n
+        full = dt * pairs_total / pairs
+        sample = (f"256 position-stratified rows of head 0, {dt:.1f} s, extrapolated by "
+                  f"(query, key) pairs to all {w.heads} heads")
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": w.n / full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "extrapolated": w.heads * w.n * w.n > (1 << 31)}
 
 
 def sweep(args, torch, api):
@@ -517,7 +638,8 @@ def main():
 
     w = wl.WORKLOADS[args.workload or wl.HEADLINE]
     log(f"workload {w.name}: generating inputs")
-    Q, K, V = make_device_inputs(w, torch)
+    pairs = [] if w.planted and not w.causal else None
+    Q, K, V = make_device_inputs(w, torch, pairs)
     dtc = HA_BF16 if w.dtype == "bf16" else HA_F32
     nb = api.workspace_bytes(w.n, w.d, w.heads, causal=w.causal, b=w.b, m=w.m, r=w.r,
                              recursion_base=w.recursion_base, dtype=dtc)
@@ -570,12 +692,25 @@ def main():
             counted = profiled_traffic(w.name, name)
             if counted is not None:
                 kernels[name]["counter_gbs"] = counted / t / 1e9
+    abytes = attention_bytes(w)
+    for name, nbytes in abytes.items():
+        if name in kernels:
+            kernels[name]["bytes"] = nbytes
+            kernels[name]["alg_gbs"] = nbytes / (kernels[name]["avg_ms"] / 1e3) / 1e9
     if dom in flops:
-        ach = flops[dom] / (kernels[dom]["avg_ms"] / 1e3)
-        roofline = {"bound": "mfma", "achieved": ach / 1e12, "peak": peak / 1e12,
-                    "unit": "TFLOP/s", "frac": ach / peak,
-                    "traffic": profiled_traffic(w.name, dom),
-                    "kernel": dom, "flops_per_launch": flops[dom]}
+        t = kernels[dom]["avg_ms"] / 1e3
+        # the bound is whichever floor is longer at the published peaks
+        mfma_floor, hbm_floor = flops[dom] / peak, abytes.get(dom, 0) / PEAK_HBM
+        if mfma_floor >= hbm_floor:
+            roofline = {"bound": "mfma", "achieved": flops[dom] / t / 1e12, "peak": peak / 1e12,
+                        "unit": "TFLOP/s", "frac": flops[dom] / t / peak}
+        else:
+            roofline = {"bound": "hbm", "achieved": abytes[dom] / t / 1e9,
+                        "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                        "frac": abytes[dom] / t / PEAK_HBM}
+        roofline.update({"traffic": profiled_traffic(w.name, dom), "kernel": dom,
+                         "flops_per_launch": flops[dom], "bytes_per_launch": abytes.get(dom),
+                         "mfma_floor_ms": mfma_floor * 1e3, "hbm_floor_ms": hbm_floor * 1e3})
         counters = profiled_mfma(w.name, dom)
         if counters is not None:
             roofline["mfma_busy"], roofline["clock_ghz"] = counters
@@ -584,16 +719,25 @@ def main():
                     "frac": None, "traffic": None, "kernel": dom}
     total_flops = sum(flops.values())
 
+    # whole forward: the longer of its MFMA floor and its HBM floor (all
+    # kernels' algorithmic bytes) against the measured step
+    fwd_bytes = sum(hbm_bytes(w).values()) + sum(abytes.values())
+    floors = {"mfma": sum(flops.values()) / peak * 1e3, "hbm": fwd_bytes / PEAK_HBM * 1e3}
+    fbound = max(floors, key=floors.get)
+    whole = {"bound": fbound, "floor_ms": floors[fbound], "frac": floors[fbound] / ms,
+             "mfma_floor_ms": floors["mfma"], "hbm_floor_ms": floors["hbm"],
+             "alg_bytes": fwd_bytes}
     result = {
-        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+        "metric": metric_for(w), "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "ms_per_step_median": per_step[len(per_step) // 2], "ms_per_step_min": per_step[0],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": w.dtype, "data": "synthetic (seeded iid N(0,1), RoPE on Q,K)",
+        "dtype": w.dtype, "data": data_for(w),
         "config": {"workload": w.name, "batch": 1, "heads": w.heads, "seq_len": w.n,
                    "head_dim": w.d, "causal": w.causal, "b": w.b, "m": w.m, "r": w.r,
                    "recursion_base": w.recursion_base, "parallelism": "single-gpu"},
         "mfma_frac_whole_forward": total_flops / (ms / 1e3) / peak,
+        "whole_forward": whole,
         "roofline": roofline,
         "kernels": kernels,
     }
@@ -617,7 +761,15 @@ def main():
             "mfma_frac": exact_flops(w) / (ems / 1e3) / peak,
             "speedup_of_hyperattention": ems / ms,
             "rel_frobenius_err_vs_exact": float(diff)}
+        if not w.causal and not w.planted:
+            # iid N(0, 1) inputs: the sampled part's noise against the exact
+            # output predicts a relative error of about sqrt(n_k / m)
+            result["exact_baseline"]["predicted_rel_err"] = (w.n / min(w.m, w.n)) ** 0.5
         del Oe
+
+    if pairs is not None:
+        log("planted recall from the library's sorted orders")
+        result["planted"] = planted_recall(w, api, Q, K, V, pairs)
 
     if args.copy_calibration:
         copy_calibration(torch)

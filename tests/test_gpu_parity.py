@@ -133,6 +133,26 @@ def test_hash_bf16_cancelling_rows_use_exact_sign():
     assert np.array_equal(codes[0].cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp32", 128), ("fp32", 64)])
+def test_hash_rows_at_the_certainty_margin(dtype, d):
+    """Rows whose projection on one hyperplane sits at 0.5, 1, 2 and 10 times
+    the kernel's certainty margin (3 gamma_d sum |x_t g_t| on the bf16 MFMA
+    path, 4 gamma_d |x| |g| on the fp32 path), both signs, every hyperplane:
+    codes bit-exact against the fp64 sequential definition, whichever side
+    of the margin the fp32 value falls."""
+    banner(f"hash at the certainty margin {dtype} d={d}")
+    from tests.margin_rows import margin_set
+    G, X, info = margin_set(21, d, dtype)
+    api = _api()
+    codes = api.sortlsh_hash(to_dev(X[None].astype(np.float32), dtype), r=8, seed=21)
+    _sync()
+    ref = osl.hash_codes(X, G)
+    got = codes[0].cpu().numpy()
+    bad = np.nonzero(got != ref)[0]
+    assert len(bad) == 0, [(int(i), info[i].tolist()) for i in bad[:8]]
+    print(f"{len(X)} rows at 0.5/1/2/10 x the margin: codes bit-exact", flush=True)
+
+
 # ------------------------------------------------- forward: integer artefacts
 
 def _check_artifacts(w, Q, K, V, ws, layout, art):

@@ -195,3 +195,18 @@ def test_zero_hyperplanes_give_the_local_block_mask():
     idx = np.arange(96)
     assert np.array_equal(s["bucket_q"], idx // 32)
     assert np.array_equal(s["bucket_k"], idx // 32)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp32", 128)])
+def test_margin_rows_sit_where_asked(dtype, d):
+    """The rows the GPU threshold test hashes: each projection on its chosen
+    hyperplane is within 20% of c times the kernel's certainty margin, with
+    the chosen sign, for c = 0.5, 1, 2, 10 (so both sides of the decision
+    are exercised), and the oracle's bit follows that sign."""
+    from tests.margin_rows import margin_set
+    G, X, info = margin_set(21, d, dtype)
+    assert len(X) >= 8 * 4 * 2 * 12
+    k, c, ratio = info[:, 0].astype(int), info[:, 1], info[:, 2]
+    assert np.all((np.abs(ratio) > 0.8 * c) & (np.abs(ratio) < 1.25 * c))
+    bits = sortlsh.sign_bits(sortlsh.projections_sequential(X, G))
+    assert np.array_equal((bits >> k) & 1, (ratio > 0).astype(int))
