@@ -63,7 +63,6 @@ struct Level {
   int64_t nbucket;    // h / b_eff
   int64_t sort_cps;   // sort chunks per segment
   int64_t sort_wg0;   // first sort chunk work-group of this level
-  int64_t seg_wg0;    // first per-segment work-group of this level
   int64_t att_wg0;    // first attention work-group of this level
   int64_t att_qch;    // query chunks per bucket
   // Sample lists of every sub-problem at this level: the uniform list holds
@@ -99,7 +98,6 @@ struct Plan {
   int64_t base_block = 0;     // causal diagonal block size n >> L
   int64_t vblocks = 0;        // V-norm blocks per head
   int64_t sort_wgs = 0;       // sort chunk work-groups (all levels/heads/sides)
-  int64_t seg_wgs = 0;        // per-segment work-groups (all levels/heads/sides)
   int64_t att_wgs = 0;        // bucket attention work-groups
   bool backward = false;      // workspace of the backward pass
   int64_t smp_wgs = 0;        // sample-slot gradient items (backward)

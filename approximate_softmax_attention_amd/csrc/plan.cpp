@@ -89,8 +89,6 @@ int make_plan(Plan& p, int64_t n, int d, int heads, int causal, int b, int m,
     v.sort_cps = ceil_div(v.h, kSortChunk);
     v.sort_wg0 = p.sort_wgs;
     p.sort_wgs += int64_t(heads) * 2 * v.nseg * v.sort_cps;
-    v.seg_wg0 = p.seg_wgs;
-    p.seg_wgs += int64_t(heads) * 2 * v.nseg;
     v.att_qch = ceil_div(v.b_eff, kAttnQ);
     const bool exhaustive = int64_t(m) >= v.h;
     v.u_cnt = exhaustive ? static_cast<int>(v.h) : m;
@@ -119,7 +117,6 @@ int make_plan(Plan& p, int64_t n, int d, int heads, int causal, int b, int m,
   add_region(p, HA_WS_PERM_K, slots * 4);
   add_region(p, HA_WS_RANK_K, slots * 4);
   add_region(p, HA_WS_SORT_HIST, p.sort_wgs * kSortBins * 4);
-  add_region(p, HA_WS_SORT_OFFS, p.sort_wgs * kSortBins * 4);
   const int64_t samples = H * p.nodes * m;
   add_region(p, HA_WS_U_IDX, samples * 4);
   add_region(p, HA_WS_U_BKT, samples * 4);

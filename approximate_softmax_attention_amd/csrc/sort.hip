@@ -4,14 +4,17 @@
 // Every (level, head, side, sub-problem) segment is sorted stably by
 // (code, index) with a counting sort over the 2^r <= 256 code values. All
 // segments of all levels are independent once the codes exist, so each of
-// the three passes covers every segment in one launch:
+// the two passes covers every segment in one launch:
 //   1. per chunk of 2048 elements: a 256-bin histogram (LDS counters);
-//   2. per segment: exclusive offsets, bin-major then chunk-minor;
-//   3. per chunk: stable ranks (wave ballots find the earlier lanes with the
+//   2. per chunk: its exclusive offsets (bin-major over the segment, then
+//      chunk-minor), summed from the segment's chunk histograms by one thread
+//      per bin; stable ranks (wave ballots find the earlier lanes with the
 //      same code, per-wave LDS counts carry the order across batches and
-//      waves), then perm (sorted position -> row) written in sorted order
+//      waves); then perm (sorted position -> row) written in sorted order
 //      from an LDS copy of the chunk, and rank (slot -> sorted position, keys
 //      only).
+// The chunks of one segment run on one XCD (chunk_of), so the short runs
+// that neighbouring chunks write into each bin of perm meet in one L2.
 #include "common.h"
 #include "device_util.h"
 
@@ -31,7 +34,6 @@ struct SortArgs {
   int32_t* perm[2];             // [L][heads][S] per side
   int32_t* rank;                // [L][heads][S] for side 1, or null
   uint32_t* hist;               // [chunks][256]
-  uint32_t* offs;               // [chunks][256]
 };
 
 struct ChunkRef {
@@ -39,20 +41,29 @@ struct ChunkRef {
   int64_t seg, chunk, h;
 };
 
-__device__ __forceinline__ int find_level(const LevelTable& t, int64_t w, int which) {
+__device__ __forceinline__ int find_level(const LevelTable& t, int64_t w) {
   int lv = 0;
-  for (int l = 1; l < t.count; ++l) {
-    const int64_t s = which == 0 ? t.lv[l].sort_wg0 : t.lv[l].seg_wg0;
-    if (w >= s) lv = l;
-  }
+  for (int l = 1; l < t.count; ++l)
+    if (w >= t.lv[l].sort_wg0) lv = l;
   return lv;
+}
+
+// Chunk processed by work-group x of a grid of n: work-groups are dealt to
+// the 8 XCDs round-robin, so XCD j is given the j-th eighth of the chunks,
+// in order, and a segment's chunks share one L2.
+__device__ __forceinline__ int64_t chunk_of(int64_t x, int64_t n) {
+  constexpr int64_t kXcd = 8;
+  const int64_t per = n / kXcd, rem = n % kXcd;
+  const int64_t xcd = x % kXcd, k = x / kXcd;
+  // XCD j takes per (+1 for j < rem) consecutive chunks
+  return xcd * per + (xcd < rem ? xcd : rem) + k;
 }
 
 // Work-group counts fit in 32 bits, and 32-bit division is far cheaper than
 // 64-bit.
 __device__ __forceinline__ ChunkRef decode_chunk(const SortArgs& a, int64_t w) {
   ChunkRef c;
-  c.lv = find_level(a.table, w, 0);
+  c.lv = find_level(a.table, w);
   const Level& L = a.table.lv[c.lv];
   uint32_t rem = uint32_t(w - L.sort_wg0);
   const uint32_t cps = uint32_t(L.sort_cps), nseg = uint32_t(L.nseg);
@@ -104,43 +115,6 @@ __global__ __launch_bounds__(kThreads) void sort_hist_kernel(SortArgs a) {
   a.hist[w * kSortBins + threadIdx.x] = hist[threadIdx.x];
 }
 
-__global__ __launch_bounds__(kThreads) void sort_offsets_kernel(SortArgs a) {
-  __shared__ uint32_t wtot[kThreads / 64];
-  const int64_t w = blockIdx.x;
-  const int lv = find_level(a.table, w, 1);
-  const Level& L = a.table.lv[lv];
-  uint32_t rem = uint32_t(w - L.seg_wg0);
-  const uint32_t nseg = uint32_t(L.nseg), sides = uint32_t(a.sides);
-  uint32_t q = rem / nseg;
-  const int64_t seg = rem - q * nseg;
-  rem = q;
-  q = rem / sides;
-  const int side = int(rem - q * sides);
-  const int head = int(q);
-  const int64_t cw0 = L.sort_wg0 + ((int64_t(head) * a.sides + side) * L.nseg + seg) * L.sort_cps;
-  const int bin = threadIdx.x;
-  const int cps = int(L.sort_cps);
-  const uint32_t* __restrict__ hist = a.hist + cw0 * kSortBins + bin;
-  uint32_t* __restrict__ offs = a.offs + cw0 * kSortBins + bin;
-  // this bin's total over the segment's chunks
-  uint32_t total = 0;
-  for (int c = 0; c < cps; ++c) total += hist[c * kSortBins];
-  // exclusive scan of the per-bin totals across the block
-  uint64_t incl = wave_incl_scan(uint64_t(total));
-  const int wave = threadIdx.x >> 6;
-  if (lane_id() == 63) wtot[wave] = uint32_t(incl);
-  __syncthreads();
-  uint32_t before = 0;
-  for (int i = 0; i < wave; ++i) before += wtot[i];
-  uint32_t running = before + uint32_t(incl) - total;
-  // bin-major, then chunk-minor offsets
-  for (int c = 0; c < cps; ++c) {
-    const uint32_t v = hist[c * kSortBins];
-    offs[c * kSortBins] = running;
-    running += v;
-  }
-}
-
 // Wave wv owns the chunk's elements [wv * kWaveSpan, (wv + 1) * kWaveSpan)
 // (kPer batches of 64), so stable ranks need no barrier inside the wave: a
 // batch's equal codes are found by ballots and the wave's running count per
@@ -157,12 +131,31 @@ __global__ __launch_bounds__(kThreads) void sort_scatter_kernel(SortArgs a) {
   __shared__ uint32_t wtot[kWaves];
   __shared__ int32_t srow[kSortChunk];
   __shared__ uint32_t spos[kSortChunk];
-  const int64_t w = blockIdx.x;
+  const int64_t w = chunk_of(blockIdx.x, gridDim.x);
   const ChunkRef c = decode_chunk(a, w);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = lane_id();
-  base[tid] = a.offs[w * kSortBins + tid];
+  {
+    // This chunk's first position per bin: the lower bins over the whole
+    // segment, plus this bin's count in the segment's earlier chunks (the
+    // chunks of a segment are consecutive, the first at w - chunk).
+    const int64_t cps = a.table.lv[c.lv].sort_cps;
+    const uint32_t* __restrict__ h = a.hist + (w - c.chunk) * kSortBins + tid;
+    uint32_t total = 0, before = 0;
+#pragma unroll 8
+    for (int64_t k = 0; k < cps; ++k) {
+      const uint32_t v = h[k * kSortBins];
+      total += v;
+      before += k < c.chunk ? v : 0u;
+    }
+    const uint32_t incl = uint32_t(wave_incl_scan(uint64_t(total)));
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    uint32_t below = 0;
+    for (int i = 0; i < wave; ++i) below += wtot[i];
+    base[tid] = below + incl - total + before;
+  }
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) wcnt[i][tid] = 0;
   const uint8_t* codes = a.codes[c.side] + int64_t(c.head) * a.n;
@@ -239,31 +232,23 @@ __global__ __launch_bounds__(kThreads) void sort_scatter_kernel(SortArgs a) {
   for (int j = tid; j < nv; j += kThreads) perm[spos[j]] = srow[j];
 }
 
-// Recompute the work-group offsets of the table for the given side count.
-int64_t retable(LevelTable& t, int heads, int sides, int64_t* seg_total) {
-  int64_t chunks = 0, segs = 0;
+// Recompute the chunk offsets of the table for the given side count.
+int64_t retable(LevelTable& t, int heads, int sides) {
+  int64_t chunks = 0;
   for (int l = 0; l < t.count; ++l) {
     Level& v = t.lv[l];
     v.sort_wg0 = chunks;
     chunks += int64_t(heads) * sides * v.nseg * v.sort_cps;
-    v.seg_wg0 = segs;
-    segs += int64_t(heads) * sides * v.nseg;
   }
-  *seg_total = segs;
   return chunks;
 }
 
-int run_sort(SortArgs& a, int64_t chunks, int64_t segs, hipStream_t s) {
+int run_sort(SortArgs& a, int64_t chunks, hipStream_t s) {
   if (chunks == 0) return HA_OK;
   {
     ProfRange pr("sort_hist", s);
     hipLaunchKernelGGL(sort_hist_kernel, dim3(unsigned(chunks)), dim3(kThreads), 0, s, a);
     HA_LAUNCH_CHECK("sort_hist");
-  }
-  {
-    ProfRange pr("sort_offsets", s);
-    hipLaunchKernelGGL(sort_offsets_kernel, dim3(unsigned(segs)), dim3(kThreads), 0, s, a);
-    HA_LAUNCH_CHECK("sort_offsets");
   }
   {
     ProfRange pr("sort_scatter", s);
@@ -289,15 +274,12 @@ int launch_sort(const Plan& p, void* ws, int sides, hipStream_t s) {
   a.perm[1] = reinterpret_cast<int32_t*>(w + p.off[HA_WS_PERM_K]);
   a.rank = reinterpret_cast<int32_t*>(w + p.off[HA_WS_RANK_K]);
   a.hist = reinterpret_cast<uint32_t*>(w + p.off[HA_WS_SORT_HIST]);
-  a.offs = reinterpret_cast<uint32_t*>(w + p.off[HA_WS_SORT_OFFS]);
-  int64_t segs = 0;
-  const int64_t chunks = retable(a.table, p.heads, sides, &segs);
-  return run_sort(a, chunks, segs, s);
+  return run_sort(a, retable(a.table, p.heads, sides), s);
 }
 
 size_t sort_single_scratch_bytes(int64_t n, int heads) {
   const int64_t chunks = int64_t(heads) * ceil_div(n, kSortChunk);
-  return size_t(2 * align256(chunks * kSortBins * 4));
+  return size_t(align256(chunks * kSortBins * 4));
 }
 
 int launch_sort_single(const uint8_t* codes, int64_t n, int heads, int32_t* perm,
@@ -323,11 +305,7 @@ int launch_sort_single(const uint8_t* codes, int64_t n, int heads, int32_t* perm
   a.rank = nullptr;
   const int64_t chunks = int64_t(heads) * v.sort_cps;
   a.hist = static_cast<uint32_t*>(scratch);
-  a.offs = reinterpret_cast<uint32_t*>(static_cast<char*>(scratch) +
-                                       align256(chunks * kSortBins * 4));
-  int64_t segs = 0;
-  const int64_t c2 = retable(a.table, heads, 1, &segs);
-  return run_sort(a, c2, segs, s);
+  return run_sort(a, retable(a.table, heads, 1), s);
 }
 
 }  // namespace ha

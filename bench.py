@@ -522,8 +522,7 @@ def backward_mode(args, torch, api, wl):
     bwd_ms = sum(v["avg_ms"] for k, v in kernels.items() if k.startswith("bwd_")) + sum(
         kernels.get(k, {}).get("avg_ms", 0.0) for k in ("hash", "vnorm_rows", "vnorm_weights",
                                                           "vnorm_prefix", "sort_hist",
-                                                          "sort_offsets", "sort_scatter",
-                                                          "samples")) / 2
+                                                          "sort_scatter", "samples")) / 2
     kfl = backward_kernel_flops(w)
     dom = max((k for k in kfl if k in kernels), key=lambda k: kernels[k]["avg_ms"])
     achieved = kfl[dom] / (kernels[dom]["avg_ms"] / 1e3)

@@ -374,7 +374,7 @@ enum ha_ws_region {
   HA_WS_CODES_Q = 0, HA_WS_CODES_K,
   HA_WS_VNORM_A, HA_WS_VNORM_W, HA_WS_VNORM_P, HA_WS_VNORM_BLK,
   HA_WS_PERM_Q, HA_WS_PERM_K, HA_WS_RANK_K,
-  HA_WS_SORT_HIST, HA_WS_SORT_OFFS,
+  HA_WS_SORT_HIST,
   HA_WS_U_IDX, HA_WS_U_BKT, HA_WS_V_IDX, HA_WS_V_BKT, HA_WS_V_W,
   HA_WS_NODE_META,
   HA_WS_PART_O, HA_WS_PART_LSE,
