@@ -102,11 +102,13 @@ def profiled_traffic(workload, kernel, backward=False):
     return val
 
 
-def profiled_mfma(workload, kernel):
+def profiled_mfma(workload, kernel, backward=False):
     """(MFMA-busy fraction, clock in GHz) of `kernel` from the committed
-    rocprofv3 MFMA counter summary, or None when there is none or the kernel
+    rocprofv3 MFMA counter summary (the forward pass's, or with backward=True
+    the forward + backward call's), or None when there is none or the kernel
     sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"hyperattn_{workload}_mfma_counters.md")
+    name = "backward_mfma_counters" if backward else "mfma_counters"
+    path = os.path.join(ROOT, "profiles", f"hyperattn_{workload}_{name}.md")
     if not os.path.exists(path):
         return None
     sha, busy, clock = None, None, None
@@ -119,7 +121,7 @@ def profiled_mfma(workload, kernel):
                 busy = float(line.split(":", 1)[1])
             elif line.startswith(f"clock-ghz {kernel}:"):
                 clock = float(line.split(":", 1)[1])
-    if sha is None or sha != kernel_source_hash(backward=True) or busy is None:
+    if sha is None or sha != kernel_source_hash(backward) or busy is None:
         return None
     return busy, clock
 
@@ -539,7 +541,7 @@ def backward_mode(args, torch, api, wl):
            "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
                         "unit": "TFLOP/s", "frac": achieved / PEAK_BF16, "traffic": traffic,
                         "kernel": dom, "flops_per_launch": kfl[dom]}}
-    counters = profiled_mfma(w.name, dom)
+    counters = profiled_mfma(w.name, dom, backward=True)
     if counters is not None:
         rec["roofline"]["mfma_busy"], rec["roofline"]["clock_ghz"] = counters
     if not args.no_exact:
