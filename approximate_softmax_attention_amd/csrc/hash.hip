@@ -152,9 +152,14 @@ __device__ void hash_rows(const T* __restrict__ X, const float* __restrict__ Gh,
 // bf16 rows: the projections X G^T are a small contraction (d x 8), done on
 // v_mfma_f32_16x16x32_bf16. Every hyperplane entry is a bf16 value, so each
 // product is exact in fp32; a second MFMA over |X| |G|^T yields
-// S_k = sum_t |x_t g_kt| (all terms positive). If each accumulation step errs
-// by at most 2u (twice IEEE fp32 rounding), |p32 - p| <= 2 gamma_d S_k and the
-// computed S_k is within a factor (1 - 2 gamma_d) of the true one, so
+// S_k = sum_t |x_t g_kt| (all terms positive). The unit's internal rounding
+// is not specified by the ISA, so the margin is chosen to hold under either
+// of two models: (A) every internal addition faithfully rounded (relative
+// error < 2u) in any order, giving |p32 - p| <= 2 gamma_d S_k; (B) each
+// instruction aligning its 33 addends to the largest, keeping >= 23 fraction
+// bits, truncating, adding exactly and rounding once, giving
+// |p32 - p| < 68 u (d/32) S_k ~ 2.13 gamma_d S_k. In both the computed S_k is
+// within a factor (1 - 2.13 gamma_d) of the true one, so
 // |p32| > 3 gamma_d S_k + 2^-100 fixes the sign of p and of its fp64
 // sequential sum. Rows with an uncertain bit recompute it in fp64 in order t.
 // Each wave takes 16 rows per step: A = 16 rows x 32 elements (lane l: row
