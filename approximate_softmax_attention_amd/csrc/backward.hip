@@ -451,12 +451,12 @@ struct Offs16 {
     const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int st = 0; st < D / 32; ++st)
-      rd[st] = uint32_t(r16 * B::CPR + ((4 * st + g) ^ B::swz(r16))) * 16u;
+      rd[st] = uint32_t(r16 * B::CPR + ((4 * st + g) ^ B::swz_t(r16))) * 16u;
     const int row = 4 * g + (r16 >> 2);
 #pragma unroll
     for (int mb = 0; mb < D / 16; ++mb) {
       const int d = 16 * mb + 4 * (r16 & 3);
-      tr[mb] = uint32_t(row * B::CPR + ((d >> 3) ^ B::swz(row))) * 16u + uint32_t(d & 7) * 2u;
+      tr[mb] = uint32_t(row * B::CPR + ((d >> 3) ^ B::swz_t(row))) * 16u + uint32_t(d & 7) * 2u;
     }
   }
 };
@@ -1152,8 +1152,9 @@ __device__ __forceinline__ void kv16_exact_sweep(const BwdArgs& a, BwdSmem<D>& s
     const int64_t r0 = q_lo + int64_t(t) * KT;
     const int nv = int(b_hi - r0 < KT ? b_hi - r0 : KT);
     BwdBuf<D>& b = sm.buf[t & 1];
-    pipe.issue(b.t, Qr, dOr, true, [&](int row) { return row < nv ? int(r0 + row) : -1; },
-               [&](int row) { return row < nv ? lse[r0 + row] * kLog2e : INFINITY; });
+    pipe.template issue<true>(b.t, Qr, dOr, true,
+                              [&](int row) { return row < nv ? int(r0 + row) : -1; },
+                              [&](int row) { return row < nv ? lse[r0 + row] * kLog2e : INFINITY; });
     if (threadIdx.x < KT) b.w2[threadIdx.x] = int(threadIdx.x) < nv ? dl[r0 + threadIdx.x] : 0.f;
   };
   issue(0);
@@ -1231,8 +1232,9 @@ __device__ __forceinline__ void kv16_sorted_loop(const BwdArgs& a, BwdSmem<D>& s
   auto issue = [&](int t) {
     const int e0 = (t % kWin) * KT;
     BwdBuf<D>& b = sm.buf[t & 1];
-    pipe.issue(b.t, Qr, dOr, true, [&](int row) { return int(sm.srow[e0 + row]); },
-               [&](int row) { return sm.sw[e0 + row]; });
+    pipe.template issue<true>(b.t, Qr, dOr, true,
+                              [&](int row) { return int(sm.srow[e0 + row]); },
+                              [&](int row) { return sm.sw[e0 + row]; });
     if (threadIdx.x < KT) b.w2[threadIdx.x] = sm.sw2[e0 + threadIdx.x];
   };
   fill_queries(a, sm, perm, p0, count, head);
@@ -1328,8 +1330,9 @@ __device__ __forceinline__ void kv16_bucket_item(const BwdArgs& a, BwdSmem<D>& s
   for (int t = 0; t < ntiles; ++t) {
     BwdBuf<D>& b = sm.buf[t];
     const int e0 = t * KT;
-    pipe.issue(b.t, Qr, dOr, true, [&](int row) { return int(sm.srow[e0 + row]); },
-               [&](int row) { return sm.sw[e0 + row]; });
+    pipe.template issue<true>(b.t, Qr, dOr, true,
+                              [&](int row) { return int(sm.srow[e0 + row]); },
+                              [&](int row) { return sm.sw[e0 + row]; });
     if (threadIdx.x < KT) b.w2[threadIdx.x] = sm.sw2[e0 + threadIdx.x];
   }
   Offs16<D> o;

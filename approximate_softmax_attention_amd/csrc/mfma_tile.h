@@ -62,6 +62,15 @@ struct alignas(16) Buf<bf16_t, D> {
     const int u = (row >> 1) & 7;
     return ((u & 1) << 2) | (((u >> 2) & 1) << 1) | ((u >> 1) & 1);
   }
+  // Tiles read by 16x16 transposing reads (the backward pass's key-major
+  // kernels, d = 128): the same bijection with the row quarter bit-reversed
+  // in the low bits, so that in any 8 aligned rows swz_t >> 1 is distinct as
+  // well. A half-wave reads 8 rows x two adjacent chunks there, and under
+  // swz rows r and r + 4 share one chunk pair (a 2-way bank conflict).
+  __device__ static int swz_t(int row) {
+    if (D == 128) return ((row & 3) << 2) | ((row >> 3) & 1) | (((row >> 2) & 1) << 1);
+    return swz(row);
+  }
   bf16_t k[KT * D];
   bf16_t v[KT * D];
   float w[KT];                                         // per-slot weight
@@ -125,13 +134,14 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t x, int64_t n) {
 // Pipe<T, D>::issue(buf, ...) starts loading one key tile; commit(buf) makes
 // it complete in LDS (before the barrier that publishes it). RowFn maps a tile
 // row to a key row of the head (-1: masked, zero-filled); WFn gives the
-// slot's weight.
+// slot's weight. bf16 tiles are laid out with Buf::swz, or with Buf::swz_t
+// when issued as issue<true> (tiles read by 16x16 transposing reads).
 template <typename T, int D> struct Pipe;
 
 template <int D>
 struct Pipe<bf16_t, D> {
   using B = Buf<bf16_t, D>;
-  template <typename RowFn, typename WFn>
+  template <bool kTr = false, typename RowFn, typename WFn>
   __device__ __forceinline__ void issue(B& b, __amdgpu_buffer_rsrc_t Kr, __amdgpu_buffer_rsrc_t Vr,
                                         bool with_v, const RowFn& rowidx, const WFn& weight) {
     constexpr int PER = B::KT * B::CPR / kThreads;
@@ -143,7 +153,7 @@ struct Pipe<bf16_t, D> {
       const int p0 = i * kThreads + wave * 64;           // wave-uniform chunk index
       const int p = p0 + lane;
       const int row = p / B::CPR;
-      const int c = (p % B::CPR) ^ B::swz(row);          // global chunk landing here
+      const int c = (p % B::CPR) ^ (kTr ? B::swz_t(row) : B::swz(row));   // chunk landing here
       const int r = rowidx(row);
       const uint32_t off = r >= 0 ? uint32_t(r) * RB + uint32_t(c) * 16u : kOob;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(Kr, (lds_void_t*)(b.k + p0 * 8), 16, off, 0, 0, 0);
