@@ -413,9 +413,14 @@ __device__ __forceinline__ void kv_tile(const BwdBuf<D>& b, const LaneOffs<bf16_
 // computes both gradients (the 32-key layout would need 192 and two sweeps).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// The k index of step st runs over 16-byte chunks st + 4(l/16) of the row
+// (elements 8st + 32(l/16) .. +7), in both operands of S and dP: then the
+// 16 lanes of each quarter read one chunk column of 16 rows and the next
+// quarter the chunk 4 further, which the LDS serves without bank conflicts
+// (chunks 4st + l/16 put every row's two chunks into one conflicting pair).
 template <int D>
 struct Frag16 {
-  bf16x8_t v[D / 32];   // v[st]: row elements 32st + 8(l/16) .. +7
+  bf16x8_t v[D / 32];   // v[st]: row elements 8st + 32(l/16) .. +7
 };
 
 template <int D>
@@ -429,12 +434,12 @@ __device__ __forceinline__ void load_frag16(Frag16<D>& f, __amdgpu_buffer_rsrc_t
   const uint32_t base = row >= 0 ? uint32_t(row) * (D * 2u) : kOob;
 #pragma unroll
   for (int st = 0; st < D / 32; ++st)
-    f.v[st] = __builtin_bit_cast(bf16x8_t, buf_load16(r, base + (32 * st + 8 * g) * 2));
+    f.v[st] = __builtin_bit_cast(bf16x8_t, buf_load16(r, base + (8 * st + 32 * g) * 2));
 }
 
 // Per-lane LDS byte offsets within one bf16 tile (Buf<bf16_t, D> layout):
 //   rd[st]: A operand of S / dP, row l % 16 of a 16-row sub-block, chunk
-//           4st + l/16 (a sub-block 16 rows further adds 16 rows: the
+//           st + 4(l/16) (a sub-block 16 rows further adds 16 rows: the
 //           swizzle repeats every 16 rows);
 //   tr[mb]: transposing read of rows 4(l/16) + (l%16)/4 (then 16 rows
 //           further), columns 16mb + 4(l % 4): lane l receives column
@@ -451,7 +456,7 @@ struct Offs16 {
     const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int st = 0; st < D / 32; ++st)
-      rd[st] = uint32_t(r16 * B::CPR + ((4 * st + g) ^ B::swz_t(r16))) * 16u;
+      rd[st] = uint32_t(r16 * B::CPR + ((st + 4 * g) ^ B::swz_t(r16))) * 16u;
     const int row = 4 * g + (r16 >> 2);
 #pragma unroll
     for (int mb = 0; mb < D / 16; ++mb) {
