@@ -1271,27 +1271,44 @@ __device__ __forceinline__ void kv16_sorted_loop(const BwdArgs& a, BwdSmem<D>& s
   }
 }
 
-template <int D>
-__device__ __forceinline__ void finish_bucket_key16(const BwdArgs& a, const BucketItem& it,
-                                                    Acc16<D>& acc, bool is_k, int64_t krow) {
-  const Level& L = a.table.lv[it.lv];
-  const int64_t h = L.h;
-  if (is_k) scale16<D>(acc, a.scale);
+// Slot of key row krow among this item's level partials.
+__device__ __forceinline__ int64_t bucket_kslot(const BwdArgs& a, const BucketItem& it,
+                                                int64_t krow) {
+  const int64_t h = a.table.lv[it.lv].h;
   const int64_t k_lo = a.table.causal ? 2 * it.seg * h : 0;
-  const int64_t kslot = (int64_t(it.lv) * a.heads + it.head) * a.S + it.seg * h + (krow - k_lo);
+  return (int64_t(it.lv) * a.heads + it.head) * a.S + it.seg * h + (krow - k_lo);
+}
+
+// dK (scaled) and dV of a bucket key: adds the key's sample-slot partials
+// (the slots on its list, first = slot_first of its slot, loaded by the
+// caller ahead of the tile loop) and stores the level partials (causal) or
+// the final rows. One walk of the list serves both gradients; each adds its
+// rows in list order.
+template <int D>
+__device__ __forceinline__ void finish_bucket_keys16(const BwdArgs& a, const BucketItem& it,
+                                                     Acc16<D>& dk, Acc16<D>& dv, int64_t krow,
+                                                     int first) {
+  const Level& L = a.table.lv[it.lv];
+  scale16<D>(dk, a.scale);
+  const int64_t kslot = bucket_kslot(a, it, krow);
   const int64_t nqc = L.smp_nqc;
   const int64_t item0 = L.smp_wg0 + (int64_t(it.head) * L.nseg + it.seg) * L.smp_nsc * nqc;
-  const float* part = is_k ? a.slot_dk : a.slot_dv;
-  for (int t = a.slot_first[kslot]; t >= 0; t = a.slot_next[it.rec * 2 * a.m + t]) {
+  for (int t = first; t >= 0; t = a.slot_next[it.rec * 2 * a.m + t]) {
     const int64_t sc = t / kAttnQ;
     const int tt = t - int(sc) * kAttnQ;
-    for (int64_t qc = 0; qc < nqc; ++qc)
-      add_row16<D>(acc, part + ((item0 + sc * nqc + qc) * kAttnQ + tt) * D);
+    for (int64_t qc = 0; qc < nqc; ++qc) {
+      const int64_t row = ((item0 + sc * nqc + qc) * kAttnQ + tt) * D;
+      add_row16<D>(dk, a.slot_dk + row);
+      add_row16<D>(dv, a.slot_dv + row);
+    }
   }
-  if (a.table.causal)
-    store_row16_f32<D>(acc, (is_k ? a.part_dk : a.part_dv) + kslot * D);
-  else
-    store_row16_bf16<D>(acc, (is_k ? a.dK : a.dV) + (int64_t(it.head) * a.n + krow) * D);
+  if (a.table.causal) {
+    store_row16_f32<D>(dv, a.part_dv + kslot * D);
+    store_row16_f32<D>(dk, a.part_dk + kslot * D);
+  } else {
+    store_row16_bf16<D>(dv, a.dV + (int64_t(it.head) * a.n + krow) * D);
+    store_row16_bf16<D>(dk, a.dK + (int64_t(it.head) * a.n + krow) * D);
+  }
 }
 
 // dK, dV of one bucket item's 256 key slots (two halves of 128, one after the
@@ -1310,6 +1327,7 @@ __device__ __forceinline__ void kv16_bucket_item(const BwdArgs& a, BwdSmem<D>& s
     for (int half = 0; half < 2; ++half) {
       const int64_t ki = kbase + half * kKeys16;
       const int64_t krow = ki < b_eff ? int64_t(a.perm_k[it.slot0 + ki]) : -1;
+      const int first = krow >= 0 ? a.slot_first[bucket_kslot(a, it, krow)] : -1;
       Frag16<D> kf, vf;
       load_frag16<D>(kf, Kr, krow);
       load_frag16<D>(vf, Vr, krow);
@@ -1318,10 +1336,7 @@ __device__ __forceinline__ void kv16_bucket_item(const BwdArgs& a, BwdSmem<D>& s
       zero16<D>(dv);
       kv16_sorted_loop<D, false>(a, sm, a.perm_q, it.slot0, b_eff, b_eff, it.head, kf, vf, dk,
                                  dv, 1.f, 1.f, 0, true);
-      if (krow >= 0) {
-        finish_bucket_key16<D>(a, it, dv, false, krow);
-        finish_bucket_key16<D>(a, it, dk, true, krow);
-      }
+      if (krow >= 0) finish_bucket_keys16<D>(a, it, dk, dv, krow, first);
     }
     return;
   }
@@ -1345,6 +1360,7 @@ __device__ __forceinline__ void kv16_bucket_item(const BwdArgs& a, BwdSmem<D>& s
   for (int half = 0; half < 2; ++half) {
     const int64_t ki = kbase + half * kKeys16;
     const int64_t krow = ki < b_eff ? int64_t(a.perm_k[it.slot0 + ki]) : -1;
+    const int first = krow >= 0 ? a.slot_first[bucket_kslot(a, it, krow)] : -1;
     Frag16<D> kf, vf;
     load_frag16<D>(kf, Kr, krow);
     load_frag16<D>(vf, Vr, krow);
@@ -1360,10 +1376,7 @@ __device__ __forceinline__ void kv16_bucket_item(const BwdArgs& a, BwdSmem<D>& s
       kv_tile16<D, false, false, true>(sm.buf[t], o, kf, vf, dk, dv, a.scale_log2, 1.f, 1.f, 0,
                                        0, true, left < KT ? left : KT, 0, 0);
     }
-    if (krow >= 0) {
-      finish_bucket_key16<D>(a, it, dv, false, krow);
-      finish_bucket_key16<D>(a, it, dk, true, krow);
-    }
+    if (krow >= 0) finish_bucket_keys16<D>(a, it, dk, dv, krow, first);
   }
   __syncthreads();   // the tiles are read until here
 }
