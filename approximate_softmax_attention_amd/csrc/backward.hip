@@ -1357,16 +1357,31 @@ __device__ __forceinline__ void kv16_bucket_item(const BwdArgs& a, BwdSmem<D>& s
   }
   Offs16<D> o;
   o.init();
+  // both halves' key rows and slot-list heads first, then each half's K and
+  // V fragments one half ahead, so that no half waits on a dependent load
+  int64_t krows[2];
+  int firsts[2];
+#pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int64_t ki = kbase + half * kKeys16;
-    const int64_t krow = ki < b_eff ? int64_t(a.perm_k[it.slot0 + ki]) : -1;
-    const int first = krow >= 0 ? a.slot_first[bucket_kslot(a, it, krow)] : -1;
-    Frag16<D> kf, vf;
-    load_frag16<D>(kf, Kr, krow);
-    load_frag16<D>(vf, Vr, krow);
+    krows[half] = ki < b_eff ? int64_t(a.perm_k[it.slot0 + ki]) : -1;
+  }
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+    firsts[half] = krows[half] >= 0 ? a.slot_first[bucket_kslot(a, it, krows[half])] : -1;
+  Frag16<D> kf, vf, kf1, vf1;
+  load_frag16<D>(kf, Kr, krows[0]);
+  load_frag16<D>(vf, Vr, krows[0]);
+  pipe.commit(sm.buf[0].t, true);
+  __syncthreads();
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
     if (half == 0) {
-      pipe.commit(sm.buf[0].t, true);
-      __syncthreads();
+      load_frag16<D>(kf1, Kr, krows[1]);
+      load_frag16<D>(vf1, Vr, krows[1]);
+    } else {
+      kf = kf1;
+      vf = vf1;
     }
     Acc16<D> dk, dv;
     zero16<D>(dk);
@@ -1376,7 +1391,7 @@ __device__ __forceinline__ void kv16_bucket_item(const BwdArgs& a, BwdSmem<D>& s
       kv_tile16<D, false, false, true>(sm.buf[t], o, kf, vf, dk, dv, a.scale_log2, 1.f, 1.f, 0,
                                        0, true, left < KT ? left : KT, 0, 0);
     }
-    if (krow >= 0) finish_bucket_keys16<D>(a, it, dk, dv, krow, first);
+    if (krows[half] >= 0) finish_bucket_keys16<D>(a, it, dk, dv, krows[half], firsts[half]);
   }
   __syncthreads();   // the tiles are read until here
 }
