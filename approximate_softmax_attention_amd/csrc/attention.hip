@@ -86,7 +86,7 @@ struct AttnArgs {
   // EXACT
   int64_t block;           // key/query block size (n for plain exact attention)
   int64_t tiles_per_block; // ceil(block / kAttnQ)
-  uint32_t items_per_head; // blocks per head * tiles_per_block
+  uint32_t items_per_head; // work items per head (exact_item)
   int causal;
   int merge_levels;        // base case: number of levels to merge (0: none)
   const void* part_o;      // [L][heads][S][d]
@@ -380,20 +380,11 @@ __device__ __forceinline__ void stage_row(const WaveState<T, D>& ws, char* st, i
 }
 
 // ------------------------------------------------------------- EXACT kernel
-// Work item lin = head * items_per_head + blk * tiles_per_block + t: query
-// tile t of key block blk. Causal tiles are taken from the longest (last) to
-// the shortest for load balance.
+// Query tile `tile` of key block blk; desc: its key tiles in descending order.
 template <typename T, int D, bool kCausal>
-__device__ __forceinline__ void exact_item(const AttnArgs& a, Smem<T, D>& sm, uint32_t lin) {
+__device__ __forceinline__ void exact_tile(const AttnArgs& a, Smem<T, D>& sm, int head,
+                                           uint32_t blk, int64_t tile, bool desc) {
   constexpr int KT = Buf<T, D>::KT;
-  // 32-bit division: far cheaper than 64-bit, and the counts fit
-  const uint32_t gx = a.items_per_head;
-  const int head = int(lin / gx);
-  const uint32_t bx = lin - uint32_t(head) * gx;
-  const uint32_t tpb = uint32_t(a.tiles_per_block);
-  const uint32_t blk = bx / tpb;
-  const uint32_t tl = bx - blk * tpb;
-  const int64_t tile = kCausal ? int64_t(tpb - 1 - tl) : int64_t(tl);
   const int64_t b_lo = blk * a.block;
   const int64_t b_hi = b_lo + a.block < a.n ? b_lo + a.block : a.n;
   const int64_t q0 = b_lo + tile * kAttnQ;
@@ -419,8 +410,10 @@ __device__ __forceinline__ void exact_item(const AttnArgs& a, Smem<T, D>& sm, ui
   const int64_t k_end = kCausal ? q_end : b_hi;
   const int ntiles = int((k_end - b_lo + KT - 1) / KT);
   Pipe<T, D> pipe;
+  // step t of the loop takes key tile kt(t); its buffer is t & 1
+  auto kt = [&](int t) { return desc ? ntiles - 1 - t : t; };
   auto issue = [&](int t) {
-    const int64_t k0 = b_lo + int64_t(t) * KT;
+    const int64_t k0 = b_lo + int64_t(kt(t)) * KT;
     const int nv = int(k_end - k0 < KT ? k_end - k0 : KT);
     pipe.issue(sm.buf[t & 1], Kr, Vr, true,
                [&](int row) { return row < nv ? int(k0 + row) : -1; },
@@ -431,7 +424,7 @@ __device__ __forceinline__ void exact_item(const AttnArgs& a, Smem<T, D>& sm, ui
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     if (t + 1 < ntiles) issue(t + 1);
-    const int64_t k0 = b_lo + int64_t(t) * KT;
+    const int64_t k0 = b_lo + int64_t(kt(t)) * KT;
     const int nvalid = int(k_end - k0 < KT ? k_end - k0 : KT);
     const bool skip = kCausal && k0 > qw0 + kQW - 1;       // wholly above the diagonal
     if (!skip) {
@@ -513,6 +506,37 @@ __device__ __forceinline__ void exact_item(const AttnArgs& a, Smem<T, D>& sm, ui
     *reinterpret_cast<uint4*>(static_cast<T*>(a.O) + hoff + grow * D + ch * S::E) =
         pack16<T>(acc[k]);
     if (ch == 0 && a.lse) a.lse[int64_t(head) * a.n + grow] = l[k];
+  }
+}
+
+// Work item lin = head * items_per_head + blk * per_block + j. Non-causal:
+// query tile j of key block blk (per_block = tiles_per_block). Causal: the
+// pair of query tiles j and tiles_per_block - 1 - j (per_block =
+// ceil(tiles_per_block / 2)), so every item of a block sees the same number
+// of key tiles; the first takes its key tiles in ascending order, the second
+// in descending order. At any moment the items of one block that started
+// together then read only two of the block's key tiles (tile tau of the
+// first sweeps, tile 2 tiles_per_block + 1 - tau of the second), and the
+// XCD's L2 serves the rest of them.
+template <typename T, int D, bool kCausal>
+__device__ __forceinline__ void exact_item(const AttnArgs& a, Smem<T, D>& sm, uint32_t lin) {
+  // 32-bit division: far cheaper than 64-bit, and the counts fit
+  const uint32_t gx = a.items_per_head;
+  const int head = int(lin / gx);
+  const uint32_t bx = lin - uint32_t(head) * gx;
+  const uint32_t tpb = uint32_t(a.tiles_per_block);
+  if constexpr (kCausal) {
+    const uint32_t ppb = (tpb + 1) / 2;
+    const uint32_t blk = bx / ppb;
+    const uint32_t j = bx - blk * ppb;
+    exact_tile<T, D, kCausal>(a, sm, head, blk, int64_t(j), false);
+    if (tpb - 1 - j != j) {
+      __syncthreads();   // the first tile's epilogue reads the buffers the second loads into
+      exact_tile<T, D, kCausal>(a, sm, head, blk, int64_t(tpb - 1 - j), true);
+    }
+  } else {
+    const uint32_t blk = bx / tpb;
+    exact_tile<T, D, kCausal>(a, sm, head, blk, int64_t(bx - blk * tpb), false);
   }
 }
 
@@ -775,10 +799,12 @@ int launch_exact(const void* Q, const void* K, const void* V, void* O, float* ls
   a.block = block;
   a.tiles_per_block = ceil_div(block, kAttnQ);
   a.causal = causal;
-  const int64_t items = ceil_div(n, block) * a.tiles_per_block * heads;
+  // causal items are pairs of query tiles (exact_item)
+  const int64_t per_block = causal ? (a.tiles_per_block + 1) / 2 : a.tiles_per_block;
+  const int64_t items = ceil_div(n, block) * per_block * heads;
   if (items >= (int64_t(1) << 31))
     return fail(HA_ERR_SHAPE, "%lld query tiles exceed the launch limit", (long long)items);
-  a.items_per_head = uint32_t(ceil_div(n, block) * a.tiles_per_block);
+  a.items_per_head = uint32_t(ceil_div(n, block) * per_block);
   a.items = uint32_t(items);
   if (merge && merge->L > 0) {
     // the merge epilogue locates partials by shifts of the base-block index
