@@ -1180,15 +1180,10 @@ __device__ __forceinline__ void kv16_exact_sweep(const BwdArgs& a, BwdSmem<D>& s
   }
 }
 
-// dK, dV of key tile t (128 keys) of the block against its queries.
+// dK, dV of key tile `tile` (128 keys) of block blk against its queries.
 template <int D, bool kCausal>
-__device__ __forceinline__ void kv16_exact_item(const BwdArgs& a, BwdSmem<D>& sm, uint32_t lin) {
-  const uint32_t gx = a.items_per_head;
-  const int head = int(lin / gx);
-  const uint32_t bx = lin - uint32_t(head) * gx;
-  const uint32_t tpb = a.tiles_per_block;
-  const uint32_t blk = bx / tpb;
-  const int64_t tile = bx - blk * tpb;
+__device__ __forceinline__ void kv16_exact_keys(const BwdArgs& a, BwdSmem<D>& sm, int head,
+                                                uint32_t blk, int64_t tile) {
   const int64_t b_lo = blk * a.block;
   const int64_t b_hi = b_lo + a.block < a.n ? b_lo + a.block : a.n;
   const int64_t k0 = b_lo + tile * kKeys16;
@@ -1216,6 +1211,30 @@ __device__ __forceinline__ void kv16_exact_item(const BwdArgs& a, BwdSmem<D>& sm
   }
   store_row16_bf16<D>(dk, a.dK + (int64_t(head) * a.n + krow) * D);
   store_row16_bf16<D>(dv, a.dV + (int64_t(head) * a.n + krow) * D);
+}
+
+// Work item lin = head * items_per_head + blk * per_block + j. Non-causal:
+// key tile j (per_block = tiles_per_block). Causal: key tiles j and
+// tiles_per_block - 1 - j (per_block = ceil(tiles_per_block / 2)), one after
+// the other, so that every item sweeps the same number of query tiles (key
+// tile j sees the queries from its own rows to the block's end); each sweep
+// ends with a barrier, after which the tile buffers are free.
+template <int D, bool kCausal>
+__device__ __forceinline__ void kv16_exact_item(const BwdArgs& a, BwdSmem<D>& sm, uint32_t lin) {
+  const uint32_t gx = a.items_per_head;
+  const int head = int(lin / gx);
+  const uint32_t bx = lin - uint32_t(head) * gx;
+  const uint32_t tpb = a.tiles_per_block;
+  if constexpr (kCausal) {
+    const uint32_t ppb = (tpb + 1) / 2;
+    const uint32_t blk = bx / ppb;
+    const uint32_t j = bx - blk * ppb;
+    kv16_exact_keys<D, kCausal>(a, sm, head, blk, int64_t(j));
+    if (tpb - 1 - j != j) kv16_exact_keys<D, kCausal>(a, sm, head, blk, int64_t(tpb - 1 - j));
+  } else {
+    const uint32_t blk = bx / tpb;
+    kv16_exact_keys<D, kCausal>(a, sm, head, blk, int64_t(bx - blk * tpb));
+  }
 }
 
 // Sweep over `count` queries at sorted positions [p0, p0 + count) of `perm`
@@ -1713,7 +1732,8 @@ int launch_bwd_exact(const BwdIO& io, int64_t n, int d, int heads, int causal, i
     // the key-major items are tiles of 128 keys (16 per wave)
     BwdArgs akv = a;
     const int64_t tpb_kv = ceil_div(block, kKeys16);
-    const int64_t per_head_kv = ceil_div(n, block) * tpb_kv;
+    // causal items are pairs of key tiles (kv16_exact_item)
+    const int64_t per_head_kv = ceil_div(n, block) * (causal ? (tpb_kv + 1) / 2 : tpb_kv);
     akv.tiles_per_block = uint32_t(tpb_kv);
     akv.items_per_head = uint32_t(per_head_kv);
     if (!rc && per_head_kv * heads >= (int64_t(1) << 31))
