@@ -352,8 +352,15 @@ __global__ __launch_bounds__(kThreads) void vnorm_rows_kernel(
 }
 
 // grid: (ceil(n/1024), heads, 2 or 1); z = 0 hashes Q, z = 1 hashes K
+// bf16 rows fit in 128 registers, four waves per SIMD: 1024 resident
+// work-groups, so that 2048 of them (n = 131072 at 8 heads, or n = 32768 at
+// 32) run as two full rounds instead of two and a part. The fp32 path keeps
+// its registers.
+template <typename T> struct HashWaves { static constexpr int value = sizeof(T) == 2 ? 4 : 1; };
+
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void hash_kernel(
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(HashWaves<T>::value))) void hash_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const float* __restrict__ G,
     const bf16_t* __restrict__ Gb, int r, int64_t n, uint8_t* __restrict__ codes_q,
     uint8_t* __restrict__ codes_k) {
