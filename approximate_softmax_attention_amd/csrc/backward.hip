@@ -94,9 +94,9 @@ struct BwdArgs {
   uint32_t items_per_head;
   int merge_levels;
   int64_t S;
-  float* part_dq;          // [L][heads][S][d]
-  float* part_dk;
-  float* part_dv;
+  bf16_t* part_dq;         // [L][heads][S][d]
+  bf16_t* part_dk;
+  bf16_t* part_dv;
   // BUCKET / SAMPLE
   LevelTable table;
   int m;
@@ -236,6 +236,25 @@ __device__ __forceinline__ void add_row_f32(f32x16* acc, const float* row) {
       acc[db][4 * q4 + 1] += v.y;
       acc[db][4 * q4 + 2] += v.z;
       acc[db][4 * q4 + 3] += v.w;
+    }
+}
+
+// Level partials are bf16 rows, like the forward pass's partial outputs.
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+template <int D>
+__device__ __forceinline__ void add_row_bf16(f32x16* acc, const bf16_t* row) {
+  const int g = lane_id() >> 5;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const uint2 v = *reinterpret_cast<const uint2*>(row + chunk_col(db, q4, g));
+      acc[db][4 * q4] += bf16_lo(v.x);
+      acc[db][4 * q4 + 1] += bf16_hi(v.x);
+      acc[db][4 * q4 + 2] += bf16_lo(v.y);
+      acc[db][4 * q4 + 3] += bf16_hi(v.y);
     }
 }
 
@@ -589,6 +608,19 @@ __device__ __forceinline__ void add_row16(Acc16<D>& a, const float* row) {
 }
 
 template <int D>
+__device__ __forceinline__ void add_row16_bf16(Acc16<D>& a, const bf16_t* row) {
+  const int g = lane_id() >> 4;
+#pragma unroll
+  for (int mb = 0; mb < D / 16; ++mb) {
+    const uint2 v = *reinterpret_cast<const uint2*>(row + 16 * mb + 4 * g);
+    a.a[mb][0] += bf16_lo(v.x);
+    a.a[mb][1] += bf16_hi(v.x);
+    a.a[mb][2] += bf16_lo(v.y);
+    a.a[mb][3] += bf16_hi(v.y);
+  }
+}
+
+template <int D>
 __device__ __forceinline__ void store_row16_f32(const Acc16<D>& a, float* row) {
   const int g = lane_id() >> 4;
 #pragma unroll
@@ -685,7 +717,7 @@ __device__ __forceinline__ void q_exact_item(const BwdArgs& a, BwdSmem<D>& sm, u
   scale_acc<D>(dq, a.scale);
   for (int lv = 0; lv < a.merge_levels; ++lv) {
     const int64_t idx = level_slot(a, lv, blk, b_lo, qrow, true, head);
-    if (idx >= 0) add_row_f32<D>(dq, a.part_dq + idx * D);
+    if (idx >= 0) add_row_bf16<D>(dq, a.part_dq + idx * D);
   }
   store_row_bf16<D>(dq, a.dQ + (int64_t(head) * a.n + qrow) * D);
 }
@@ -740,7 +772,7 @@ __device__ __forceinline__ void finish_exact_key(const BwdArgs& a, f32x16* acc, 
   if (is_k) scale_acc<D>(acc, a.scale);
   for (int lv = 0; lv < a.merge_levels; ++lv) {
     const int64_t idx = level_slot(a, lv, blk, b_lo, krow, false, head);
-    if (idx >= 0) add_row_f32<D>(acc, (is_k ? a.part_dk : a.part_dv) + idx * D);
+    if (idx >= 0) add_row_bf16<D>(acc, (is_k ? a.part_dk : a.part_dv) + idx * D);
   }
   store_row_bf16<D>(acc, (is_k ? a.dK : a.dV) + (int64_t(head) * a.n + krow) * D);
 }
@@ -933,7 +965,7 @@ __device__ __forceinline__ void q_bucket_item(const BwdArgs& a, BwdSmem<D>& sm, 
     // queries of sub-problem seg are rows [2 seg h + h, 2 seg h + 2h); their
     // slot is seg h + (row - 2 seg h - h)
     const int64_t slot = (int64_t(it.lv) * a.heads + it.head) * a.S + (qrow - (it.seg + 1) * h);
-    store_row_f32<D>(dq, a.part_dq + slot * D);
+    store_row_bf16<D>(dq, a.part_dq + slot * D);
   } else {
     store_row_bf16<D>(dq, a.dQ + (int64_t(it.head) * a.n + qrow) * D);
   }
@@ -1037,7 +1069,7 @@ __device__ __forceinline__ void finish_bucket_key(const BwdArgs& a, const Bucket
       add_row_f32<D>(acc, part + ((item0 + sc * nqc + qc) * kAttnQ + tt) * D);
   }
   if (a.table.causal)
-    store_row_f32<D>(acc, (is_k ? a.part_dk : a.part_dv) + kslot * D);
+    store_row_bf16<D>(acc, (is_k ? a.part_dk : a.part_dv) + kslot * D);
   else
     store_row_bf16<D>(acc, (is_k ? a.dK : a.dV) + (int64_t(it.head) * a.n + krow) * D);
 }
@@ -1205,8 +1237,8 @@ __device__ __forceinline__ void kv16_exact_keys(const BwdArgs& a, BwdSmem<D>& sm
   for (int lv = 0; lv < a.merge_levels; ++lv) {
     const int64_t idx = level_slot(a, lv, blk, b_lo, krow, false, head);
     if (idx >= 0) {
-      add_row16<D>(dk, a.part_dk + idx * D);
-      add_row16<D>(dv, a.part_dv + idx * D);
+      add_row16_bf16<D>(dk, a.part_dk + idx * D);
+      add_row16_bf16<D>(dv, a.part_dv + idx * D);
     }
   }
   store_row16_bf16<D>(dk, a.dK + (int64_t(head) * a.n + krow) * D);
@@ -1322,8 +1354,8 @@ __device__ __forceinline__ void finish_bucket_keys16(const BwdArgs& a, const Buc
     }
   }
   if (a.table.causal) {
-    store_row16_f32<D>(dv, a.part_dv + kslot * D);
-    store_row16_f32<D>(dk, a.part_dk + kslot * D);
+    store_row16_bf16<D>(dv, a.part_dv + kslot * D);
+    store_row16_bf16<D>(dk, a.part_dk + kslot * D);
   } else {
     store_row16_bf16<D>(dv, a.dV + (int64_t(it.head) * a.n + krow) * D);
     store_row16_bf16<D>(dk, a.dK + (int64_t(it.head) * a.n + krow) * D);
@@ -1617,9 +1649,9 @@ void plan_args(BwdArgs& a, const Plan& p, void* ws) {
   a.slot_dv = reinterpret_cast<float*>(w + p.off[HA_WS_SLOT_DV]);
   a.queue = reinterpret_cast<uint32_t*>(w + p.off[HA_WS_SCHED]);
   if (p.causal && p.L > 0) {
-    a.part_dq = reinterpret_cast<float*>(w + p.off[HA_WS_PART_DQ]);
-    a.part_dk = reinterpret_cast<float*>(w + p.off[HA_WS_PART_DK]);
-    a.part_dv = reinterpret_cast<float*>(w + p.off[HA_WS_PART_DV]);
+    a.part_dq = reinterpret_cast<bf16_t*>(w + p.off[HA_WS_PART_DQ]);
+    a.part_dk = reinterpret_cast<bf16_t*>(w + p.off[HA_WS_PART_DK]);
+    a.part_dv = reinterpret_cast<bf16_t*>(w + p.off[HA_WS_PART_DV]);
   }
 }
 
@@ -1719,9 +1751,9 @@ int launch_bwd_exact(const BwdIO& io, int64_t n, int d, int heads, int causal, i
     const char* w = static_cast<const char*>(ws);
     a.merge_levels = merge->L;
     a.S = merge->S;
-    a.part_dq = reinterpret_cast<float*>(const_cast<char*>(w) + merge->off[HA_WS_PART_DQ]);
-    a.part_dk = reinterpret_cast<float*>(const_cast<char*>(w) + merge->off[HA_WS_PART_DK]);
-    a.part_dv = reinterpret_cast<float*>(const_cast<char*>(w) + merge->off[HA_WS_PART_DV]);
+    a.part_dq = reinterpret_cast<bf16_t*>(const_cast<char*>(w) + merge->off[HA_WS_PART_DQ]);
+    a.part_dk = reinterpret_cast<bf16_t*>(const_cast<char*>(w) + merge->off[HA_WS_PART_DK]);
+    a.part_dv = reinterpret_cast<bf16_t*>(const_cast<char*>(w) + merge->off[HA_WS_PART_DV]);
   }
   const char* nq = merge ? "bwd_base_q" : "bwd_exact_q";
   const char* nkv = merge ? "bwd_base_kv" : "bwd_exact_kv";

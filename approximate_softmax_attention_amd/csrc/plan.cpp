@@ -135,9 +135,9 @@ int make_plan(Plan& p, int64_t n, int d, int heads, int causal, int b, int m,
   if (backward) {
     add_region(p, HA_WS_DELTA, H * n * 4);
     if (p.causal && p.L > 0) {
-      add_region(p, HA_WS_PART_DQ, slots * d * 4);
-      add_region(p, HA_WS_PART_DK, slots * d * 4);
-      add_region(p, HA_WS_PART_DV, slots * d * 4);
+      add_region(p, HA_WS_PART_DQ, slots * d * 2);
+      add_region(p, HA_WS_PART_DK, slots * d * 2);
+      add_region(p, HA_WS_PART_DV, slots * d * 2);
     }
     add_region(p, HA_WS_SLOT_FIRST, slots * 4);
     add_region(p, HA_WS_SLOT_NEXT, H * p.nodes * 2 * m * 4);

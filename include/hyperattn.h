@@ -235,14 +235,16 @@ int rowsum_estimate(const void* Q, const void* K, int64_t n, int d, int heads,
  * outputs for these inputs and arguments (lse is required).
  * dQ, dK, dV: outputs [heads][n][d] bf16.
  * The buckets and samples are recomputed from `seed` on the device, so the
- * arguments must be those of the forward call. Accumulation is in fp32, and
- * every sum runs in a fixed order with no atomics, so results are
- * deterministic.
+ * arguments must be those of the forward call. Accumulation is in fp32
+ * (a causal level's partial gradient is rounded to bf16 once before the base
+ * case adds it), and every sum runs in a fixed order with no atomics, so
+ * results are deterministic.
  * bf16 only (HA_ERR_UNSUPPORTED for HA_F32), m <= 2048; other arguments and
  * errors as hyperattn_forward.
  * workspace: >= hyperattn_backward_workspace_bytes(...) with the same
- * arguments. It is larger than the forward's: it holds per-level fp32
- * partial gradients and the sample slots' partial gradients.
+ * arguments. It is larger than the forward's: it holds per-level bf16
+ * partial gradients (rounded like the forward's partial outputs) and the
+ * sample slots' fp32 partial gradients.
  */
 int hyperattn_backward(const void* Q, const void* K, const void* V,
                        const void* O, const float* lse, const void* dO,
