@@ -14,7 +14,7 @@
 namespace ha {
 
 constexpr int kMaxLevels = 21;      // 20 halvings + 1
-constexpr int kSortChunk = 2048;     // elements per sort work-group
+constexpr int kSortChunk = 4096;     // elements per sort work-group
 constexpr int kSortBins = 256;       // codes are < 2^r <= 256
 
 // ---------------------------------------------------------------- errors

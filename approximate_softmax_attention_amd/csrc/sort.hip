@@ -5,7 +5,7 @@
 // (code, index) with a counting sort over the 2^r <= 256 code values. All
 // segments of all levels are independent once the codes exist, so each of
 // the two passes covers every segment in one launch:
-//   1. per chunk of 2048 elements: a 256-bin histogram (LDS counters);
+//   1. per chunk of kSortChunk elements: a 256-bin histogram (LDS counters);
 //   2. per chunk: its exclusive offsets (bin-major over the segment, then
 //      chunk-minor), summed from the segment's chunk histograms by one thread
 //      per bin; stable ranks (wave ballots find the earlier lanes with the
@@ -93,7 +93,9 @@ constexpr int kPer = kSortChunk / kThreads;      // elements per thread and chun
 
 __global__ __launch_bounds__(kThreads) void sort_hist_kernel(SortArgs a) {
   __shared__ uint32_t hist[kSortBins];
-  const int64_t w = blockIdx.x;
+  // the scatter's chunk-to-XCD mapping: a chunk's histogram and codes are
+  // in the L2 of the XCD that ranks it
+  const int64_t w = chunk_of(blockIdx.x, gridDim.x);
   const ChunkRef c = decode_chunk(a, w);
   hist[threadIdx.x] = 0;
   const uint8_t* codes = a.codes[c.side] + int64_t(c.head) * a.n +
