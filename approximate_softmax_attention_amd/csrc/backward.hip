@@ -34,9 +34,10 @@
 // partial slot gradients stay apart and the bucket kernel adds them, with
 // every other slot drawn on the same key row in slot order, to that row's
 // gradient: no floating-point atomics, so results are deterministic.
-// Causal recursion: the bucket kernels write per-level partial gradients and
-// the base case kernels add them to the rows of their diagonal blocks, as
-// the forward pass's base case merges partial outputs.
+// Causal recursion: the bucket kernels write per-level partial gradients
+// (bf16 rows, as the forward pass's partial outputs) and the base case
+// kernels add them in fp32 to the rows of their diagonal blocks, as the
+// forward pass's base case merges partial outputs.
 #include <cmath>
 #include <type_traits>
 
