@@ -305,7 +305,6 @@ int launch_sort_single(const uint8_t* codes, int64_t n, int heads, int32_t* perm
   a.codes[0] = a.codes[1] = codes;
   a.perm[0] = a.perm[1] = perm;
   a.rank = nullptr;
-  const int64_t chunks = int64_t(heads) * v.sort_cps;
   a.hist = static_cast<uint32_t*>(scratch);
   return run_sort(a, retable(a.table, heads, 1), s);
 }
