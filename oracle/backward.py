@@ -39,7 +39,7 @@ P_ij = e^{s_ij - Lambda_i}.
 
 import numpy as np
 
-from . import exact, hyperattention as ha, sampling, sortlsh
+from . import exact, hyperattention as ha
 
 
 def _as64(x):
