@@ -294,9 +294,9 @@ def cpu_baseline(w):
 
 def cpu_baseline_exact(w):
     """The oracle's exact attention as it stands: the whole workload when its
-    score matrices are small (heads * n^2 <= 2^31), else 256 position-
+    score matrices are small (heads * n^2 <= 2^31), else 4096 position-
     stratified query rows of head 0 scaled by the number of (query, key)
-    pairs of the whole forward ("extrapolated")."""
+    pairs of the whole forward ("extrapolated"; about 25 s at n = 131072)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -312,7 +312,8 @@ def cpu_baseline_exact(w):
         full, sample = dt, f"the whole workload ({w.heads} heads), {dt:.1f} s"
     else:
         q, k, v, _ = wl.make_head(w, 0)
-        edges = np.linspace(0, w.n, 257).astype(np.int64)
+        nrows = 4096
+        edges = np.linspace(0, w.n, nrows + 1).astype(np.int64)
         rs = np.random.default_rng(0)
         rows = np.array([rs.integers(lo, hi) for lo, hi in zip(edges[:-1], edges[1:])])
         t0 = time.perf_counter()
@@ -320,8 +321,8 @@ def cpu_baseline_exact(w):
         dt = time.perf_counter() - t0
         pairs = float((rows + 1).sum()) if w.causal else float(len(rows)) * w.n
         full = dt * pairs_total / pairs
-        sample = (f"256 position-stratified rows of head 0, {dt:.1f} s, extrapolated by "
-                  f"(query, key) pairs to all {w.heads} heads")
+        sample = (f"{nrows} position-stratified rows of head 0, {dt:.1f} s, extrapolated "
+                  f"by (query, key) pairs to all {w.heads} heads")
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": w.n / full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": sample, "extrapolated": w.heads * w.n * w.n > (1 << 31)}
