@@ -77,6 +77,24 @@ def test_sortlsh_hash_bit_exact(dtype, d):
         assert codes[0, 5].item() == 0
 
 
+def test_sortlsh_sort_spans_several_chunks():
+    """n = 10007 rows per head: the stable sort runs over three chunks (two
+    whole ones and a ragged tail), so each chunk's offsets come from its
+    segment's earlier chunk histograms."""
+    banner("hash + sort n=10007")
+    w, Q, K, V, _ = _inputs("single_head_noncausal_n1024_d64_fp32", heads=2, n=10007, d=128,
+                            dtype="bf16")
+    api = _api()
+    codes, perm = api.sortlsh_hash(to_dev(Q, "bf16"), r=8, seed=77, with_perm=True)
+    _sync()
+    G = osl.hyperplanes(77, 2, 8, 128)
+    for h in range(2):
+        ref = osl.hash_codes(Q[h], G[h])
+        assert np.array_equal(codes[h].cpu().numpy(), ref)
+        rp, _ = osl.sort_segment(ref)
+        assert np.array_equal(perm[h].cpu().numpy(), rp)
+
+
 def test_hash_without_hyperplanes_is_the_identity_order():
     """r = 0: every code is 0 and the stable sort keeps index order (ragged
     n, so the code rows of the second head are not 16-byte aligned)."""
@@ -191,6 +209,9 @@ FORWARD_CASES = {
                                        dict(heads=2, n=4096, dtype="bf16", b=256, m=512)),
     "causal_bf16_d128_slot_refill": ("chatglm2_causal_n32768_d128_h32_bf16",
                                      dict(heads=1, n=8192, b=512, m=300, recursion_base=1024)),
+    # a segment of 9000 rows: three sort chunks, the last ragged
+    "noncausal_bf16_d64_three_sort_chunks": ("single_head_noncausal_n1024_d64_fp32",
+                                             dict(heads=2, n=9000, dtype="bf16", b=120, m=100)),
     # r = 0: the local block mask in place of sortLSH
     "local_mask_causal_bf16_d128": ("chatglm2_causal_n32768_d128_h32_bf16",
                                     dict(heads=2, n=4096, b=128, m=100, r=0,
